@@ -1,0 +1,202 @@
+/*
+ * sparse_attn.h -- C ABI of the indexer-selected sparse attention library for AMD
+ * Instinct MI355X (gfx950).  Library: libsparse_attn.so.
+ *
+ * The method (two stages):
+ *   1. a lightweight indexer scores every preceding token,
+ *        I(t,s) = sum_j w(t,j) * ReLU( q(t,j) . k(s) ),
+ *      over H_I low-dimensional index heads (width d_I) and one index key k(s) per token
+ *      -- "Sparse Attention and RL Optimization: Three Technical Breakthroughs in LLM
+ *      Post-Training", section 2.2;
+ *   2. each query keeps the top-k preceding tokens by that score and runs causal softmax
+ *      attention over only those KV rows -- the same page, section 2.3 and the section
+ *      2.5 pseudocode; "Long-Context LLMs Explained: Sparse Attention, Stable
+ *      Reinforcement Learning, and Verifiable Synthetic Data", sections 2.2-2.4 (decode
+ *      reads only the selected k KV entries of a paged cache, section 2.3; prefill and
+ *      decode are tuned as separate phases, section 2.5).
+ *
+ * Conventions for every call below
+ *   - Tensors are DEVICE pointers to caller-owned, contiguous, row-major memory, 16-byte
+ *     aligned.  The library never frees or retains them after the call returns.
+ *   - Element type of q, k, v, q_idx, k_idx is the handle's dtype (fp32 or bf16, given as
+ *     raw bits).  w, scores, out and lse are always fp32; indices are int32.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and do
+ *     not synchronise, allocate device memory or touch the host after launch.  Scratch
+ *     memory is the caller's `ws` workspace, sized by sparse_attn_workspace_size().
+ *   - Host-side validation happens before any launch; on failure nothing is launched and
+ *     the status plus sparse_attn_last_error() explain why.  Values that live in device
+ *     memory (indices, block tables, context lengths, per-sequence k) are range-checked
+ *     by the kernels: offending entries are skipped (never dereferenced) and a bit is set
+ *     in the handle's device error word, read back by sparse_attn_check().
+ *   - Causality: query t sees keys s <= t (itself included); a decode query with context
+ *     length n sees s < n, its own key being the last cached token.
+ *   - Ties in top-k go to the lower token index.  With fewer than k visible tokens all
+ *     visible tokens are selected and the remaining slots are -1.  Index lists are
+ *     written in ascending token order.
+ *   - A handle is not thread-safe; use one handle per host thread / stream.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sa_handle_s *sa_handle_t;
+
+typedef enum {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1,  /* bad pointer, shape, size or config                    */
+    SA_ERR_UNSUPPORTED = 2,  /* valid request this build does not serve               */
+    SA_ERR_WORKSPACE = 3,    /* ws is NULL or smaller than sparse_attn_workspace_size */
+    SA_ERR_HIP = 4,          /* a HIP runtime call failed (launch, copy, alloc)       */
+    SA_ERR_DEVICE_CHECK = 5  /* sparse_attn_check(): a kernel flagged bad device data */
+} sa_status_t;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype_t;
+
+/* Bits of the device error word (sparse_attn_check). */
+#define SA_DEVERR_INDEX_RANGE   1u  /* an attention index was >= the visible length    */
+#define SA_DEVERR_BLOCK_TABLE   2u  /* a visible token's page was -1 or >= n_pages       */
+#define SA_DEVERR_CTX_LEN       4u  /* ctx_len[b] outside [1, max_ctx]                   */
+#define SA_DEVERR_TOPK          8u  /* topk[b] outside [1, max_topk]                     */
+
+typedef struct {
+    int32_t n_idx_heads;   /* H_I: index heads (e.g. 64)                                  */
+    int32_t d_idx;         /* d_I: index head width (e.g. 128)                            */
+    int32_t n_heads;       /* H: attention query heads (e.g. 16)                          */
+    int32_t n_kv_heads;    /* H_kv: 1 (all heads share one KV row) or H                   */
+    int32_t d_qk;          /* query/key width per head (e.g. 576)                         */
+    int32_t d_v;           /* value width per head (e.g. 512)                             */
+    int32_t v_from_k;      /* 1: the value is the first d_v columns of the key row (one
+                              shared latent row per token, multi-head latent attention as
+                              kept by the model in "A Guide to Sparse Attention and
+                              Efficient Reinforcement Learning in LLM Long-Context
+                              Inference", section 1); 0: separate v tensor             */
+    int32_t page_size;     /* tokens per KV page for decode (e.g. 64)                     */
+    int32_t max_topk;      /* largest k any call may ask for, 1..8192                      */
+    sa_dtype_t dtype;      /* element type of q, k, v, q_idx, k_idx                       */
+    float softmax_scale;   /* attention logit scale; 0 means 1/sqrt(d_qk)                 */
+} sa_config_t;
+
+/* Operations for sparse_attn_workspace_size(). */
+#define SA_OP_PREFILL 1  /* n = L (sequence length), max_ctx ignored                    */
+#define SA_OP_DECODE  2  /* n = B (batch), max_ctx = upper bound of every ctx_len[b]     */
+#define SA_OP_TOPK    3  /* n = rows, max_ctx = cols                                      */
+
+/* Create a handle for one configuration.  Validates the config, allocates the 4-byte
+ * device error word on the current device (the only device allocation the library makes)
+ * and picks kernels.  Returns SA_ERR_INVALID_ARG for an inconsistent config. */
+sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out);
+
+/* Release a handle (synchronises the device before freeing the error word). */
+void sparse_attn_destroy(sa_handle_t h);
+
+/* Text of the last error on this handle ("" if none); with h == NULL, the last error of
+ * sparse_attn_create on this thread.  Owned by the library, valid until the next call. */
+const char *sparse_attn_last_error(sa_handle_t h);
+
+/* Bytes of workspace a call of `op` at size n / max_ctx needs (may be 0). */
+sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t max_ctx,
+                                       size_t *bytes);
+
+/* Synchronise `stream`, read and clear the device error word.  SA_OK if it was zero,
+ * otherwise SA_ERR_DEVICE_CHECK with the bits in *bits (if bits != NULL). */
+sa_status_t sparse_attn_check(sa_handle_t h, void *stream, uint32_t *bits);
+
+/* Indexer scores of a whole sequence, materialised -- "Sparse Attention and RL
+ * Optimization...", section 2.2 (formula) with the causal mask of the section 2.5
+ * pseudocode.  A parity/debug entry: the [L, L] matrix is only built for L <= 16384.
+ *   q_idx  [L, H_I, d_I]  dtype      index queries q(t,j)
+ *   w      [L, H_I]       fp32       head weights w(t,j) (any sign)
+ *   k_idx  [L, d_I]       dtype      index keys k(s), shared by all heads
+ *   scores [L, L]         fp32 out   scores[t,s] = I(t,s) for s <= t, -inf for s > t
+ * Errors: SA_ERR_INVALID_ARG (NULL pointer, L < 1), SA_ERR_UNSUPPORTED (L > 16384). */
+sa_status_t indexer_scores(sa_handle_t h, const void *q_idx, const float *w, const void *k_idx,
+                           int64_t L, float *scores, void *stream);
+
+/* Per-row top-k of a score matrix -- "Sparse Attention and RL Optimization...", section
+ * 2.3 (top-k preceding tokens per query by index score) and the `topk` step of the
+ * section 2.5 pseudocode.
+ *   scores    [rows, ld] fp32   row r's candidates are scores[r, 0 .. valid(r))
+ *   valid_len [rows] int32 or NULL: valid(r) = valid_len[r] (must be in [1, cols]); NULL
+ *             means the causal rule valid(r) = min(r + 1, cols)
+ *   k_per_row [rows] int32 or NULL: k(r) = k_per_row[r] (1 <= k(r) <= k); NULL means k
+ *   k         width of each idx row, 1 <= k <= max_topk
+ *   idx       [rows, k] int32 out: the min(k(r), valid(r)) columns with the largest
+ *             scores (ties -> lower column), ascending, then -1 padding
+ * Scores must not be NaN.  ws may be NULL (the call needs no workspace).
+ * Errors: SA_ERR_INVALID_ARG for NULL tensors, rows/cols < 1, ld < cols, k outside
+ * [1, max_topk]; device-side SA_DEVERR_TOPK for bad valid_len / k_per_row entries. */
+sa_status_t topk_select(sa_handle_t h, const float *scores, int64_t rows, int64_t cols, int64_t ld,
+                        const int32_t *valid_len, const int32_t *k_per_row, int32_t k,
+                        int32_t *idx, void *stream);
+
+/* Causal prefill of one sequence: indexer -> per-query top-k -> attention over the
+ * selected rows -- the whole pipeline of "Sparse Attention and RL Optimization...",
+ * section 2.5 and "Long-Context LLMs Explained...", section 2.4.  Scores are produced
+ * and consumed per block of queries in the workspace; the [L, L] matrix is never formed.
+ *   q      [L, H, d_qk]     dtype    attention queries
+ *   k      [L, H_kv, d_qk]  dtype    keys (the shared latent row when H_kv = 1)
+ *   v      [L, H_kv, d_v]   dtype    values, or NULL when v_from_k = 1
+ *   q_idx  [L, H_I, d_I], w [L, H_I] fp32, k_idx [L, d_I]: the indexer inputs
+ *   topk   k, 1 <= k <= max_topk
+ *   out    [L, H, d_v] fp32 out: softmax(scale q k_sel^T) v_sel per query and head
+ *   lse    [L, H] fp32 out or NULL: log-sum-exp of the scaled logits (natural log)
+ *   idx_out [L, topk] int32 out or NULL: the selected tokens (ascending, -1 padded)
+ *   ws, ws_bytes: workspace of at least sparse_attn_workspace_size(SA_OP_PREFILL, L)
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP. */
+sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, const void *v,
+                                const void *q_idx, const float *w, const void *k_idx, int64_t L,
+                                int32_t topk, float *out, float *lse, int32_t *idx_out,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step for B sequences against paged caches -- "Long-Context LLMs
+ * Explained...", section 2.3: the indexer scores the whole cached context, and attention
+ * reads only the selected KV rows, located through the block table.
+ *   q          [B, H, d_qk]           dtype   the new token's queries
+ *   q_idx      [B, H_I, d_I], w [B, H_I] fp32: its indexer inputs
+ *   kv_pages   [n_pages, page_size, H_kv, d_qk] dtype   key (latent) page pool
+ *   v_pages    [n_pages, page_size, H_kv, d_v]  dtype   value pool, or NULL if v_from_k
+ *   kidx_pages [n_pages, page_size, d_I]        dtype   index-key page pool
+ *   block_table [B, max_blocks] int32: logical page j of sequence b is pool page
+ *               block_table[b, j]; token s is slot s % page_size of page s / page_size
+ *   ctx_len    [B] int32: n_b visible tokens (1 <= n_b <= max_ctx), the new token last
+ *   topk       [B] int32: k_b (1 <= k_b <= max_topk); min(k_b, n_b) rows are attended
+ *   max_ctx    host-side upper bound of every ctx_len (sizes the launch), <= max_blocks *
+ *              page_size
+ *   out [B, H, d_v] fp32 out; lse [B, H] fp32 out or NULL; idx_out [B, max_topk] int32 out
+ *   or NULL (logical token positions, ascending, -1 padded)
+ *   ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_DECODE, B, max_ctx)
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP; device-side SA_DEVERR_* bits
+ * for out-of-range ctx_len, topk or block-table entries (those sequences are skipped). */
+sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                               const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                               const int32_t *ctx_len, const int32_t *topk, int32_t B,
+                               int32_t max_ctx, float *out, float *lse, int32_t *idx_out,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Kernel timing, a tracing aid for benchmarks.  While enabled, every kernel the handle
+ * launches is bracketed by a pair of hipEvents recorded on the launch stream, and the
+ * elapsed times are summed per kernel kind.  Enabling resets the sums; it creates events
+ * (host-side runtime objects) but allocates no device memory in the library's own name.
+ * sparse_attn_profile_read synchronises on the recorded events and returns, per kind, the
+ * summed milliseconds and the number of launches (arrays of SA_KERNEL_COUNT entries).
+ * While profiling is on, calls may synchronise the host when many events are pending. */
+#define SA_KERNEL_INDEXER   0  /* indexer scores (prefill blocks, decode, indexer_scores) */
+#define SA_KERNEL_TOPK      1  /* per-row top-k selection                                 */
+#define SA_KERNEL_ATTENTION 2  /* attention over the selected rows                        */
+#define SA_KERNEL_MERGE     3  /* merge of split decode attention states                  */
+#define SA_KERNEL_COUNT     4
+sa_status_t sparse_attn_profile(sa_handle_t h, int enable);
+sa_status_t sparse_attn_profile_read(sa_handle_t h, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

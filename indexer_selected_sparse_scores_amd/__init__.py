@@ -1,0 +1,240 @@
+"""Indexer-selected sparse attention on AMD Instinct MI355X (gfx950).
+
+Python binding of ``libsparse_attn.so`` (declared in ``include/sparse_attn.h``).  The
+functions here carry the C names and only marshal arguments: torch tensors become device
+pointers, the current HIP stream is passed along, and a non-OK status becomes a
+``SparseAttnError``.  Every step of the computation runs in the library's HIP kernels;
+there is no Python or CPU fallback, and a missing library raises at import of the first
+call.
+
+The method: a lightweight indexer scores every preceding token, I(t,s) = sum_j w(t,j)
+ReLU(q(t,j).k(s)) ("Sparse Attention and RL Optimization: Three Technical Breakthroughs in
+LLM Post-Training", section 2.2); each query keeps the top-k tokens (section 2.3) and runs
+softmax attention over only those KV rows (section 2.5; for decode over a paged cache,
+"Long-Context LLMs Explained: Sparse Attention, Stable Reinforcement Learning, and
+Verifiable Synthetic Data", section 2.3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_DEVICE_CHECK = range(6)
+SA_F32, SA_BF16 = 0, 1
+SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK = 1, 2, 3
+SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK = 1, 2, 4, 8
+
+# Every symbol include/sparse_attn.h declares.
+EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error",
+            "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
+            "sparse_attn_prefill", "sparse_attn_decode", "sparse_attn_profile",
+            "sparse_attn_profile_read")
+KERNEL_KINDS = ("indexer", "topk", "attention", "merge")
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class sa_config_t(ctypes.Structure):
+    _fields_ = [("n_idx_heads", ctypes.c_int32), ("d_idx", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32), ("v_from_k", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_topk", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class Config:
+    n_idx_heads: int = 64
+    d_idx: int = 128
+    n_heads: int = 16
+    n_kv_heads: int = 1
+    d_qk: int = 576
+    d_v: int = 512
+    v_from_k: bool = True
+    page_size: int = 64
+    max_topk: int = 2048
+    dtype: str = "bf16"          # element type of q, k, v, q_idx, k_idx: "bf16" or "f32"
+    softmax_scale: float = 0.0   # 0 -> 1/sqrt(d_qk)
+
+    def to_c(self) -> sa_config_t:
+        return sa_config_t(self.n_idx_heads, self.d_idx, self.n_heads, self.n_kv_heads, self.d_qk,
+                           self.d_v, int(self.v_from_k), self.page_size, self.max_topk,
+                           SA_BF16 if self.dtype == "bf16" else SA_F32, float(self.softmax_scale))
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libsparse_attn.so (built by ``indexer_selected_sparse_scores_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python indexer_selected_sparse_scores_amd/build.py` (no fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    st = ctypes.c_int
+    sig = {
+        "sparse_attn_create": ([ctypes.POINTER(sa_config_t), ctypes.POINTER(P)], st),
+        "sparse_attn_destroy": ([P], None),
+        "sparse_attn_last_error": ([P], ctypes.c_char_p),
+        "sparse_attn_workspace_size": ([P, ctypes.c_int, i64, i64, ctypes.POINTER(sz)], st),
+        "sparse_attn_check": ([P, P, ctypes.POINTER(ctypes.c_uint32)], st),
+        "indexer_scores": ([P, P, P, P, i64, P, P], st),
+        "topk_select": ([P, P, i64, i64, i64, P, P, i32, P, P], st),
+        "sparse_attn_prefill": ([P, P, P, P, P, P, P, i64, i32, P, P, P, P, sz, P], st),
+        "sparse_attn_decode": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, P, P, P, P, sz, P], st),
+        "sparse_attn_profile": ([P, ctypes.c_int], st),
+        "sparse_attn_profile_read": ([P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL; ints pass through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(h, status: int):
+    if status != SA_OK:
+        msg = load_library().sparse_attn_last_error(h)
+        raise SparseAttnError(status, msg.decode() if msg else "")
+
+
+class Handle:
+    """Owns an sa_handle_t (created on the current device)."""
+
+    def __init__(self, cfg: Config):
+        lib = load_library()
+        self.cfg = cfg
+        self._c = cfg.to_c()
+        h = ctypes.c_void_p()
+        st = lib.sparse_attn_create(ctypes.byref(self._c), ctypes.byref(h))
+        if st != SA_OK:
+            raise SparseAttnError(st, lib.sparse_attn_last_error(None).decode())
+        self.ptr = h.value
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            load_library().sparse_attn_destroy(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def sparse_attn_create(cfg: Config) -> Handle:
+    return Handle(cfg)
+
+
+def sparse_attn_destroy(h: Handle) -> None:
+    h.close()
+
+
+def sparse_attn_last_error(h: Handle | None) -> str:
+    msg = load_library().sparse_attn_last_error(h.ptr if h else None)
+    return msg.decode() if msg else ""
+
+
+def sparse_attn_workspace_size(h: Handle, op: int, n: int, max_ctx: int = 0) -> int:
+    out = ctypes.c_size_t()
+    _check(h.ptr, load_library().sparse_attn_workspace_size(h.ptr, op, n, max_ctx, ctypes.byref(out)))
+    return out.value
+
+
+def sparse_attn_check(h: Handle, stream=None) -> int:
+    """Synchronise and read the device error word; raises SparseAttnError if set."""
+    bits = ctypes.c_uint32()
+    _check(h.ptr, load_library().sparse_attn_check(h.ptr, _stream(stream), ctypes.byref(bits)))
+    return bits.value
+
+
+def indexer_scores(h: Handle, q_idx, w, k_idx, scores, stream=None) -> None:
+    L = q_idx.shape[0]
+    _check(h.ptr, load_library().indexer_scores(h.ptr, _ptr(q_idx), _ptr(w), _ptr(k_idx), L,
+                                                _ptr(scores), _stream(stream)))
+
+
+def topk_select(h: Handle, scores, k: int, idx, valid_len=None, k_per_row=None, cols=None,
+                stream=None) -> None:
+    rows, ld = scores.shape
+    cols = ld if cols is None else cols
+    _check(h.ptr, load_library().topk_select(h.ptr, _ptr(scores), rows, cols, ld, _ptr(valid_len),
+                                             _ptr(k_per_row), int(k), _ptr(idx), _stream(stream)))
+
+
+def sparse_attn_prefill(h: Handle, q, k, v, q_idx, w, k_idx, topk: int, out, lse=None,
+                        idx_out=None, ws=None, stream=None) -> None:
+    L = q.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(h.ptr, load_library().sparse_attn_prefill(
+        h.ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(w), _ptr(k_idx), L, int(topk), _ptr(out),
+        _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_decode(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len,
+                       topk, max_ctx: int, out, lse=None, idx_out=None, ws=None, stream=None) -> None:
+    B = q.shape[0]
+    n_pages = kv_pages.shape[0]
+    max_blocks = block_table.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(h.ptr, load_library().sparse_attn_decode(
+        h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
+        _ptr(block_table), max_blocks, _ptr(ctx_len), _ptr(topk), B, int(max_ctx), _ptr(out), _ptr(lse),
+        _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_profile(h: Handle, enable: bool) -> None:
+    _check(h.ptr, load_library().sparse_attn_profile(h.ptr, int(bool(enable))))
+
+
+def sparse_attn_profile_read(h: Handle) -> dict:
+    """{kernel kind: (summed ms, launches)} since profiling was enabled (synchronises)."""
+    ms = (ctypes.c_double * len(KERNEL_KINDS))()
+    n = (ctypes.c_int64 * len(KERNEL_KINDS))()
+    _check(h.ptr, load_library().sparse_attn_profile_read(h.ptr, ms, n))
+    return {k: (ms[i], n[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def workspace(h: Handle, op: int, n: int, max_ctx: int = 0, device=None):
+    """A torch uint8 tensor of the size sparse_attn_workspace_size() asks for."""
+    import torch
+    nbytes = sparse_attn_workspace_size(h, op, n, max_ctx)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device or "cuda")

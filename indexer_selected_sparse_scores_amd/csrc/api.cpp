@@ -1,0 +1,436 @@
+// C ABI of libsparse_attn: host-side validation, workspace carving and kernel launches.
+// Every entry point validates its arguments before launching anything, never allocates
+// device memory (except the error word in sparse_attn_create) and never synchronises
+// (except sparse_attn_check and sparse_attn_destroy).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "sa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_create_error;
+
+constexpr int64_t kMaxIndexerScoresL = 16384;
+constexpr int32_t kMaxTopk = 8192;
+constexpr size_t kAlign = 256;
+// Prefill scores are produced and consumed per block of query rows; a block's scores
+// take at most this many bytes of workspace.
+constexpr size_t kPrefillChunkBytes = size_t(1) << 29;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+sa_status_t fail(sa_handle_t h, sa_status_t st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    if (h) h->last_error = buf;
+    else g_create_error = buf;
+    return st;
+}
+
+sa_status_t hip_status(sa_handle_t h, hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return SA_OK;
+    return fail(h, SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(const sa_handle_s &h) { return h.cfg.dtype == SA_BF16 ? 2 : 4; }
+
+sa_status_t check_device(sa_handle_t h)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(h, SA_ERR_HIP, "hipGetDevice failed");
+    if (dev != h->device)
+        return fail(h, SA_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev,
+                    h->device);
+    return SA_OK;
+}
+
+// Rows of queries whose scores are materialised at once in the prefill workspace.
+int64_t prefill_chunk_rows(int64_t L)
+{
+    int64_t rows = (int64_t)(kPrefillChunkBytes / (sizeof(float) * (size_t)L));
+    rows = rows / 4 * 4;
+    if (rows < 4) rows = 4;
+    if (rows > L) rows = L;
+    return rows;
+}
+
+struct PrefillLayout {
+    size_t scores, idx, total;
+};
+
+PrefillLayout prefill_layout(const sa_handle_s &h, int64_t L)
+{
+    PrefillLayout p;
+    p.scores = 0;
+    p.idx = align_up((size_t)prefill_chunk_rows(L) * (size_t)L * sizeof(float));
+    p.total = p.idx + align_up((size_t)L * (size_t)h.cfg.max_topk * sizeof(int32_t));
+    return p;
+}
+
+struct DecodeLayout {
+    size_t scores, idx, attn, total;
+};
+
+DecodeLayout decode_layout(const sa_handle_s &h, int64_t B, int64_t max_ctx)
+{
+    DecodeLayout d;
+    d.scores = 0;
+    d.idx = align_up((size_t)B * (size_t)max_ctx * sizeof(float));
+    d.attn = d.idx + align_up((size_t)B * (size_t)h.cfg.max_topk * sizeof(int32_t));
+    d.total = d.attn + align_up(sa::attention_workspace(h, B, true));
+    return d;
+}
+
+}  // namespace
+
+namespace sa {
+
+KernelTimer::KernelTimer(sa_handle_s &h, int kind, hipStream_t st) : h_(h), kind_(kind), st_(st)
+{
+    if (!h_.profiling) return;
+    if (h_.spare_events.empty()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        h_.spare_events.push_back(e);
+    }
+    start_ = h_.spare_events.back();
+    h_.spare_events.pop_back();
+    if (hipEventRecord(start_, st_) != hipSuccess) {
+        h_.spare_events.push_back(start_);
+        start_ = nullptr;
+    }
+}
+
+KernelTimer::~KernelTimer()
+{
+    if (!start_) return;
+    hipEvent_t stop;
+    if (h_.spare_events.empty()) {
+        if (hipEventCreate(&stop) != hipSuccess) {
+            h_.spare_events.push_back(start_);
+            return;
+        }
+    } else {
+        stop = h_.spare_events.back();
+        h_.spare_events.pop_back();
+    }
+    (void)hipEventRecord(stop, st_);
+    h_.pending[kind_].emplace_back(start_, stop);
+    size_t n = 0;
+    for (int k = 0; k < SA_KERNEL_COUNT; ++k) n += h_.pending[k].size();
+    if (n >= 2048) (void)drain_profile(h_);
+}
+
+hipError_t drain_profile(sa_handle_s &h)
+{
+    hipError_t first = hipSuccess;
+    for (int k = 0; k < SA_KERNEL_COUNT; ++k) {
+        for (auto &pr : h.pending[k]) {
+            float ms = 0.f;
+            hipError_t e = hipEventSynchronize(pr.second);
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+            if (e == hipSuccess) {
+                h.total_ms[k] += ms;
+                h.launches[k] += 1;
+            } else if (first == hipSuccess) {
+                first = e;
+            }
+            h.spare_events.push_back(pr.first);
+            h.spare_events.push_back(pr.second);
+        }
+        h.pending[k].clear();
+    }
+    return first;
+}
+
+}  // namespace sa
+
+extern "C" {
+
+sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
+{
+    g_create_error.clear();
+    if (!cfg || !out) return fail(nullptr, SA_ERR_INVALID_ARG, "cfg and out must not be NULL");
+    *out = nullptr;
+    const sa_config_t &c = *cfg;
+    if (c.dtype != SA_F32 && c.dtype != SA_BF16)
+        return fail(nullptr, SA_ERR_INVALID_ARG, "dtype must be SA_F32 or SA_BF16");
+    if (c.n_idx_heads < 1 || c.d_idx < 1 || c.n_heads < 1 || c.n_kv_heads < 1 || c.d_qk < 1 || c.d_v < 1)
+        return fail(nullptr, SA_ERR_INVALID_ARG, "head counts and widths must be >= 1");
+    if (c.n_heads % c.n_kv_heads != 0)
+        return fail(nullptr, SA_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_kv_heads (%d)",
+                    c.n_heads, c.n_kv_heads);
+    if (c.v_from_k != 0 && c.v_from_k != 1) return fail(nullptr, SA_ERR_INVALID_ARG, "v_from_k must be 0 or 1");
+    if (c.v_from_k && c.d_v > c.d_qk)
+        return fail(nullptr, SA_ERR_INVALID_ARG, "v_from_k needs d_v (%d) <= d_qk (%d)", c.d_v, c.d_qk);
+    if (c.max_topk < 1 || c.max_topk > kMaxTopk)
+        return fail(nullptr, SA_ERR_INVALID_ARG, "max_topk must be in [1, %d]", kMaxTopk);
+    if (c.page_size < 1) return fail(nullptr, SA_ERR_INVALID_ARG, "page_size must be >= 1");
+    if (!(c.softmax_scale >= 0.f) || !std::isfinite(c.softmax_scale))
+        return fail(nullptr, SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+
+    sa_handle_s *h = new (std::nothrow) sa_handle_s();
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "out of host memory");
+    h->cfg = c;
+    h->scale = c.softmax_scale > 0.f ? c.softmax_scale : (float)(1.0 / std::sqrt((double)c.d_qk));
+    h->fast_indexer = c.dtype == SA_BF16 && c.n_idx_heads == 64 && c.d_idx == 128;
+    h->fast_attn = c.dtype == SA_BF16 && c.n_heads == 16 && c.n_kv_heads == 1 && c.d_qk == 576 &&
+                   c.d_v == 512 && c.v_from_k == 1;
+    if (!h->fast_indexer && (size_t)(c.n_idx_heads * c.d_idx + c.n_idx_heads) * 4 > 64 * 1024) {
+        delete h;
+        return fail(nullptr, SA_ERR_UNSUPPORTED, "n_idx_heads * d_idx too large for the generic indexer");
+    }
+    if (!h->fast_attn && (size_t)(c.d_qk + c.max_topk) * 4 > 64 * 1024) {
+        delete h;
+        return fail(nullptr, SA_ERR_UNSUPPORTED, "d_qk + max_topk too large for the generic attention");
+    }
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return fail(nullptr, SA_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+    }
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&h->d_err), sizeof(uint32_t));
+    if (e == hipSuccess) e = hipMemset(h->d_err, 0, sizeof(uint32_t));
+    if (e != hipSuccess) {
+        if (h->d_err) (void)hipFree(h->d_err);
+        delete h;
+        return fail(nullptr, SA_ERR_HIP, "allocating the device error word: %s", hipGetErrorString(e));
+    }
+    *out = h;
+    return SA_OK;
+}
+
+void sparse_attn_destroy(sa_handle_t h)
+{
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    (void)sa::drain_profile(*h);
+    for (hipEvent_t e : h->spare_events) (void)hipEventDestroy(e);
+    (void)hipFree(h->d_err);
+    delete h;
+}
+
+sa_status_t sparse_attn_profile(sa_handle_t h, int enable)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    sa_status_t s = hip_status(h, sa::drain_profile(*h), "draining timing events");
+    for (int k = 0; k < SA_KERNEL_COUNT; ++k) {
+        h->total_ms[k] = 0.0;
+        h->launches[k] = 0;
+    }
+    h->profiling = enable != 0;
+    return s;
+}
+
+sa_status_t sparse_attn_profile_read(sa_handle_t h, double *total_ms, int64_t *launches)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    if (!total_ms || !launches) return fail(h, SA_ERR_INVALID_ARG, "NULL output array");
+    sa_status_t s = hip_status(h, sa::drain_profile(*h), "reading timing events");
+    for (int k = 0; k < SA_KERNEL_COUNT; ++k) {
+        total_ms[k] = h->total_ms[k];
+        launches[k] = h->launches[k];
+    }
+    return s;
+}
+
+const char *sparse_attn_last_error(sa_handle_t h)
+{
+    return h ? h->last_error.c_str() : g_create_error.c_str();
+}
+
+sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t max_ctx, size_t *bytes)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    if (!bytes) return fail(h, SA_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    if (n < 1) return fail(h, SA_ERR_INVALID_ARG, "n must be >= 1");
+    switch (op) {
+    case SA_OP_PREFILL:
+        if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "L exceeds int32 token indices");
+        *bytes = prefill_layout(*h, n).total;
+        return SA_OK;
+    case SA_OP_DECODE:
+        if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
+        *bytes = decode_layout(*h, n, max_ctx).total;
+        return SA_OK;
+    case SA_OP_TOPK:
+        *bytes = 0;
+        return SA_OK;
+    default:
+        return fail(h, SA_ERR_INVALID_ARG, "unknown op %d", op);
+    }
+}
+
+sa_status_t sparse_attn_check(sa_handle_t h, void *stream, uint32_t *bits)
+{
+    if (bits) *bits = 0;
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    sa_status_t s = hip_status(h, hipStreamSynchronize(st), "hipStreamSynchronize");
+    if (s != SA_OK) return s;
+    uint32_t v = 0;
+    s = hip_status(h, hipMemcpy(&v, h->d_err, sizeof(v), hipMemcpyDeviceToHost), "reading the error word");
+    if (s != SA_OK) return s;
+    if (bits) *bits = v;
+    if (v == 0) return SA_OK;
+    s = hip_status(h, hipMemset(h->d_err, 0, sizeof(uint32_t)), "clearing the error word");
+    if (s != SA_OK) return s;
+    return fail(h, SA_ERR_DEVICE_CHECK, "device-side check failed, bits 0x%x", v);
+}
+
+sa_status_t indexer_scores(sa_handle_t h, const void *q_idx, const float *w, const void *k_idx,
+                           int64_t L, float *scores, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!q_idx || !w || !k_idx || !scores) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (L < 1) return fail(h, SA_ERR_INVALID_ARG, "L must be >= 1");
+    if (L > kMaxIndexerScoresL)
+        return fail(h, SA_ERR_UNSUPPORTED, "indexer_scores materialises [L, L]; L must be <= %lld",
+                    (long long)kMaxIndexerScoresL);
+    if (!aligned16(q_idx) || !aligned16(k_idx)) return fail(h, SA_ERR_INVALID_ARG, "q_idx/k_idx must be 16-byte aligned");
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    sa::RowSource keys{k_idx, h->cfg.d_idx, nullptr, 0, 0, 0};
+    sa::Visibility vis{0, nullptr, 0};
+    return hip_status(h, sa::launch_indexer(*h, q_idx, w, L, keys, vis, scores, L, L,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                      "indexer launch");
+}
+
+sa_status_t topk_select(sa_handle_t h, const float *scores, int64_t rows, int64_t cols, int64_t ld,
+                        const int32_t *valid_len, const int32_t *k_per_row, int32_t k, int32_t *idx,
+                        void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!scores || !idx) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (rows < 1 || cols < 1) return fail(h, SA_ERR_INVALID_ARG, "rows and cols must be >= 1");
+    if (cols > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "cols exceeds int32 indices");
+    if (rows > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "rows exceeds the launch limit");
+    if (ld < cols) return fail(h, SA_ERR_INVALID_ARG, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+    if (k < 1 || k > h->cfg.max_topk)
+        return fail(h, SA_ERR_INVALID_ARG, "k (%d) must be in [1, max_topk=%d]", k, h->cfg.max_topk);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    return hip_status(h, sa::launch_topk(*h, scores, ld, rows, cols, valid_len, 0, k_per_row, k, idx, k,
+                                         h->d_err, reinterpret_cast<hipStream_t>(stream)),
+                      "top-k launch");
+}
+
+sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, const void *v,
+                                const void *q_idx, const float *w, const void *k_idx, int64_t L,
+                                int32_t topk, float *out, float *lse, int32_t *idx_out, void *ws,
+                                size_t ws_bytes, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    const sa_config_t &c = h->cfg;
+    if (!q || !k || !q_idx || !w || !k_idx || !out) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (c.v_from_k ? v != nullptr : v == nullptr)
+        return fail(h, SA_ERR_INVALID_ARG, c.v_from_k ? "v must be NULL when v_from_k = 1"
+                                                      : "v must not be NULL when v_from_k = 0");
+    if (L < 1 || L > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "L must be in [1, 2^31)");
+    if (topk < 1 || topk > c.max_topk)
+        return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
+    if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(q_idx) || !aligned16(k_idx))
+        return fail(h, SA_ERR_INVALID_ARG, "q, k, v, q_idx and k_idx must be 16-byte aligned");
+    const PrefillLayout lay = prefill_layout(*h, L);
+    if (!ws || ws_bytes < lay.total)
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *base = reinterpret_cast<char *>(ws);
+    float *scores = reinterpret_cast<float *>(base + lay.scores);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
+    const size_t es = elem_size(*h);
+
+    // indexer -> top-k per block of query rows; the block's scores live in the workspace
+    const int64_t chunk = prefill_chunk_rows(L);
+    sa::RowSource keys{k_idx, c.d_idx, nullptr, 0, 0, 0};
+    for (int64_t r0 = 0; r0 < L; r0 += chunk) {
+        const int64_t rows = r0 + chunk < L ? chunk : L - r0;
+        const int64_t cols = r0 + rows;  // keys any row of the block can see
+        sa::Visibility vis{r0, nullptr, 0};
+        s = hip_status(h, sa::launch_indexer(*h, reinterpret_cast<const char *>(q_idx) + r0 * c.n_idx_heads * c.d_idx * es,
+                                             w + r0 * c.n_idx_heads, rows, keys, vis, scores, cols, cols, st),
+                       "indexer launch");
+        if (s != SA_OK) return s;
+        s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
+                                          idx + r0 * topk, topk, h->d_err, st),
+                       "top-k launch");
+        if (s != SA_OK) return s;
+    }
+    sa::RowSource kv{k, (int64_t)c.n_kv_heads * c.d_qk, nullptr, 0, 0, 0};
+    sa::RowSource vv{v, (int64_t)c.n_kv_heads * c.d_v, nullptr, 0, 0, 0};
+    sa::Visibility vis{0, nullptr, 0};
+    sa::Selection sel{idx, topk, topk, nullptr};
+    return hip_status(h, sa::launch_attention(*h, q, L, kv, vv, vis, sel, out, lse, nullptr, st),
+                      "attention launch");
+}
+
+sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                               const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                               const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                               float *out, float *lse, int32_t *idx_out, void *ws, size_t ws_bytes,
+                               void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    const sa_config_t &c = h->cfg;
+    if (!q || !q_idx || !w || !kv_pages || !kidx_pages || !block_table || !ctx_len || !topk || !out)
+        return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (c.v_from_k ? v_pages != nullptr : v_pages == nullptr)
+        return fail(h, SA_ERR_INVALID_ARG, c.v_from_k ? "v_pages must be NULL when v_from_k = 1"
+                                                      : "v_pages must not be NULL when v_from_k = 0");
+    if (B < 1) return fail(h, SA_ERR_INVALID_ARG, "B must be >= 1");
+    if (n_pages < 1) return fail(h, SA_ERR_INVALID_ARG, "n_pages must be >= 1");
+    if (max_blocks < 1) return fail(h, SA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+    if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)max_blocks * c.page_size)
+        return fail(h, SA_ERR_INVALID_ARG, "max_ctx (%d) must be in [1, max_blocks * page_size = %lld]",
+                    max_ctx, (long long)max_blocks * c.page_size);
+    if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
+        (v_pages && !aligned16(v_pages)))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+    const DecodeLayout lay = decode_layout(*h, B, max_ctx);
+    if (!ws || ws_bytes < lay.total)
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *base = reinterpret_cast<char *>(ws);
+    float *scores = reinterpret_cast<float *>(base + lay.scores);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
+
+    sa::RowSource keys{kidx_pages, c.d_idx, block_table, max_blocks, c.page_size, n_pages};
+    sa::Visibility vis{0, ctx_len, max_ctx};
+    s = hip_status(h, sa::launch_indexer(*h, q_idx, w, B, keys, vis, scores, max_ctx, max_ctx, st),
+                   "indexer launch");
+    if (s != SA_OK) return s;
+    s = hip_status(h, sa::launch_topk(*h, scores, max_ctx, B, max_ctx, ctx_len, 0, topk, c.max_topk, idx,
+                                      c.max_topk, h->d_err, st),
+                   "top-k launch");
+    if (s != SA_OK) return s;
+    sa::RowSource kv{kv_pages, (int64_t)c.n_kv_heads * c.d_qk, block_table, max_blocks, c.page_size, n_pages};
+    sa::RowSource vv{v_pages, (int64_t)c.n_kv_heads * c.d_v, block_table, max_blocks, c.page_size, n_pages};
+    sa::Selection sel{idx, c.max_topk, c.max_topk, topk};
+    return hip_status(h, sa::launch_attention(*h, q, B, kv, vv, vis, sel, out, lse, base + lay.attn, st),
+                      "attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Host-side internals of libsparse_attn: the handle and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/sparse_attn.h"
+
+struct sa_handle_s {
+    sa_config_t cfg;
+    float scale;            // resolved attention logit scale
+    uint32_t *d_err;        // device error word (SA_DEVERR_* bits)
+    int device;
+    bool fast_indexer;      // bf16, H_I = 64, d_I = 128: MFMA indexer kernels
+    bool fast_attn;         // bf16, H = 16, H_kv = 1, d_qk = 576, d_v = 512, v_from_k
+    std::string last_error;
+
+    // kernel timing (sparse_attn_profile)
+    bool profiling = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[SA_KERNEL_COUNT];
+    std::vector<hipEvent_t> spare_events;
+    double total_ms[SA_KERNEL_COUNT] = {};
+    int64_t launches[SA_KERNEL_COUNT] = {};
+};
+
+namespace sa {
+
+// Brackets one kernel launch with events while the handle is profiling.
+class KernelTimer {
+public:
+    KernelTimer(sa_handle_s &h, int kind, hipStream_t st);
+    ~KernelTimer();
+
+private:
+    sa_handle_s &h_;
+    int kind_;
+    hipStream_t st_;
+    hipEvent_t start_ = nullptr;
+};
+
+// Synchronise on and account every pending event pair.
+hipError_t drain_profile(sa_handle_s &h);
+
+// Where the index keys / KV rows of a query row live.
+//  contiguous: row s of sequence = base + s * row_elems
+//  paged:      token s of sequence b = pool page block_table[b * max_blocks + s / page_size],
+//              slot s % page_size; pages hold page_size rows of row_elems elements.
+struct RowSource {
+    const void *base;
+    int64_t row_elems;              // elements per token row
+    const int32_t *block_table;     // nullptr -> contiguous
+    int32_t max_blocks;
+    int32_t page_size;
+    int64_t n_pages;
+};
+
+// Which keys a query row sees: keys s < visible(r), where visible(r) = causal_row0 + r + 1
+// (prefill) or ctx_len[r] (decode; must lie in [1, max_ctx]).
+struct Visibility {
+    int64_t causal_row0;
+    const int32_t *ctx_len;         // nullptr -> causal rule
+    int32_t max_ctx;
+};
+
+// ---- indexer: scores[r, s] for s < n_cols; s >= visible(r) gets -inf -------------------
+hipError_t launch_indexer(sa_handle_s &h, const void *q_idx, const float *w,
+                          int64_t n_rows, RowSource keys, Visibility vis, float *scores,
+                          int64_t ld, int64_t n_cols, hipStream_t st);
+
+// ---- per-row top-k over materialised scores ----------------------------------------------
+// valid(r) = valid_len ? valid_len[r] : min(causal_row0 + r + 1, cols); k(r) = k_per_row ?
+// k_per_row[r] : k.  idx row r gets the min(k(r), valid(r)) best columns ascending, -1 pad.
+hipError_t launch_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t rows, int64_t cols,
+                       const int32_t *valid_len, int64_t causal_row0, const int32_t *k_per_row,
+                       int32_t k, int32_t *idx, int64_t idx_ld, uint32_t *err, hipStream_t st);
+
+// ---- attention over selected rows --------------------------------------------------------
+// Query row r attends to the first m(r) = min(k(r), visible(r)) entries of idx row r.
+struct Selection {
+    const int32_t *idx;
+    int64_t idx_ld;
+    int32_t k;                      // k(r) = k_per_row ? k_per_row[r] : k
+    const int32_t *k_per_row;
+};
+
+hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows,
+                            RowSource kv, RowSource v, Visibility vis, Selection sel,
+                            float *out, float *lse, void *ws, hipStream_t st);
+
+// Workspace bytes launch_attention needs for n_rows decode rows (split partials).
+size_t attention_workspace(const sa_handle_s &h, int64_t n_rows, bool decode);
+
+}  // namespace sa
