@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of indexer-selected sparse attention on one MI355X.
+
+One step = one causal prefill of a 131072-token sequence (indexer scores of every causal
+pair, per-query top-2048, attention over the selected rows) plus one decode step of 64
+sequences at 131072 tokens of paged context (indexer over the whole context, top-2048,
+attention over the selected rows of the paged cache).  Inputs are seeded synthetic data
+resident in HBM before timing starts.
+
+Prints one JSON line: `value` is prefill tokens/s at 128K context; decode tokens/s, the
+per-kernel times (HIP events recorded by the library on the launch stream), the roofline
+of the dominant kernel and the CPU oracle's throughput on a bounded sample ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode tokens/s and prefill tokens/s at 128K ctx, top-k=2048; % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--prefill-len", type=int, default=131072)
+    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-ctx", type=int, default=131072)
+    ap.add_argument("--topk", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build runs the per-GPU share of the path and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import indexer_selected_sparse_scores_amd as sa
+    from indexer_selected_sparse_scores_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    L, B, N, K = args.prefill_len, args.decode_batch, args.decode_ctx, args.topk
+
+    pre_wl = inputs.small(inputs.WORKLOADS["prefill_128k"], L=L, topk=K)
+    dec_wl = inputs.small(inputs.WORKLOADS["decode_b64_128k"], B=B, ctx_range=(N, N), topk=K)
+    cfg = inputs.library_config(pre_wl, max_topk=K)
+
+    log(f"[bench] generating prefill inputs L={L}")
+    P = inputs.prefill_inputs(pre_wl, dev)
+    log(f"[bench] generating decode inputs B={B} ctx={N}")
+    D = inputs.decode_inputs(dec_wl, dev)
+    torch.cuda.synchronize()
+
+    h_pre = sa.Handle(cfg)
+    h_dec = sa.Handle(cfg)
+    s = cfg
+    out_p = torch.empty((L, s.n_heads, s.d_v), device=dev)
+    lse_p = torch.empty((L, s.n_heads), device=dev)
+    idx_p = torch.empty((L, K), device=dev, dtype=torch.int32)
+    ws_p = sa.workspace(h_pre, sa.SA_OP_PREFILL, L)
+    out_d = torch.empty((B, s.n_heads, s.d_v), device=dev)
+    lse_d = torch.empty((B, s.n_heads), device=dev)
+    idx_d = torch.empty((B, K), device=dev, dtype=torch.int32)
+    ws_d = sa.workspace(h_dec, sa.SA_OP_DECODE, B, D["max_ctx"])
+
+    def prefill():
+        sa.sparse_attn_prefill(h_pre, P["q"], P["k"], None, P["q_idx"], P["w"], P["k_idx"], K,
+                               out_p, lse_p, idx_p, ws_p)
+
+    def decode():
+        sa.sparse_attn_decode(h_dec, D["q"], D["q_idx"], D["w"], D["kv_pages"], None, D["kidx_pages"],
+                              D["block_table"], D["ctx_len"], D["topk"], D["max_ctx"], out_d, lse_d,
+                              idx_d, ws_d)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+    sa.sparse_attn_check(h_pre)
+    sa.sparse_attn_check(h_dec)
+
+    profile = not args.no_profile
+    if profile:
+        sa.sparse_attn_profile(h_pre, True)
+        sa.sparse_attn_profile(h_dec, True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[3 * i].record()
+        prefill()
+        ev[3 * i + 1].record()
+        decode()
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)) / args.steps
+    dec_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)) / args.steps
+    kern_pre = sa.sparse_attn_profile_read(h_pre) if profile else {}
+    kern_dec = sa.sparse_attn_profile_read(h_dec) if profile else {}
+    sa.sparse_attn_check(h_pre)
+    sa.sparse_attn_check(h_dec)
+    log(f"[bench] prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms per step (wall {wall:.2f} s)")
+
+    # algorithmic work (per step)
+    pairs = L * (L + 1) // 2
+    idx_flops = pairs * 2 * s.n_idx_heads * s.d_idx
+    ctx_total = int(D["ctx_np"].sum())
+    dec_idx_bytes = ctx_total * s.d_idx * 2
+    sel_rows = int(np.minimum(D["ctx_np"], K).sum())
+    dec_gather_bytes = sel_rows * s.d_qk * 2
+
+    def per_launch(kern, kind):
+        ms, n = kern.get(kind, (0.0, 0))
+        return (ms / n, n, ms) if n else (None, 0, 0.0)
+
+    kernels = {}
+    roofline = roofline_dec = None
+    if profile:
+        for name, kern in (("prefill", kern_pre), ("decode", kern_dec)):
+            for kind in sa.KERNEL_KINDS:
+                avg, n, tot = per_launch(kern, kind)
+                if n:
+                    kernels[f"{name}.{kind}"] = {"launches_per_step": n / args.steps,
+                                                 "avg_ms": round(avg, 5),
+                                                 "ms_per_step": round(tot / args.steps, 4)}
+        avg, n, tot = per_launch(kern_pre, "indexer")
+        if n:
+            tflops = idx_flops * args.steps / (tot * 1e-3) / 1e12
+            roofline = {"kernel": "indexer_mfma_kernel (prefill)", "bound": "mfma",
+                        "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "algorithmic_per_step": f"{idx_flops:.4g} flop = {pairs} causal pairs x "
+                                                f"{2 * s.n_idx_heads * s.d_idx} flop"}
+        avg, n, tot = per_launch(kern_dec, "indexer")
+        if n:
+            gbs = dec_idx_bytes * args.steps / (tot * 1e-3) / 1e9
+            roofline_dec = {"kernel": "indexer_mfma_kernel (paged decode)", "bound": "hbm",
+                            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                            "algorithmic_per_step": f"{dec_idx_bytes} B = {ctx_total} context tokens x "
+                                                    f"{s.d_idx * 2} B of index key"}
+        avg, n, tot = per_launch(kern_dec, "attention")
+        if n:
+            gbs = dec_gather_bytes * args.steps / (tot * 1e-3) / 1e9
+            kernels["decode.attention"]["achieved_GBs"] = round(gbs, 1)
+            kernels["decode.attention"]["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(P, pre_wl, K, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": round(L / (pre_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre_ms + dec_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill L={L} + decode B={B} ctx={N}", "topk": K,
+                   "index_heads": s.n_idx_heads, "d_index": s.d_idx, "heads": s.n_heads,
+                   "d_qk": s.d_qk, "d_v": s.d_v, "page_size": s.page_size,
+                   "prefill_workload": "prefill_128k", "decode_workload": "decode_b64_128k"},
+        "prefill_tokens_per_s": round(L / (pre_ms * 1e-3), 1),
+        "decode_tokens_per_s": round(B / (dec_ms * 1e-3), 1),
+        "prefill_ms": round(pre_ms, 4),
+        "decode_ms": round(dec_ms, 4),
+        "roofline": roofline,
+        "roofline_decode": roofline_dec,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    h_pre.close()
+    h_dec.close()
+
+
+def cpu_baseline(P, wl, K, seconds):
+    """The oracle as it stands, on a bounded sample of the prefill workload: uniformly drawn
+    query rows, each scored against all of its preceding keys, top-k selected and attended.
+    Uniform rows have the average causal length, so rows/s estimates prefill tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    L = P["q"].shape[0]
+    d_qk = P["q"].shape[-1]
+    d_v = 512 if wl.shapes.latent else wl.shapes.d_v
+    rng = np.random.default_rng(20261202)
+    k_idx = P["k_idx"].float().cpu().numpy()
+    kv = P["k"].float().cpu().numpy()
+    threads = oracle.num_threads()
+
+    def run(n):
+        rows = np.sort(rng.integers(0, L, n))
+        sel = torch.as_tensor(rows, device=P["q"].device)
+        q_idx = P["q_idx"][sel].float().cpu().numpy()
+        w = P["w"][sel].float().cpu().numpy()
+        q = P["q"][sel].float().cpu().numpy()
+        t0 = time.perf_counter()
+        sc = oracle.indexer_scores(q_idx, w, k_idx, rows + 1)
+        idx = oracle.topk(sc, rows + 1, K)
+        oracle.attention_rows(q, kv, None, idx, oracle.default_scale(d_qk), d_v=d_v)
+        return time.perf_counter() - t0
+
+    log(f"[bench] cpu baseline: oracle on sampled rows (~{seconds:.0f} s, {threads} threads)")
+    n0 = max(2, threads // 2)
+    t0 = run(n0)
+    n = int(min(4096, max(n0, n0 * seconds / max(t0, 1e-3))))
+    t = run(n)
+    return {"value": round(n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} uniformly drawn query rows of the L={L} prefill (indexer over all "
+                      f"preceding keys, top-{K}, attention), {t:.1f} s on {threads} threads"}
+
+
+if __name__ == "__main__":
+    main()
