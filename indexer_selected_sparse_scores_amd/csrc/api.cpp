@@ -71,9 +71,17 @@ struct PrefillLayout {
     size_t scores, idx, total;
 };
 
+// Fast path (bf16, 64 x 128 indexer): [idx | fused indexer/top-k workspace].
+// Generic path: [scores of one block of query rows | idx].
 PrefillLayout prefill_layout(const sa_handle_s &h, int64_t L)
 {
     PrefillLayout p;
+    if (h.fast_indexer) {
+        p.idx = 0;
+        p.scores = align_up((size_t)L * (size_t)h.cfg.max_topk * sizeof(int32_t));
+        p.total = p.scores + align_up(sa::prefill_topk_workspace(h, L));
+        return p;
+    }
     p.scores = 0;
     p.idx = align_up((size_t)prefill_chunk_rows(L) * (size_t)L * sizeof(float));
     p.total = p.idx + align_up((size_t)L * (size_t)h.cfg.max_topk * sizeof(int32_t));
@@ -197,7 +205,9 @@ sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
         delete h;
         return fail(nullptr, SA_ERR_UNSUPPORTED, "d_qk + max_topk too large for the generic attention");
     }
-    if (hipGetDevice(&h->device) != hipSuccess) {
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
+        h->n_cu < 1) {
         delete h;
         return fail(nullptr, SA_ERR_HIP, "hipGetDevice failed (no HIP device?)");
     }
@@ -359,21 +369,28 @@ sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, con
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
     const size_t es = elem_size(*h);
 
-    // indexer -> top-k per block of query rows; the block's scores live in the workspace
-    const int64_t chunk = prefill_chunk_rows(L);
-    sa::RowSource keys{k_idx, c.d_idx, nullptr, 0, 0, 0};
-    for (int64_t r0 = 0; r0 < L; r0 += chunk) {
-        const int64_t rows = r0 + chunk < L ? chunk : L - r0;
-        const int64_t cols = r0 + rows;  // keys any row of the block can see
-        sa::Visibility vis{r0, nullptr, 0};
-        s = hip_status(h, sa::launch_indexer(*h, reinterpret_cast<const char *>(q_idx) + r0 * c.n_idx_heads * c.d_idx * es,
-                                             w + r0 * c.n_idx_heads, rows, keys, vis, scores, cols, cols, st),
-                       "indexer launch");
+    if (h->fast_indexer) {
+        // fused indexer + streaming top-k: no score matrix at all
+        s = hip_status(h, sa::launch_prefill_topk(*h, q_idx, w, k_idx, L, topk, idx, base + lay.scores, st),
+                       "indexer/top-k launch");
         if (s != SA_OK) return s;
-        s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
-                                          idx + r0 * topk, topk, h->d_err, st),
-                       "top-k launch");
-        if (s != SA_OK) return s;
+    } else {
+        // indexer -> top-k per block of query rows; the block's scores live in the workspace
+        const int64_t chunk = prefill_chunk_rows(L);
+        sa::RowSource keys{k_idx, c.d_idx, nullptr, 0, 0, 0};
+        for (int64_t r0 = 0; r0 < L; r0 += chunk) {
+            const int64_t rows = r0 + chunk < L ? chunk : L - r0;
+            const int64_t cols = r0 + rows;  // keys any row of the block can see
+            sa::Visibility vis{r0, nullptr, 0};
+            s = hip_status(h, sa::launch_indexer(*h, reinterpret_cast<const char *>(q_idx) + r0 * c.n_idx_heads * c.d_idx * es,
+                                                 w + r0 * c.n_idx_heads, rows, keys, vis, scores, cols, cols, st),
+                           "indexer launch");
+            if (s != SA_OK) return s;
+            s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
+                                              idx + r0 * topk, topk, h->d_err, st),
+                           "top-k launch");
+            if (s != SA_OK) return s;
+        }
     }
     sa::RowSource kv{k, (int64_t)c.n_kv_heads * c.d_qk, nullptr, 0, 0, 0};
     sa::RowSource vv{v, (int64_t)c.n_kv_heads * c.d_v, nullptr, 0, 0, 0};

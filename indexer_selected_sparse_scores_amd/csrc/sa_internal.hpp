@@ -15,6 +15,7 @@ struct sa_handle_s {
     float scale;            // resolved attention logit scale
     uint32_t *d_err;        // device error word (SA_DEVERR_* bits)
     int device;
+    int n_cu;               // compute units of the device (sizes persistent grids)
     bool fast_indexer;      // bf16, H_I = 64, d_I = 128: MFMA indexer kernels
     bool fast_attn;         // bf16, H = 16, H_kv = 1, d_qk = 576, d_v = 512, v_from_k
     std::string last_error;
@@ -90,6 +91,12 @@ struct Selection {
 hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows,
                             RowSource kv, RowSource v, Visibility vis, Selection sel,
                             float *out, float *lse, void *ws, hipStream_t st);
+
+// ---- fused prefill indexer + streaming top-k (bf16, H_I = 64, d_I = 128) ---------------
+// idx [L, topk] gets every row's selection; ws holds prefill_topk_workspace(h, L) bytes.
+size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L);
+hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
+                               int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st);
 
 // Workspace bytes launch_attention needs for n_rows decode rows (split partials).
 size_t attention_workspace(const sa_handle_s &h, int64_t n_rows, bool decode);

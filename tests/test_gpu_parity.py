@@ -48,20 +48,19 @@ def _prefill(h, d, topk, want_lse=True):
 
 
 def _check_prefill_rows(d, out, lse, idx, topk, rows, latent, d_v, what):
-    q_idx, w, k_idx = to_np(d["q_idx"]), to_np(d["w"]), to_np(d["k_idx"])
     rows = np.asarray(rows, dtype=np.int64)
-    sc = oracle.indexer_scores(q_idx[rows], w[rows], k_idx, rows + 1)
-    gi = to_np(idx)
+    rt = torch.as_tensor(rows, device=d["q"].device)
+    sub = lambda t: to_np(t[rt])  # only the sampled rows leave the device
+    sc = oracle.indexer_scores(sub(d["q_idx"]), sub(d["w"]), to_np(d["k_idx"]), rows + 1)
+    gi = sub(idx)
     diffs = 0
     for i, t in enumerate(rows):
         m = min(topk, t + 1)
-        diffs += check_topk_row(gi[t], sc[i], m, t + 1, what=f"{what} row {t}")
-    sel = gi[rows]
-    ref_out, ref_lse = oracle.attention_rows(to_np(d["q"])[rows], to_np(d["k"]),
-                                             None if latent else to_np(d["v"]), sel,
+        diffs += check_topk_row(gi[i], sc[i], m, t + 1, what=f"{what} row {t}")
+    ref_out, ref_lse = oracle.attention_rows(sub(d["q"]), to_np(d["k"]),
+                                             None if latent else to_np(d["v"]), gi,
                                              oracle.default_scale(d["q"].shape[-1]), d_v=d_v)
-    err = check_attention(to_np(out)[rows], None if lse is None else to_np(lse)[rows], ref_out,
-                          ref_lse, what=what)
+    err = check_attention(sub(out), None if lse is None else sub(lse), ref_out, ref_lse, what=what)
     say(f"{what}: rows={len(rows)} near-tie set diffs={diffs} max|dO|={err:.2e}")
     return diffs
 
@@ -194,6 +193,55 @@ def test_prefill_8k_sampled():
     rows = np.unique(np.concatenate([[0, 1, 2, 100, 2046, 2047, 2048, 2049, 4000, 8190, 8191],
                                      np.random.default_rng(8).integers(0, wl.L, 37)]))
     _check_prefill_rows(d, out, lse, idx, wl.topk, rows, latent=True, d_v=512, what="8k")
+
+
+@pytest.mark.parametrize("L,topk", [(2051, 256), (4100, 2048)])
+def test_prefill_latent_ragged(L, topk):
+    """Several 8-row tiles and 64-key tiles with ragged tails; rows below and above k."""
+    wl = inputs.WORKLOADS["prefill_8k"]
+    say(f"prefill latent ragged L={L} topk={topk}")
+    d = inputs.prefill_inputs(wl, DEV, L=L, seed=L + 1)
+    with sa.Handle(inputs.library_config(wl, max_topk=topk)) as h:
+        out, lse, idx = _prefill(h, d, topk)
+    rows = np.unique(np.concatenate([np.arange(0, 9), [topk - 2, topk - 1, topk, topk + 1],
+                                     np.arange(L - 9, L),
+                                     np.random.default_rng(L).integers(0, L, 24)]))
+    _check_prefill_rows(d, out, lse, idx, topk, rows, latent=True, d_v=512, what=f"ragged L={L}")
+
+
+def test_prefill_all_scores_tied():
+    """q_idx = 0 makes every score exactly 0: the selection is the lowest k indices.  Rows
+    past 8192 keys have more tied candidates than the on-chip buffer holds."""
+    wl = inputs.WORKLOADS["prefill_8k"]
+    L, topk = 8300, 512
+    say(f"prefill all-tied scores L={L} topk={topk}")
+    d = inputs.prefill_inputs(wl, DEV, L=L, seed=77)
+    d["q_idx"] = torch.zeros_like(d["q_idx"])
+    with sa.Handle(inputs.library_config(wl, max_topk=topk)) as h:
+        out, lse, idx = _prefill(h, d, topk)
+    gi = to_np(idx)
+    for t in (0, 5, topk - 1, topk, 4000, 8191, 8192, 8250, L - 1):
+        m = min(topk, t + 1)
+        assert np.array_equal(gi[t][:m], np.arange(m)), f"row {t}"
+        assert np.all(gi[t][m:] == -1)
+    rows = np.array([0, topk, 8192, L - 1])
+    _check_prefill_rows(d, out, lse, idx, topk, rows, latent=True, d_v=512, what="all-tied")
+
+
+def test_prefill_128k_sampled():
+    """The 131072-token prefill exactly as the benchmark runs it, checked on sampled rows."""
+    wl = inputs.WORKLOADS["prefill_128k"]
+    say(f"prefill prefill_128k L={wl.L} topk={wl.topk} (sampled rows)")
+    d = inputs.prefill_inputs(wl, DEV)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _prefill(h, d, wl.topk)
+    sal = d["salient"]
+    rows = np.unique(np.concatenate([[0, 2047, 2048, 65535, wl.L - 2, wl.L - 1],
+                                     sal[[0, len(sal) // 2, -1]] + 1,
+                                     np.random.default_rng(128).integers(0, wl.L, 6)]))
+    _check_prefill_rows(d, out, lse, idx, wl.topk, rows, latent=True, d_v=512, what="128k")
+    del out, lse, idx, d
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------------------
