@@ -8,15 +8,15 @@
 // cache are read (that page, section 2.3).
 //
 // attn_latent_mfma_kernel serves the latent layout (bf16, 16 heads sharing one 576-wide
-// row per token whose first 512 columns are the value).  A 256-thread workgroup gathers 64
-// selected rows at a time into LDS with 16-byte loads (1152 bytes per row, read once for
-// all 16 heads), computes the 16 x 64 logits with v_mfma_f32_16x16x32_bf16 (each wave
-// takes 16 rows), keeps an online softmax (running max / sum per head, exp2 with the log2(e)
-// factor folded into the scale), and accumulates P.V with the same MFMA, each wave owning
-// 128 of the 512 value columns.  P enters the MFMA as a bf16 hi part plus a bf16 residual,
-// so the weights keep ~16 mantissa bits.  In decode the selected rows of one sequence are
-// split across workgroups and a second kernel merges the partial (max, sum, accumulator)
-// states.
+// row per token whose first 512 columns are the value).  A 512-thread workgroup walks the
+// selected rows of one query in chunks of 64, gathered into LDS with 16-byte loads (1152
+// bytes per row, read once for all 16 heads); the next chunk's gather is in flight in
+// registers while the current one is computed.  Logits and P.V run on
+// v_mfma_f32_16x16x32_bf16 with an online softmax (running max / sum per head, exp2 with the
+// log2(e) factor folded into the scale).  P enters the MFMA as a bf16 hi part plus a bf16
+// residual, so the weights keep ~16 mantissa bits.  In decode the selected rows of one
+// sequence are split across workgroups and a second kernel merges the partial (max, sum,
+// accumulator) states.
 //
 // attn_generic_kernel serves every other shape (fp32 or bf16): one workgroup per (row,
 // head), logits in LDS, two-pass softmax.
@@ -64,21 +64,71 @@ constexpr int kLH = 16;         // query heads
 constexpr int kLDqk = 576;      // key width
 constexpr int kLDv = 512;       // value width (leading columns of the key row)
 constexpr int kChunk = 64;      // selected rows per LDS chunk
+constexpr int kAThreads = 512;  // 8 waves
 constexpr int kRowBytes = kLDqk * 2;
-constexpr int kLdsRow = kRowBytes + 16;   // padded LDS row stride (bytes)
-constexpr int kPieces = kRowBytes / 16;   // 16-byte pieces per row
-constexpr int kLoadIters = kChunk * kPieces / 256;
-static_assert(kChunk * kPieces % 256 == 0, "chunk load must tile the workgroup");
+constexpr int kLdsRow = kRowBytes + 16;                 // padded LDS row stride (bytes)
+constexpr int kPieces = kRowBytes / 16;                 // 16-byte pieces per row (72)
+constexpr int kGather = kChunk * kPieces / kAThreads;   // pieces each thread moves per chunk (9)
+constexpr int kKSteps = kLDqk / 32;                     // 18 k-steps of the logits MFMA
+constexpr int kKHalf = kKSteps / 2;                     // each wave group takes half of them
+constexpr int kLogitLd = kChunk + 4;                    // padded per-head row of logits (floats)
+static_assert(kChunk * kPieces % kAThreads == 0, "chunk gather must tile the workgroup");
 
+struct AttnShared {
+    unsigned char rows[kChunk * kLdsRow];   // gathered rows of the current chunk
+    float logits[2][kLH * kLogitLd];        // partial logits of the two K-halves, [head][slot]
+    int64_t row_off[2][kChunk];             // element offsets of a chunk's rows (-1: none)
+};
+
+// Element offset of selected slot j of query row r, -1 if the slot is unused or invalid.
+__device__ __forceinline__ int64_t slot_offset(const RowSource &kv, const int32_t *idx_row, int64_t r,
+                                               int64_t j, int64_t j_end, int64_t visible, uint32_t *err)
+{
+    if (j >= j_end) return -1;
+    const int64_t s = idx_row[j];
+    if (s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
+    if (s < 0 || s >= visible) return -1;
+    const int64_t off = token_offset(kv, r, s);
+    if (off < 0) flag_error(err, SA_DEVERR_BLOCK_TABLE);
+    return off;
+}
+
+// The P.V contraction runs over the 64 rows of a chunk in an order of our choosing, as long
+// as P and V agree.  MFMA k index 8 g + j (lane group g = lane / 16, j = 0..7) of a 32-row
+// half is row 8 g + 2 j (j < 4) or 8 g + 2 (j - 4) + 1 (j >= 4): the V fragment is then two
+// transposing LDS reads over rows two apart, which fall in disjoint banks.  slot_of_row
+// inverts the map; logits are stored at their slot so that P is read in k order.
+__device__ __forceinline__ int slot_of_row(int row)
+{
+    const int w = row & 7;
+    return (row & ~7) | ((w & 1) << 2) | (w >> 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Lane l of each 16-lane group gets column c0 + l % 16 of the 4 rows whose 8-byte pieces the
+// group's lanes point at (ds_read_b64_tr_b16: lane i, element e comes from element i % 4 of
+// the row addressed by lane 4 e + i / 4).
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(reinterpret_cast<uintptr_t>(p)));
+}
+
+// One workgroup = one query row (all 16 heads) and a range of its selected rows, processed
+// in chunks of 64 rows.  The gather of chunk c+1 (16-byte loads into registers), the page
+// lookup of chunk c+2 and the index of chunk c+3 are in flight while chunk c is computed from
+// LDS: logits on v_mfma_f32_16x16x32_bf16 (waves 0-3 and 4-7 take the two halves of the
+// 576-wide contraction for 16 rows each), an online softmax per head (exp2, log2(e) folded
+// into the scale), and P.V on the same MFMA with P split into bf16 hi + lo parts (each wave
+// owns 64 of the 512 value columns).
 template <bool kSplit>
-__global__ __launch_bounds__(256, 2) void attn_latent_mfma_kernel(
+__global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
     const uint16_t *__restrict__ q, int64_t n_rows, RowSource kv, Visibility vis, Selection sel,
     float scale_log2, float *__restrict__ out, float *__restrict__ lse, int split_rows, int n_splits,
     float *__restrict__ part_o, float *__restrict__ part_ml, uint32_t *err)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char rows_lds[kChunk * kLdsRow];
-    __shared__ float s_lds[kLH * kChunk];
-    __shared__ int64_t row_off[kChunk];
+    __shared__ __attribute__((aligned(16))) AttnShared sh;
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int hh = lane % 16, grp = lane / 16;
@@ -93,69 +143,107 @@ __global__ __launch_bounds__(256, 2) void attn_latent_mfma_kernel(
     if (kSplit && j_begin >= m) return;  // the merge kernel ignores unused splits
     const int32_t *idx_row = sel.idx + r * sel.idx_ld;
     const uint16_t *kv_base = reinterpret_cast<const uint16_t *>(kv.base);
+    const int n_chunks = (int)((j_end - j_begin + kChunk - 1) / kChunk);
 
-    // A operand of Q.K^T: head hh, dims 32*ks + 8*grp .. +7
-    bf16x8 qa[kLDqk / 32];
+    // logits: wave w covers rows 16 (w % 4) .. +15 and k-steps 9 (w / 4) .. +8
+    const int nt_qk = wave & 3, kh = wave >> 2;
+    bf16x8 qa[kKHalf];
     const uint16_t *qr = q + (r * kLH + hh) * kLDqk;
 #pragma unroll
-    for (int ks = 0; ks < kLDqk / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks + 8 * grp));
+    for (int i = 0; i < kKHalf; ++i) qa[i] = as_bf16x8(load16(qr + 32 * (kKHalf * kh + i) + 8 * grp));
+
+    // offsets of chunks 0 and 1; the index of chunk 2 waits in a register
+    int64_t pend_j = j_begin + 2 * kChunk + tid;   // slot whose index `pend_s` holds
+    int64_t pend_s = -1;
+    if (tid < kChunk) {
+        sh.row_off[0][tid] = slot_offset(kv, idx_row, r, j_begin + tid, j_end, visible, err);
+        sh.row_off[1][tid] = slot_offset(kv, idx_row, r, j_begin + kChunk + tid, j_end, visible, err);
+        if (pend_j < j_end) pend_s = idx_row[pend_j];
+    }
+    __syncthreads();
+    uint4 g[kGather];
+    auto gather = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kGather; ++u) {
+            const int pc = tid + kAThreads * u;
+            const int64_t off = sh.row_off[buf][pc / kPieces];
+            g[u] = off >= 0 ? load16(kv_base + off + (pc % kPieces) * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int u = 0; u < kGather; ++u) {
+            const int pc = tid + kAThreads * u;
+            *reinterpret_cast<uint4 *>(sh.rows + (pc / kPieces) * kLdsRow + (pc % kPieces) * 16) = g[u];
+        }
+    };
+    gather(0);
+    stash();
 
     const float neg_inf = -__builtin_inff();
     float m_run = neg_inf, l_run = 0.f;   // softmax state of head hh (log2 domain)
-    f32x4 acc[8];                         // O[4*grp + i][128*wave + 16*nt + hh]
+    f32x4 acc[4];                         // O[4 grp + i][64 wave + 16 nt + hh]
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll 1
-    for (int64_t c = j_begin; c < j_end; c += kChunk) {
-        if (tid < kChunk) {
-            int64_t j = c + tid, off = -1;
-            if (j < j_end) {
-                int64_t s = idx_row[j];
-                if (s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
-                if (s >= 0 && s < visible) {
-                    off = token_offset(kv, r, s);
-                    if (off < 0) flag_error(err, SA_DEVERR_BLOCK_TABLE);
+    for (int c = 0; c < n_chunks; ++c) {
+        __syncthreads();  // rows = chunk c, row_off[c & 1] = chunk c, row_off[(c + 1) & 1] = chunk c + 1
+        const bool more = c + 1 < n_chunks;
+        // Slot pend_j (chunk c + 2): its index arrived during the previous chunk; its page
+        // lookup and the index of chunk c + 3 are issued before this chunk's gather loads, so
+        // the memory counter reaches them first, and they are consumed after the compute.
+        int64_t off_next = -1;
+        int32_t page = 0;
+        bool page_pending = false;
+        if (tid < kChunk && pend_j < j_end) {
+            if (pend_s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
+            if (pend_s >= 0 && pend_s < visible) {
+                if (kv.block_table) {
+                    page = kv.block_table[r * kv.max_blocks + pend_s / kv.page_size];
+                    page_pending = true;
+                } else {
+                    off_next = pend_s * kv.row_elems;
                 }
             }
-            row_off[tid] = off;
         }
-        __syncthreads();
-        // gather the chunk: 64 rows x 72 pieces of 16 bytes, zero rows for unused slots
-#pragma unroll
-        for (int it = 0; it < kLoadIters; ++it) {
-            const int p = tid + 256 * it;
-            const int row = p / kPieces, piece = p % kPieces;
-            const int64_t off = row_off[row];
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (off >= 0) v = load16(kv_base + off + piece * 8);
-            *reinterpret_cast<uint4 *>(rows_lds + row * kLdsRow + piece * 16) = v;
-        }
-        __syncthreads();
+        const int64_t s_next = pend_s;
+        pend_j += kChunk;
+        pend_s = -1;
+        if (tid < kChunk && pend_j < j_end) pend_s = idx_row[pend_j];
+        if (more) gather((c + 1) & 1);
 
-        // logits of rows 16*wave .. +15 for all 16 heads
+        // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh
         {
             f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-            const unsigned char *kb = rows_lds + (16 * wave + hh) * kLdsRow + 16 * grp;
+            const int row = 16 * nt_qk + hh;
+            const unsigned char *kb = sh.rows + row * kLdsRow + 16 * grp + 64 * kKHalf * kh;
 #pragma unroll
-            for (int ks = 0; ks < kLDqk / 32; ++ks) {
-                bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 64 * ks));
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc, 0, 0, 0);
+            for (int i = 0; i < kKHalf; ++i) {
+                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 64 * i));
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], b, sacc, 0, 0, 0);
             }
-            const int row = 16 * wave + hh;
-            const bool valid = row_off[row] >= 0;
+            const bool valid = sh.row_off[c & 1][row] >= 0;
+            const int slot = slot_of_row(row);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s_lds[(4 * grp + i) * kChunk + row] = valid ? sacc[i] * scale_log2 : neg_inf;
+            for (int i = 0; i < 4; ++i) sh.logits[kh][(4 * grp + i) * kLogitLd + slot] = valid ? sacc[i] : neg_inf;
         }
         __syncthreads();
 
         // online softmax update for head hh over the 64 rows (identical in every wave)
-        float p[16];
+        float p[16];  // p[8 ks + j]: MFMA k index 32 ks + 8 grp + j
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) p[8 * ks + i] = s_lds[hh * kChunk + 32 * ks + 8 * grp + i];
+            for (int h4 = 0; h4 < 2; ++h4) {
+                const int e = hh * kLogitLd + 32 * ks + 8 * grp + 4 * h4;
+                const float4 x0 = *reinterpret_cast<const float4 *>(&sh.logits[0][e]);
+                const float4 x1 = *reinterpret_cast<const float4 *>(&sh.logits[1][e]);
+                p[8 * ks + 4 * h4 + 0] = (x0.x + x1.x) * scale_log2;
+                p[8 * ks + 4 * h4 + 1] = (x0.y + x1.y) * scale_log2;
+                p[8 * ks + 4 * h4 + 2] = (x0.z + x1.z) * scale_log2;
+                p[8 * ks + 4 * h4 + 3] = (x0.w + x1.w) * scale_log2;
+            }
         float cmax = p[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, p[i]);
@@ -177,45 +265,47 @@ __global__ __launch_bounds__(256, 2) void attn_latent_mfma_kernel(
 
         bf16x8 pa_hi[2], pa_lo[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            uint16_t hi[8], lo[8];
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                hi[i] = f32_to_bf16_bits(p[8 * ks + i]);
-                lo[i] = f32_to_bf16_bits(p[8 * ks + i] - bf16_bits_to_f32(hi[i]));
+                const __bf16 hi = (__bf16)p[8 * ks + i];
+                pa_hi[ks][i] = hi;
+                pa_lo[ks][i] = (__bf16)(p[8 * ks + i] - (float)hi);
             }
-            uint4 vh = make_uint4(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16),
-                                  hi[4] | ((uint32_t)hi[5] << 16), hi[6] | ((uint32_t)hi[7] << 16));
-            uint4 vl = make_uint4(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16),
-                                  lo[4] | ((uint32_t)lo[5] << 16), lo[6] | ((uint32_t)lo[7] << 16));
-            pa_hi[ks] = as_bf16x8(vh);
-            pa_lo[ks] = as_bf16x8(vl);
-        }
-        // rescale the accumulator rows (heads 4*grp + i) by their alpha
+        // rescale the accumulator rows (heads 4 grp + i) by their alpha
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float a = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[nt][i] *= a;
+            for (int nt = 0; nt < 4; ++nt) acc[nt][i] *= a;
         }
-        // P.V over the 64 rows; V[row][col] is column col of the gathered latent row
+        // P.V over the 64 rows; V[row][col] is column col of the gathered latent row.  The
+        // B fragment of lane (hh, grp): rows 32 ks + 8 grp + {0, 2, 4, 6} then {1, 3, 5, 7},
+        // column 64 wave + 16 nt + hh, via two transposing reads whose lanes point at row
+        // 32 ks + 8 grp + 2 (hh / 4) (+1) and columns 64 wave + 16 nt + 4 (hh % 4) .. +3.
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                const int col = 128 * wave + 16 * nt + hh;
-                const unsigned char *vb = rows_lds + (32 * ks + 8 * grp) * kLdsRow + 2 * col;
-                uint16_t e[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) e[i] = *reinterpret_cast<const uint16_t *>(vb + i * kLdsRow);
-                uint4 vv = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                      e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
-                const bf16x8 b = as_bf16x8(vv);
+            for (int nt = 0; nt < 4; ++nt) {
+                const unsigned char *vb = sh.rows + (32 * ks + 8 * grp + 2 * (hh / 4)) * kLdsRow +
+                                          2 * (64 * wave + 16 * nt + 4 * (hh % 4));
+                const s16x4 lo4 = lds_read_tr16(vb);
+                const s16x4 hi4 = lds_read_tr16(vb + kLdsRow);
+                const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi[ks], b, acc[nt], 0, 0, 0);
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo[ks], b, acc[nt], 0, 0, 0);
             }
         }
-        __syncthreads();
+        __syncthreads();  // every wave is done with rows, logits and row_off[c & 1]
+        if (more) stash();
+        if (page_pending) {
+            if (page >= 0 && page < kv.n_pages) {
+                off_next = ((int64_t)page * kv.page_size + s_next % kv.page_size) * kv.row_elems;
+            } else {
+                flag_error(err, SA_DEVERR_BLOCK_TABLE);
+            }
+        }
+        if (tid < kChunk) sh.row_off[c & 1][tid] = off_next;
     }
 
     if (!kSplit) {
@@ -223,9 +313,9 @@ __global__ __launch_bounds__(256, 2) void attn_latent_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float iv = __shfl(inv, 4 * grp + i);
-            float *orow = out + (r * kLH + 4 * grp + i) * kLDv + 128 * wave + hh;
+            float *orow = out + (r * kLH + 4 * grp + i) * kLDv + 64 * wave + hh;
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = acc[nt][i] * iv;
+            for (int nt = 0; nt < 4; ++nt) orow[16 * nt] = acc[nt][i] * iv;
         }
         if (lse && wave == 0 && lane < kLH)
             lse[r * kLH + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
@@ -233,9 +323,9 @@ __global__ __launch_bounds__(256, 2) void attn_latent_mfma_kernel(
         const int64_t slot = r * n_splits + split;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float *prow = part_o + (slot * kLH + 4 * grp + i) * kLDv + 128 * wave + hh;
+            float *prow = part_o + (slot * kLH + 4 * grp + i) * kLDv + 64 * wave + hh;
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) prow[16 * nt] = acc[nt][i];
+            for (int nt = 0; nt < 4; ++nt) prow[16 * nt] = acc[nt][i];
         }
         if (wave == 0 && lane < kLH) {
             part_ml[(slot * kLH + lane) * 2 + 0] = m_run;
@@ -245,13 +335,14 @@ __global__ __launch_bounds__(256, 2) void attn_latent_mfma_kernel(
 }
 
 // Merge the per-split softmax states of each decode row: O = sum_s 2^(m_s - M) o_s /
-// sum_s 2^(m_s - M) l_s with M = max_s m_s.
-__global__ __launch_bounds__(256) void attn_merge_kernel(
-    Visibility vis, Selection sel, int split_rows, int n_splits, int H, int d_v,
-    const float *__restrict__ part_o, const float *__restrict__ part_ml, float *__restrict__ out,
-    float *__restrict__ lse)
+// sum_s 2^(m_s - M) l_s with M = max_s m_s.  One 128-thread workgroup per (row, head), four
+// value columns per thread.
+__global__ __launch_bounds__(128) void attn_merge_kernel(
+    Visibility vis, Selection sel, int split_rows, int n_splits, const float *__restrict__ part_o,
+    const float *__restrict__ part_ml, float *__restrict__ out, float *__restrict__ lse)
 {
-    const int64_t r = blockIdx.x;
+    const int64_t r = blockIdx.x / kLH;
+    const int h = blockIdx.x % kLH;
     int64_t visible = vis.ctx_len ? (int64_t)vis.ctx_len[r] : vis.causal_row0 + r + 1;
     if (vis.ctx_len && (visible < 1 || visible > vis.max_ctx)) visible = 0;
     int64_t k = sel.k_per_row ? (int64_t)sel.k_per_row[r] : (int64_t)sel.k;
@@ -259,24 +350,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     const int64_t m = k < visible ? k : visible;
     const int used = (int)((m + split_rows - 1) / split_rows);
     const float neg_inf = -__builtin_inff();
-    for (int e = threadIdx.x; e < H * d_v; e += blockDim.x) {
-        const int h = e / d_v, d = e % d_v;
-        float M = neg_inf;
-        for (int s = 0; s < used; ++s) M = fmaxf(M, part_ml[((r * n_splits + s) * H + h) * 2]);
-        float num = 0.f, den = 0.f;
-        if (M != neg_inf) {
-            for (int s = 0; s < used; ++s) {
-                const int64_t slot = (r * n_splits + s) * H + h;
-                const float ms = part_ml[slot * 2];
-                if (ms == neg_inf) continue;
-                const float f = exp2f(ms - M);
-                den = fmaf(part_ml[slot * 2 + 1], f, den);
-                num = fmaf(part_o[slot * d_v + d], f, num);
-            }
+    float M = neg_inf;
+    for (int s = 0; s < used; ++s) M = fmaxf(M, part_ml[((r * n_splits + s) * kLH + h) * 2]);
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+    if (M != neg_inf) {
+        for (int s = 0; s < used; ++s) {
+            const int64_t slot = (r * n_splits + s) * kLH + h;
+            const float ms = part_ml[slot * 2];
+            if (ms == neg_inf) continue;
+            const float f = exp2f(ms - M);
+            den = fmaf(part_ml[slot * 2 + 1], f, den);
+            const float4 o = reinterpret_cast<const float4 *>(part_o + slot * kLDv)[threadIdx.x];
+            num.x = fmaf(o.x, f, num.x);
+            num.y = fmaf(o.y, f, num.y);
+            num.z = fmaf(o.z, f, num.z);
+            num.w = fmaf(o.w, f, num.w);
         }
-        out[(r * H + h) * (int64_t)d_v + d] = den > 0.f ? num / den : 0.f;
-        if (lse && d == 0) lse[r * H + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : neg_inf;
     }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    reinterpret_cast<float4 *>(out + (r * kLH + h) * (int64_t)kLDv)[threadIdx.x] =
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    if (lse && threadIdx.x == 0) lse[r * kLH + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : neg_inf;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -386,7 +481,7 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSo
         const uint16_t *qq = reinterpret_cast<const uint16_t *>(q);
         if (!decode) {
             KernelTimer timer(h, SA_KERNEL_ATTENTION, st);
-            hipLaunchKernelGGL(attn_latent_mfma_kernel<false>, dim3((unsigned)n_rows), dim3(256), 0, st,
+            hipLaunchKernelGGL(attn_latent_mfma_kernel<false>, dim3((unsigned)n_rows), dim3(kAThreads), 0, st,
                                qq, n_rows, kv, vis, sel, scale_log2, out, lse, 0, 1, nullptr, nullptr,
                                h.d_err);
             return hipGetLastError();
@@ -397,14 +492,14 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSo
         {
             KernelTimer timer(h, SA_KERNEL_ATTENTION, st);
             hipLaunchKernelGGL(attn_latent_mfma_kernel<true>, dim3((unsigned)n_rows, (unsigned)n_splits),
-                               dim3(256), 0, st, qq, n_rows, kv, vis, sel, scale_log2, out, lse,
+                               dim3(kAThreads), 0, st, qq, n_rows, kv, vis, sel, scale_log2, out, lse,
                                kSplitRows, n_splits, part_o, part_ml, h.d_err);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         KernelTimer timer(h, SA_KERNEL_MERGE, st);
-        hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)n_rows), dim3(256), 0, st, vis, sel,
-                           kSplitRows, n_splits, kLH, kLDv, part_o, part_ml, out, lse);
+        hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(n_rows * kLH)), dim3(kLDv / 4), 0, st, vis, sel,
+                           kSplitRows, n_splits, part_o, part_ml, out, lse);
         return hipGetLastError();
     }
     const sa_config_t &c = h.cfg;

@@ -38,6 +38,8 @@ constexpr int kD = 128;             // index head width
 constexpr int kRows = 8;            // query rows per tile = waves per workgroup
 constexpr int kThreads = kRows * kWave;
 constexpr int kKT = 64;             // keys per LDS tile
+constexpr int kHalves = kKT / 32;   // 32-key MFMA column blocks per tile
+constexpr int kTileLoads = kKT * 16 / 512;  // 16-byte chunks each thread moves per tile
 constexpr int kChunks = kD * 2 / 16;  // 16-byte chunks per key row (16)
 constexpr int kBins = 2048;         // histogram bins over the key's top 11 bits
 constexpr int kBinShift = 21;
@@ -48,7 +50,7 @@ constexpr int kPerThread = 16;      // consecutive candidates per thread in orde
 static_assert(kRows * kBins * 4 == kCap * 8, "the histogram region holds the candidates");
 
 struct Shared {
-    uint4 keys[2][kKT * kChunks];        // 2 x 16 KB key tiles
+    uint4 keys[2][kKT * kChunks];        // double-buffered key tiles
     uint32_t region[kRows * kBins];      // 64 KB: histograms, then candidate (key, index)
     uint32_t radix[128];
     int wave_sums[kRows];
@@ -64,6 +66,21 @@ struct Shared {
 __device__ __forceinline__ float relu(float x)
 {
     return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Scheduling pattern of one 32-key half-tile: its 8 B-fragment reads, then the 16 MFMAs
+// interleaved with the 64 VALU ops of the previous half-tile's epilogue.
+template <int kId>
+__device__ __forceinline__ void interleave_half()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, kId);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, kId);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, kId);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, kId);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, kId);
 }
 
 // Exclusive prefix sum over the 512 threads (thread order); *total gets the sum.
@@ -92,18 +109,24 @@ __device__ __forceinline__ int block_scan(int v, int *wave_sums, int *total)
 
 // One wave: the highest bin b of a 2048-bin histogram such that the bins >= b hold at least
 // m entries.  Returns -1 if the whole histogram holds fewer than m.  *above = entries in bins
-// > b, *upto = entries in bins >= b.  Every lane returns the same values.
+// > b, *upto = entries in bins >= b (either may be NULL).  Every lane returns the same values.
 __device__ __forceinline__ int threshold_bin(const uint32_t *hist, int m, int *above, int *upto)
 {
     const int lane = lane_id();
     // lane l covers bins [kBins - 32 (l + 1), kBins - 32 l): lane 0 holds the top bins
     const uint32_t *hb = hist + kBins - 32 * (lane + 1);
-    int sum = 0;
+    uint32_t c[32];
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
         const uint4 v = *reinterpret_cast<const uint4 *>(hb + i);
-        sum += (int)(v.x + v.y + v.z + v.w);
+        c[i] = v.x;
+        c[i + 1] = v.y;
+        c[i + 2] = v.z;
+        c[i + 3] = v.w;
     }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sum += (int)c[i];
     int incl = sum;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -112,27 +135,24 @@ __device__ __forceinline__ int threshold_bin(const uint32_t *hist, int m, int *a
     }
     const uint64_t hit = __ballot(incl >= m);
     if (hit == 0) {
-        *above = 0;
-        *upto = __shfl(incl, kWave - 1);
+        if (above) *above = 0;
+        if (upto) *upto = __shfl(incl, kWave - 1);
         return -1;
     }
     const int src = __builtin_ctzll(hit);
-    int bin = -1, ab = 0, up = 0;
-    if (lane == src) {
-        int cum = incl - sum;
-        for (int i = 31; i >= 0; --i) {
-            const int c = (int)hb[i];
-            if (cum + c >= m) {
-                bin = kBins - 32 * (lane + 1) + i;
-                ab = cum;
-                up = cum + c;
-                break;
-            }
-            cum += c;
-        }
+    // every lane walks its own bins from the top (only lane src's answer is used)
+    int cum = incl - sum, bin = -1, ab = 0, up = 0;
+#pragma unroll
+    for (int i = 31; i >= 0; --i) {
+        const int ci = (int)c[i];
+        const bool here = bin < 0 && cum + ci >= m;
+        bin = here ? kBins - 32 * (lane + 1) + i : bin;
+        ab = here ? cum : ab;
+        up = here ? cum + ci : up;
+        cum += ci;
     }
-    *above = __shfl(ab, src);
-    *upto = __shfl(up, src);
+    if (above) *above = __shfl(ab, src);
+    if (upto) *upto = __shfl(up, src);
     return __shfl(bin, src);
 }
 
@@ -278,9 +298,9 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             // key tile loader: thread i moves chunks i and i + 512 of the 1024 in a tile;
             // LDS slot (r, j) holds chunk j ^ (r % 16) of key row r
             const int n_kt = (int)(t_last / kKT) + 1;
-            auto load_tile = [&](int kt, uint4 (&v)[2]) {
+            auto load_tile = [&](int kt, uint4 (&v)[kTileLoads]) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
+                for (int u = 0; u < kTileLoads; ++u) {
                     const int c = tid + u * kThreads;
                     const int r = c / kChunks, j = c % kChunks;
                     int64_t s = (int64_t)kt * kKT + r;
@@ -288,83 +308,111 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                     v[u] = load16(k_idx + s * kD + 8 * (j ^ (r % 16)));
                 }
             };
-            auto store_tile = [&](int buf, const uint4 (&v)[2]) {
+            auto store_tile = [&](int buf, const uint4 (&v)[kTileLoads]) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) sh.keys[buf][tid + u * kThreads] = v[u];
+                for (int u = 0; u < kTileLoads; ++u) sh.keys[buf][tid + u * kThreads] = v[u];
             };
             {
-                uint4 v[2];
+                uint4 v[kTileLoads];
                 load_tile(0, v);
                 store_tile(0, v);
             }
             uint32_t *hist = sh.region + wave * kBins;
             int run_bin = 0;  // running threshold bin: scores in lower bins are dropped
 
+            // Software pipeline over half-tiles of 32 keys: while the MFMAs of half-tile h run,
+            // the VALU applies ReLU, the weights and the in-lane head sum to the accumulators of
+            // half-tile h - 1.  acc[0] holds the even half-tiles, acc[1] the odd ones; a window
+            // of 64 keys shifted by -32 (odd half of tile kt - 1, even half of tile kt) is then
+            // finished by one v_permlane32_swap: lane l scores key 64 kt - 32 + l.
+            f32x16 acc[2][2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) acc[st][mt] = f32x16{};
+
+            // all keys of a window go through the histogram; the ones at or above the running
+            // threshold bin are appended to the row's candidate list in key order
+            auto finish_window = [&](float part_odd, float part_even, int64_t s) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part_odd),
+                                                                 __float_as_uint(part_even), false, false);
+                const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const bool vis = s >= 0 && s <= row;
+                const uint32_t key = order_key(score);
+                atomicAdd(&hist[key >> kBinShift], vis ? 1u : 0u);
+                const bool keep = vis && (int)(key >> kBinShift) >= run_bin;
+                const uint64_t ballot = __ballot(keep);
+                if (keep) {
+                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
+                    my_cands[n_cand + rank] = make_uint2(key, (uint32_t)s);
+                }
+                n_cand += __popcll(ballot);
+            };
+
 #pragma unroll 1
             for (int kt = 0; kt < n_kt; ++kt) {
                 __syncthreads();
-                uint4 nxt[2];
+                uint4 nxt[kTileLoads];
                 const bool more = kt + 1 < n_kt;
                 if (more) load_tile(kt + 1, nxt);
-                const int64_t base = (int64_t)kt * kKT;
-                if (selects && base <= row) {
+                if (selects) {
                     const uint4 *kb = sh.keys[kt & 1];
-                    f32x16 acc[2][2];
+                    float part_odd = 0.f;
 #pragma unroll
-                    for (int st = 0; st < 2; ++st)
+                    for (int hf = 0; hf < kHalves; ++hf) {
+                        const int st = hf & 1;  // accumulator pair of this half-tile
+                        // B fragments of half-tile hf: key 32 hf + l % 32, dims 16 ks + 8 (l / 32)
+                        bf16x8 b[kD / 16];
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt) acc[st][mt] = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < kD / 16; ++ks) {
-                        bf16x8 b[2];
-#pragma unroll
-                        for (int st = 0; st < 2; ++st) {
-                            const int r = 32 * st + lane % 32;
+                        for (int ks = 0; ks < kD / 16; ++ks) {
+                            const int r = 32 * hf + lane % 32;
                             const int j = (2 * ks + lane / 32) ^ (r % 16);
-                            b[st] = as_bf16x8(kb[r * kChunks + j]);
+                            b[ks] = as_bf16x8(kb[r * kChunks + j]);
                         }
-#pragma unroll
-                        for (int st = 0; st < 2; ++st)
-#pragma unroll
-                            for (int mt = 0; mt < 2; ++mt)
-                                acc[st][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[st],
-                                                                                      acc[st][mt], 0, 0, 0);
-                    }
-                    // register g of lane l: head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4, key l % 32
-                    float part[2];
-#pragma unroll
-                    for (int st = 0; st < 2; ++st) {
+                        // epilogue of the previous half-tile (the other accumulator pair):
+                        // register g of lane l is head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4
                         float p = 0.f;
 #pragma unroll
                         for (int g = 0; g < 16; ++g) {
-                            p = fmaf(wv[0][g], relu(acc[st][0][g]), p);
-                            p = fmaf(wv[1][g], relu(acc[st][1][g]), p);
+                            p = fmaf(wv[0][g], relu(acc[st ^ 1][0][g]), p);
+                            p = fmaf(wv[1][g], relu(acc[st ^ 1][1][g]), p);
                         }
-                        part[st] = p;
+                        acc[st][0] = f32x16{};
+                        acc[st][1] = f32x16{};
+#pragma unroll
+                        for (int ks = 0; ks < kD / 16; ++ks)
+#pragma unroll
+                            for (int mt = 0; mt < 2; ++mt)
+                                acc[st][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks],
+                                                                                      acc[st][mt], 0, 0, 0);
+                        // 8 fragment reads, then one MFMA per 4 VALU of the epilogue
+                        if (hf == 0) interleave_half<0>();
+                        else if (hf == 1) interleave_half<1>();
+                        else if (hf == 2) interleave_half<2>();
+                        else interleave_half<3>();
+                        if (st == 0) {
+                            part_odd = p;  // odd half-tile before this one
+                        } else {
+                            // window: odd half-tile hf - 2 and even half-tile hf - 1
+                            finish_window(part_odd, p, (int64_t)kt * kKT + 32 * (hf - 2) + lane);
+                        }
                     }
-                    // lanes 0-31 finish key l (tile 0), lanes 32-63 key l (tile 1)
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
-                                                                     __float_as_uint(part[1]), false, false);
-                    const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                    const int64_t s = base + lane;
-                    const bool vis = s <= row;
-                    const uint32_t key = order_key(score);
-                    if (vis) atomicAdd(&hist[key >> kBinShift], 1u);
-                    const bool keep = vis && (int)(key >> kBinShift) >= run_bin;
-                    const uint64_t ballot = __ballot(keep);
-                    if (keep) {
-                        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
-                                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
-                        my_cands[n_cand + rank] = make_uint2(key, (uint32_t)s);
-                    }
-                    n_cand += __popcll(ballot);
-                    if ((kt % kRefresh) == kRefresh - 1 && base + kKT >= m) {
-                        int ab, up;
-                        const int b = threshold_bin(hist, m, &ab, &up);
+                    if ((kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
+                        const int b = threshold_bin(hist, m, nullptr, nullptr);
                         if (b > run_bin) run_bin = b;
                     }
                 }
                 if (more) store_tile((kt + 1) & 1, nxt);
+            }
+            if (selects) {  // the odd half of the last tile
+                float p = 0.f;
+#pragma unroll
+                for (int g = 0; g < 16; ++g) {
+                    p = fmaf(wv[0][g], relu(acc[1][0][g]), p);
+                    p = fmaf(wv[1][g], relu(acc[1][1][g]), p);
+                }
+                finish_window(p, 0.f, (int64_t)n_kt * kKT - 32 + lane);
             }
         }
         // final threshold per row (each wave its own row), then free the histograms
