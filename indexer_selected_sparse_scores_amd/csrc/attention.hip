@@ -63,20 +63,22 @@ __device__ __forceinline__ int64_t token_offset(const RowSource &src, int64_t b,
 constexpr int kLH = 16;         // query heads
 constexpr int kLDqk = 576;      // key width
 constexpr int kLDv = 512;       // value width (leading columns of the key row)
-constexpr int kChunk = 64;      // selected rows per LDS chunk
+constexpr int kChunk = 64;      // selected rows per chunk
 constexpr int kAThreads = 512;  // 8 waves
 constexpr int kRowBytes = kLDqk * 2;
-constexpr int kLdsRow = kRowBytes + 16;                 // padded LDS row stride (bytes)
-constexpr int kPieces = kRowBytes / 16;                 // 16-byte pieces per row (72)
-constexpr int kGather = kChunk * kPieces / kAThreads;   // pieces each thread moves per chunk (9)
+constexpr int kLdsRow = kLDv * 2 + 16;                  // padded LDS row of the value part (bytes)
 constexpr int kKSteps = kLDqk / 32;                     // 18 k-steps of the logits MFMA
 constexpr int kKHalf = kKSteps / 2;                     // each wave group takes half of them
 constexpr int kLogitLd = kChunk + 4;                    // padded per-head row of logits (floats)
-static_assert(kChunk * kPieces % kAThreads == 0, "chunk gather must tile the workgroup");
+constexpr int kVPieces = kLDv / 8;                      // 16-byte pieces of the value part (64)
 
 struct AttnShared {
-    unsigned char rows[kChunk * kLdsRow];   // gathered rows of the current chunk
+    unsigned char rows[kChunk * kLdsRow];   // value part of the current chunk's rows
     float logits[2][kLH * kLogitLd];        // partial logits of the two K-halves, [head][slot]
+    uint4 p_hi[2][kLH][4];                  // P as the A operand of P.V: [half][head][lane group]
+    uint4 p_lo[2][kLH][4];                  //   (8 bf16 each), hi part and bf16 residual
+    float alpha[kLH];                       // per-head rescale of this chunk
+    float inv_l[kLH];                       // per-head 1 / softmax sum (end of the row)
     int64_t row_off[2][kChunk];             // element offsets of a chunk's rows (-1: none)
 };
 
@@ -97,7 +99,7 @@ __device__ __forceinline__ int64_t slot_offset(const RowSource &kv, const int32_
 // as P and V agree.  MFMA k index 8 g + j (lane group g = lane / 16, j = 0..7) of a 32-row
 // half is row 8 g + 2 j (j < 4) or 8 g + 2 (j - 4) + 1 (j >= 4): the V fragment is then two
 // transposing LDS reads over rows two apart, which fall in disjoint banks.  slot_of_row
-// inverts the map; logits are stored at their slot so that P is read in k order.
+// inverts the map; logits are stored at their slot so that P is produced in k order.
 __device__ __forceinline__ int slot_of_row(int row)
 {
     const int w = row & 7;
@@ -116,12 +118,15 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char *p)
 }
 
 // One workgroup = one query row (all 16 heads) and a range of its selected rows, processed
-// in chunks of 64 rows.  The gather of chunk c+1 (16-byte loads into registers), the page
-// lookup of chunk c+2 and the index of chunk c+3 are in flight while chunk c is computed from
-// LDS: logits on v_mfma_f32_16x16x32_bf16 (waves 0-3 and 4-7 take the two halves of the
-// 576-wide contraction for 16 rows each), an online softmax per head (exp2, log2(e) folded
-// into the scale), and P.V on the same MFMA with P split into bf16 hi + lo parts (each wave
-// owns 64 of the 512 value columns).
+// in chunks of 64 rows.  Wave w computes the logits of rows 16 (w % 4) .. +15 over half
+// w / 4 of the 576-wide contraction (v_mfma_f32_16x16x32_bf16, q fragments in registers);
+// each thread gathers exactly the nine 16-byte pieces of K its own MFMAs consume, so the
+// logits come straight from registers, and only the value part of the rows goes through LDS.
+// The gather of chunk c+1, the page lookup of chunk c+2 and the index of chunk c+3 are in
+// flight while chunk c is computed.  Wave w owns the online softmax of heads 2w and 2w+1
+// (running max / sum, exp2 with log2(e) folded into the scale) and publishes P as bf16 hi +
+// residual, so the weights keep ~16 mantissa bits; every wave then accumulates P.V for 64 of
+// the 512 value columns, with V fragments from transposing LDS reads.
 template <bool kSplit>
 __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
     const uint16_t *__restrict__ q, int64_t n_rows, RowSource kv, Visibility vis, Selection sel,
@@ -147,6 +152,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
 
     // logits: wave w covers rows 16 (w % 4) .. +15 and k-steps 9 (w / 4) .. +8
     const int nt_qk = wave & 3, kh = wave >> 2;
+    const int my_row = 16 * nt_qk + hh;             // the chunk row this lane's K pieces come from
     bf16x8 qa[kKHalf];
     const uint16_t *qr = q + (r * kLH + hh) * kLDqk;
 #pragma unroll
@@ -161,34 +167,42 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
         if (pend_j < j_end) pend_s = idx_row[pend_j];
     }
     __syncthreads();
-    uint4 g[kGather];
+
+    // piece i of this thread: 16 bytes at dims 32 (9 kh + i) + 8 grp of row my_row
+    uint4 g[kKHalf];
     auto gather = [&](int buf) {
+        const int64_t off = sh.row_off[buf][my_row];
 #pragma unroll
-        for (int u = 0; u < kGather; ++u) {
-            const int pc = tid + kAThreads * u;
-            const int64_t off = sh.row_off[buf][pc / kPieces];
-            g[u] = off >= 0 ? load16(kv_base + off + (pc % kPieces) * 8) : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int i = 0; i < kKHalf; ++i)
+            g[i] = off >= 0 ? load16(kv_base + off + 32 * (kKHalf * kh + i) + 8 * grp) : make_uint4(0u, 0u, 0u, 0u);
     };
+    // the value part (pieces 0..63 of a row) goes to LDS for P.V
     auto stash = [&]() {
 #pragma unroll
-        for (int u = 0; u < kGather; ++u) {
-            const int pc = tid + kAThreads * u;
-            *reinterpret_cast<uint4 *>(sh.rows + (pc / kPieces) * kLdsRow + (pc % kPieces) * 16) = g[u];
+        for (int i = 0; i < kKHalf; ++i) {
+            const int piece = 4 * (kKHalf * kh + i) + grp;
+            if (piece < kVPieces)
+                *reinterpret_cast<uint4 *>(sh.rows + my_row * kLdsRow + piece * 16) = g[i];
         }
     };
     gather(0);
     stash();
+    uint4 kf[kKHalf];  // K pieces of the chunk being computed
+#pragma unroll
+    for (int i = 0; i < kKHalf; ++i) kf[i] = g[i];
 
     const float neg_inf = -__builtin_inff();
-    float m_run = neg_inf, l_run = 0.f;   // softmax state of head hh (log2 domain)
-    f32x4 acc[4];                         // O[4 grp + i][64 wave + 16 nt + hh]
+    // softmax state of head 2 wave + lane / 32 (log2 domain), owned by this wave
+    const int sm_head = 2 * wave + lane / 32;
+    float m_run = neg_inf, l_run = 0.f;
+    f32x4 acc[4];  // O[4 grp + i][64 wave + 16 nt + hh]
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll 1
     for (int c = 0; c < n_chunks; ++c) {
-        __syncthreads();  // rows = chunk c, row_off[c & 1] = chunk c, row_off[(c + 1) & 1] = chunk c + 1
+        // rows = values of chunk c, kf = K pieces of chunk c, row_off[c & 1] = chunk c,
+        // row_off[(c + 1) & 1] = chunk c + 1
         const bool more = c + 1 < n_chunks;
         // Slot pend_j (chunk c + 2): its index arrived during the previous chunk; its page
         // lookup and the index of chunk c + 3 are issued before this chunk's gather loads, so
@@ -215,76 +229,70 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
 
         // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh
         {
-            f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-            const int row = 16 * nt_qk + hh;
-            const unsigned char *kb = sh.rows + row * kLdsRow + 16 * grp + 64 * kKHalf * kh;
+            f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = {0.f, 0.f, 0.f, 0.f};  // two chains
 #pragma unroll
-            for (int i = 0; i < kKHalf; ++i) {
-                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(kb + 64 * i));
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], b, sacc, 0, 0, 0);
+            for (int i = 0; i < kKHalf; i += 2) {
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], as_bf16x8(kf[i]), sa0, 0, 0, 0);
+                if (i + 1 < kKHalf)
+                    sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i + 1], as_bf16x8(kf[i + 1]), sa1, 0, 0, 0);
             }
-            const bool valid = sh.row_off[c & 1][row] >= 0;
-            const int slot = slot_of_row(row);
+            const f32x4 sacc = sa0 + sa1;
+            // output (head 4 grp + i, row my_row)
+            const bool valid = sh.row_off[c & 1][my_row] >= 0;
+            const int slot = slot_of_row(my_row);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sh.logits[kh][(4 * grp + i) * kLogitLd + slot] = valid ? sacc[i] : neg_inf;
         }
         __syncthreads();
 
-        // online softmax update for head hh over the 64 rows (identical in every wave)
-        float p[16];  // p[8 ks + j]: MFMA k index 32 ks + 8 grp + j
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int h4 = 0; h4 < 2; ++h4) {
-                const int e = hh * kLogitLd + 32 * ks + 8 * grp + 4 * h4;
-                const float4 x0 = *reinterpret_cast<const float4 *>(&sh.logits[0][e]);
-                const float4 x1 = *reinterpret_cast<const float4 *>(&sh.logits[1][e]);
-                p[8 * ks + 4 * h4 + 0] = (x0.x + x1.x) * scale_log2;
-                p[8 * ks + 4 * h4 + 1] = (x0.y + x1.y) * scale_log2;
-                p[8 * ks + 4 * h4 + 2] = (x0.z + x1.z) * scale_log2;
-                p[8 * ks + 4 * h4 + 3] = (x0.w + x1.w) * scale_log2;
-            }
-        float cmax = p[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) cmax = fmaxf(cmax, p[i]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(m_run, cmax);
-        const bool any = m_new != neg_inf;
-        const float alpha = any ? exp2f(m_run - m_new) : 1.f;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            p[i] = any ? exp2f(p[i] - m_new) : 0.f;
-            psum += p[i];
+        // online softmax of head sm_head over the 64 slots: this lane takes slots l % 32 and
+        // 32 + l % 32
+        {
+            const int sl = lane % 32;
+            const float* lg0 = &sh.logits[0][sm_head * kLogitLd];
+            const float* lg1 = &sh.logits[1][sm_head * kLogitLd];
+            const float x0 = (lg0[sl] + lg1[sl]) * scale_log2;
+            const float x1 = (lg0[32 + sl] + lg1[32 + sl]) * scale_log2;
+            const float cmax = half_wave_max(fmaxf(x0, x1));
+            const float m_new = fmaxf(m_run, cmax);
+            const bool any = m_new != neg_inf;
+            const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            const float p0 = any ? __builtin_amdgcn_exp2f(x0 - m_new) : 0.f;
+            const float p1 = any ? __builtin_amdgcn_exp2f(x1 - m_new) : 0.f;
+            const float psum = half_wave_sum(p0 + p1);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            // slot sl is MFMA k index sl of half 0 (lane group sl / 8, element sl % 8)
+            const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+            const __bf16 r0 = (__bf16)(p0 - (float)h0), r1 = (__bf16)(p1 - (float)h1);
+            __bf16 *ph = reinterpret_cast<__bf16 *>(&sh.p_hi[0][sm_head][0]);
+            __bf16 *pl = reinterpret_cast<__bf16 *>(&sh.p_lo[0][sm_head][0]);
+            ph[sl] = h0;
+            pl[sl] = r0;
+            ph[kLH * 32 + sl] = h1;  // half 1
+            pl[kLH * 32 + sl] = r1;
+            if (sl == 0) sh.alpha[sm_head] = alpha;
         }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        __syncthreads();
 
-        bf16x8 pa_hi[2], pa_lo[2];
+        // rescale the accumulator rows (heads 4 grp + i), then P.V over the 64 rows
+        {
+            const float4 al = *reinterpret_cast<const float4 *>(&sh.alpha[4 * grp]);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const __bf16 hi = (__bf16)p[8 * ks + i];
-                pa_hi[ks][i] = hi;
-                pa_lo[ks][i] = (__bf16)(p[8 * ks + i] - (float)hi);
+            for (int nt = 0; nt < 4; ++nt) {
+                acc[nt][0] *= al.x;
+                acc[nt][1] *= al.y;
+                acc[nt][2] *= al.z;
+                acc[nt][3] *= al.w;
             }
-        // rescale the accumulator rows (heads 4 grp + i) by their alpha
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float a = __shfl(alpha, 4 * grp + i);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) acc[nt][i] *= a;
         }
-        // P.V over the 64 rows; V[row][col] is column col of the gathered latent row.  The
         // B fragment of lane (hh, grp): rows 32 ks + 8 grp + {0, 2, 4, 6} then {1, 3, 5, 7},
         // column 64 wave + 16 nt + hh, via two transposing reads whose lanes point at row
         // 32 ks + 8 grp + 2 (hh / 4) (+1) and columns 64 wave + 16 nt + 4 (hh % 4) .. +3.
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 pa_hi = as_bf16x8(sh.p_hi[ks][hh][grp]);
+            const bf16x8 pa_lo = as_bf16x8(sh.p_lo[ks][hh][grp]);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const unsigned char *vb = sh.rows + (32 * ks + 8 * grp + 2 * (hh / 4)) * kLdsRow +
@@ -292,12 +300,13 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
                 const s16x4 lo4 = lds_read_tr16(vb);
                 const s16x4 hi4 = lds_read_tr16(vb + kLdsRow);
                 const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi[ks], b, acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo[ks], b, acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, b, acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, b, acc[nt], 0, 0, 0);
             }
         }
-        __syncthreads();  // every wave is done with rows, logits and row_off[c & 1]
-        if (more) stash();
+        // row_off[c & 1] was last read by this chunk's logits (before the barrier above); it
+        // now takes chunk c + 2, which the gather of the next iteration reads after the
+        // barrier below
         if (page_pending) {
             if (page >= 0 && page < kv.n_pages) {
                 off_next = ((int64_t)page * kv.page_size + s_next % kv.page_size) * kv.row_elems;
@@ -306,19 +315,27 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
             }
         }
         if (tid < kChunk) sh.row_off[c & 1][tid] = off_next;
+        __syncthreads();  // every wave is done with rows, logits and P; row_off is published
+        if (more) {
+            stash();
+#pragma unroll
+            for (int i = 0; i < kKHalf; ++i) kf[i] = g[i];
+        }
     }
 
     if (!kSplit) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        if (lane % 32 == 0) sh.inv_l[sm_head] = l_run > 0.f ? 1.f / l_run : 0.f;
+        if (lse && lane % 32 == 0)
+            lse[r * kLH + sm_head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
+        __syncthreads();
+        const float4 iv = *reinterpret_cast<const float4 *>(&sh.inv_l[4 * grp]);
+        const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float iv = __shfl(inv, 4 * grp + i);
             float *orow = out + (r * kLH + 4 * grp + i) * kLDv + 64 * wave + hh;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) orow[16 * nt] = acc[nt][i] * iv;
+            for (int nt = 0; nt < 4; ++nt) orow[16 * nt] = acc[nt][i] * ivs[i];
         }
-        if (lse && wave == 0 && lane < kLH)
-            lse[r * kLH + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
     } else {
         const int64_t slot = r * n_splits + split;
 #pragma unroll
@@ -327,9 +344,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) prow[16 * nt] = acc[nt][i];
         }
-        if (wave == 0 && lane < kLH) {
-            part_ml[(slot * kLH + lane) * 2 + 0] = m_run;
-            part_ml[(slot * kLH + lane) * 2 + 1] = l_run;
+        if (lane % 32 == 0) {
+            part_ml[(slot * kLH + sm_head) * 2 + 0] = m_run;
+            part_ml[(slot * kLH + sm_head) * 2 + 1] = l_run;
         }
     }
 }

@@ -60,6 +60,38 @@ __device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit)
     if (err) atomicOr(err, bit);
 }
 
+// Cross-lane reductions over each 32-lane half of the wave on the VALU: DPP quad
+// permutations and row mirrors combine 16 lanes, v_permlane16_swap the two 16-lane rows.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float half_wave_max(float x)
+{
+    x = fmaxf(x, dpp_mov<kDppXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppXor2>(x));
+    x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_mov<kDppRowMirror>(x));
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+__device__ __forceinline__ float half_wave_sum(float x)
+{
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    x += dpp_mov<kDppRowHalfMirror>(x);
+    x += dpp_mov<kDppRowMirror>(x);
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
