@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attention.hip", "prefill_topk.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attention.hip", "prefill_topk.hip", "decode.hip"]
 ARCH = os.environ.get("SA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

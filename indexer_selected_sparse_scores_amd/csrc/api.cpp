@@ -92,11 +92,14 @@ struct DecodeLayout {
     size_t scores, idx, attn, total;
 };
 
+// Fast path: [decode top-k workspace (scores, histograms, candidates) | idx | attention
+// partials].  Generic path: [scores [B, max_ctx] | idx | attention partials].
 DecodeLayout decode_layout(const sa_handle_s &h, int64_t B, int64_t max_ctx)
 {
     DecodeLayout d;
     d.scores = 0;
-    d.idx = align_up((size_t)B * (size_t)max_ctx * sizeof(float));
+    d.idx = h.fast_decode ? align_up(sa::decode_topk_layout(B, max_ctx).total)
+                          : align_up((size_t)B * (size_t)max_ctx * sizeof(float));
     d.attn = d.idx + align_up((size_t)B * (size_t)h.cfg.max_topk * sizeof(int32_t));
     d.total = d.attn + align_up(sa::attention_workspace(h, B, true));
     return d;
@@ -195,6 +198,7 @@ sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
     h->cfg = c;
     h->scale = c.softmax_scale > 0.f ? c.softmax_scale : (float)(1.0 / std::sqrt((double)c.d_qk));
     h->fast_indexer = c.dtype == SA_BF16 && c.n_idx_heads == 64 && c.d_idx == 128;
+    h->fast_decode = h->fast_indexer && c.page_size == 64;
     h->fast_attn = c.dtype == SA_BF16 && c.n_heads == 16 && c.n_kv_heads == 1 && c.d_qk == 576 &&
                    c.d_v == 512 && c.v_from_k == 1;
     if (!h->fast_indexer && (size_t)(c.n_idx_heads * c.d_idx + c.n_idx_heads) * 4 > 64 * 1024) {
@@ -415,7 +419,7 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
     if (c.v_from_k ? v_pages != nullptr : v_pages == nullptr)
         return fail(h, SA_ERR_INVALID_ARG, c.v_from_k ? "v_pages must be NULL when v_from_k = 1"
                                                       : "v_pages must not be NULL when v_from_k = 0");
-    if (B < 1) return fail(h, SA_ERR_INVALID_ARG, "B must be >= 1");
+    if (B < 1 || B > 65535) return fail(h, SA_ERR_INVALID_ARG, "B must be in [1, 65535]");
     if (n_pages < 1) return fail(h, SA_ERR_INVALID_ARG, "n_pages must be >= 1");
     if (max_blocks < 1) return fail(h, SA_ERR_INVALID_ARG, "max_blocks must be >= 1");
     if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)max_blocks * c.page_size)
@@ -434,15 +438,22 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
     float *scores = reinterpret_cast<float *>(base + lay.scores);
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
 
-    sa::RowSource keys{kidx_pages, c.d_idx, block_table, max_blocks, c.page_size, n_pages};
     sa::Visibility vis{0, ctx_len, max_ctx};
-    s = hip_status(h, sa::launch_indexer(*h, q_idx, w, B, keys, vis, scores, max_ctx, max_ctx, st),
-                   "indexer launch");
-    if (s != SA_OK) return s;
-    s = hip_status(h, sa::launch_topk(*h, scores, max_ctx, B, max_ctx, ctx_len, 0, topk, c.max_topk, idx,
-                                      c.max_topk, h->d_err, st),
-                   "top-k launch");
-    if (s != SA_OK) return s;
+    if (h->fast_decode) {
+        s = hip_status(h, sa::launch_decode_indexer_topk(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks,
+                                                         ctx_len, topk, B, max_ctx, idx, base + lay.scores, st),
+                       "decode indexer/top-k launch");
+        if (s != SA_OK) return s;
+    } else {
+        sa::RowSource keys{kidx_pages, c.d_idx, block_table, max_blocks, c.page_size, n_pages};
+        s = hip_status(h, sa::launch_indexer(*h, q_idx, w, B, keys, vis, scores, max_ctx, max_ctx, st),
+                       "indexer launch");
+        if (s != SA_OK) return s;
+        s = hip_status(h, sa::launch_topk(*h, scores, max_ctx, B, max_ctx, ctx_len, 0, topk, c.max_topk, idx,
+                                          c.max_topk, h->d_err, st),
+                       "top-k launch");
+        if (s != SA_OK) return s;
+    }
     sa::RowSource kv{kv_pages, (int64_t)c.n_kv_heads * c.d_qk, block_table, max_blocks, c.page_size, n_pages};
     sa::RowSource vv{v_pages, (int64_t)c.n_kv_heads * c.d_v, block_table, max_blocks, c.page_size, n_pages};
     sa::Selection sel{idx, c.max_topk, c.max_topk, topk};

@@ -1,0 +1,340 @@
+// Paged decode: indexer scores over the whole cached context and the per-sequence top-k, on
+// gfx950.
+//
+// One new token per sequence attends to the k_b most relevant of its n_b cached tokens
+// ("Long-Context LLMs Explained: Sparse Attention, Stable Reinforcement Learning, and
+// Verifiable Synthetic Data", section 2.3: the indexer scores every cached token, and only the
+// selected KV entries are read, through the paged cache).  The score is
+// I(s) = sum_j w(j) ReLU(q(j).k(s)) ("Sparse Attention and RL Optimization: Three Technical
+// Breakthroughs in LLM Post-Training", section 2.2); selection keeps the largest scores,
+// ties to the lower token index (section 2.3).
+//
+// Fast path (bf16, H_I = 64, d_I = 128, 64-token pages), three kernels:
+//  * indexer_decode_kernel: grid (1024-key blocks, sequences).  Each wave streams 4 pages of
+//    index keys straight into v_mfma_f32_32x32x16_bf16 B fragments (next half-page in flight
+//    while the current one is multiplied; q and the head weights stay in registers), applies
+//    ReLU / weights / head sum in registers, writes the fp32 scores and counts them in a
+//    2048-bin LDS histogram that is added to the sequence's histogram in global memory.  The
+//    scan over index keys is the HBM-bound part of decode (256 bytes per cached token).
+//  * decode_collect_kernel: grid (8192-score chunks, sequences).  From the histogram, the bin
+//    b* holding the k_b-th largest score; every score in bins >= b* is appended, in token
+//    order, to a segment of the sequence's candidate list (segments in chunk order).
+//  * decode_select_kernel: one workgroup per sequence joins the segments in LDS, finds the
+//    exact k_b-th key with an MSD radix select and writes the selection in ascending order;
+//    a sequence whose candidates exceed the LDS buffer is selected from its full score row.
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+#include "topk_device.hpp"
+
+namespace sa {
+
+namespace {
+
+constexpr int kH = 64;                 // index heads
+constexpr int kD = 128;                // index head width
+constexpr int kPage = 64;              // tokens per page
+constexpr int kIdxThreads = 256;       // indexer workgroup (4 waves)
+constexpr int kPagesPerWave = 4;
+constexpr int kKeysPerBlock = kPage * kPagesPerWave * (kIdxThreads / kWave);  // 1024
+constexpr int kCollectThreads = 256;
+constexpr int kChunkScores = 8192;     // scores per collect workgroup
+constexpr int kSelectWaves = 8;
+using topk::kBins;
+using topk::kBinShift;
+using topk::kCap;
+
+__device__ __forceinline__ bool decode_row_ok(const int32_t *ctx_len, const int32_t *topk_b, int32_t max_ctx,
+                                              int32_t max_topk, int64_t b, int64_t *n, int64_t *m)
+{
+    *n = ctx_len[b];
+    const int64_t k = topk_b[b];
+    if (*n < 1 || *n > max_ctx || k < 1 || k > max_topk) return false;
+    *m = k < *n ? k : *n;
+    return true;
+}
+
+__global__ void decode_reset_kernel(uint32_t *hist, int32_t *cand_count, int64_t B)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < B * kBins) hist[i] = 0;
+    if (i < B) cand_count[i] = 0;
+}
+
+__global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ kidx_pages,
+    int64_t n_pages, const int32_t *__restrict__ block_table, int32_t max_blocks,
+    const int32_t *__restrict__ ctx_len, int32_t max_ctx, float *__restrict__ scores, int64_t ld,
+    uint32_t *__restrict__ hist_g, uint32_t *err)
+{
+    __shared__ uint32_t hist[kBins];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const int64_t b = blockIdx.y;
+    const int64_t n = ctx_len[b];
+    if (n < 1 || n > max_ctx) {
+        if (tid == 0 && blockIdx.x == 0) flag_error(err, SA_DEVERR_CTX_LEN);
+        return;
+    }
+    const int64_t key0 = (int64_t)blockIdx.x * kKeysPerBlock;
+    if (key0 >= n) return;
+    for (int i = tid; i < kBins; i += kIdxThreads) hist[i] = 0;
+    __syncthreads();
+
+    // A operand (64 heads x 128 dims of q) and the head weights in the accumulator layout
+    bf16x8 a[2][kD / 16];
+    float wv[2][16];
+    const uint16_t *qr = q_idx + b * (int64_t)kH * kD;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks)
+            a[mt][ks] = as_bf16x8(load16(qr + (32 * mt + lane % 32) * kD + 16 * ks + 8 * (lane / 32)));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 16; ++g)
+            wv[mt][g] = w[b * kH + 32 * mt + 8 * (g / 4) + 4 * (lane / 32) + g % 4];
+
+    // this wave's pages: logical pages lp0 .. lp0 + 3
+    const int64_t lp0 = key0 / kPage + (int64_t)kPagesPerWave * wave;
+    int64_t page[kPagesPerWave];
+    bool page_ok[kPagesPerWave];
+#pragma unroll
+    for (int i = 0; i < kPagesPerWave; ++i) {
+        const bool used = (lp0 + i) * kPage < n;
+        const int32_t p = used ? block_table[b * max_blocks + lp0 + i] : 0;
+        page_ok[i] = p >= 0 && p < n_pages;
+        if (used && !page_ok[i] && lane == 0) flag_error(err, SA_DEVERR_BLOCK_TABLE);
+        page[i] = page_ok[i] ? p : 0;  // an unused or bad page is read from page 0 and ignored
+    }
+
+    // half-page h: keys 32 (h % 2) + l % 32 of page h / 2; lane l reads dims 16 ks + 8 (l / 32)
+    auto load_half = [&](int h, bf16x8 (&bf)[kD / 16]) {
+        const uint16_t *src = kidx_pages + (page[h / 2] * kPage + 32 * (h % 2) + lane % 32) * (int64_t)kD +
+                              8 * (lane / 32);
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) bf[ks] = as_bf16x8(load16(src + 16 * ks));
+    };
+    bf16x8 bc[kD / 16], bn[kD / 16];
+    load_half(0, bc);
+#pragma unroll
+    for (int h = 0; h < 2 * kPagesPerWave; ++h) {
+        const int64_t kbase = (lp0 + h / 2) * kPage + 32 * (h % 2);
+        if (h + 1 < 2 * kPagesPerWave) load_half(h + 1, bn);
+        if (kbase < n) {  // uniform over the wave
+            f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int ks = 0; ks < kD / 16; ++ks) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][ks], bc[ks], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][ks], bc[ks], acc1, 0, 0, 0);
+            }
+            // register g of lane l: head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4, key l % 32
+            float part = 0.f;
+#pragma unroll
+            for (int g = 0; g < 16; ++g) {
+                part = fmaf(wv[0][g], relu(acc0[g]), part);
+                part = fmaf(wv[1][g], relu(acc1[g]), part);
+            }
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                             false, false);
+            float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (!page_ok[h / 2]) score = -__builtin_inff();
+            const int64_t s = kbase + lane;
+            if (lane < 32 && s < n) {
+                scores[b * ld + s] = score;
+                atomicAdd(&hist[order_key(score) >> kBinShift], 1u);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) bc[ks] = bn[ks];
+    }
+    __syncthreads();
+    for (int i = tid; i < kBins; i += kIdxThreads) {
+        const uint32_t c = hist[i];
+        if (c) atomicAdd(&hist_g[b * kBins + i], c);
+    }
+}
+
+// Candidates of one chunk of a sequence's scores: those in bins >= b*, in token order.
+__global__ __launch_bounds__(kCollectThreads) void decode_collect_kernel(
+    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ctx_len, int32_t max_ctx,
+    const int32_t *__restrict__ topk_b, int32_t max_topk, const uint32_t *__restrict__ hist_g,
+    uint2 *__restrict__ cands, int32_t *__restrict__ cand_count, int2 *__restrict__ seg, int n_chunks)
+{
+    constexpr int kWaves = kCollectThreads / kWave;
+    constexpr int kPer = kChunkScores / kCollectThreads;  // 32 consecutive scores per thread
+    __shared__ int wave_sums[kWaves];
+    __shared__ int sh_bin, sh_base;
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int c = blockIdx.x;
+    int64_t n, m;
+    if (!decode_row_ok(ctx_len, topk_b, max_ctx, max_topk, b, &n, &m)) return;
+    if (m == n) return;  // every visible token is selected
+    const int64_t lo = (int64_t)c * kChunkScores;
+    if (lo >= n) return;
+    if (tid < kWave) {
+        const int bin = topk::threshold_bin(hist_g + b * kBins, (int)m, nullptr, nullptr);
+        if (tid == 0) sh_bin = bin;
+    }
+    __syncthreads();
+    const uint32_t key_lo = (uint32_t)sh_bin << kBinShift;
+
+    // this thread's 32 consecutive scores: positions lo + 32 tid ..
+    const int64_t s0 = lo + (int64_t)kPer * tid;
+    uint32_t keys[kPer];
+    uint32_t sel = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; i += 4) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (s0 + i + 3 < n) {
+            v = *reinterpret_cast<const float4 *>(scores + b * ld + s0 + i);
+        } else {
+            if (s0 + i < n) v.x = scores[b * ld + s0 + i];
+            if (s0 + i + 1 < n) v.y = scores[b * ld + s0 + i + 1];
+            if (s0 + i + 2 < n) v.z = scores[b * ld + s0 + i + 2];
+        }
+        keys[i] = order_key(v.x);
+        keys[i + 1] = order_key(v.y);
+        keys[i + 2] = order_key(v.z);
+        keys[i + 3] = order_key(v.w);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) sel |= (s0 + i < n && keys[i] >= key_lo ? 1u : 0u) << i;
+    int total;
+    int pos = topk::block_scan<kWaves>(__popc(sel), wave_sums, &total);
+    if (tid == 0) {
+        sh_base = atomicAdd(&cand_count[b], total);
+        seg[b * n_chunks + c] = make_int2(sh_base, total);
+    }
+    __syncthreads();
+    uint2 *dst = cands + b * kCap;
+    pos += sh_base;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if ((sel >> i) & 1u) {
+            if (pos < kCap) dst[pos] = make_uint2(keys[i], (uint32_t)(s0 + i));
+            ++pos;
+        }
+}
+
+__global__ __launch_bounds__(kSelectWaves *kWave) void decode_select_kernel(
+    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ctx_len, int32_t max_ctx,
+    const int32_t *__restrict__ topk_b, int32_t max_topk, const uint32_t *__restrict__ hist_g,
+    const uint2 *__restrict__ cands, const int32_t *__restrict__ cand_count, const int2 *__restrict__ seg,
+    int n_chunks, int32_t *__restrict__ idx, uint32_t *err)
+{
+    constexpr int kThreads = kSelectWaves * kWave;
+    __shared__ uint32_t ck[kCap];
+    __shared__ int32_t ci[kCap];
+    __shared__ topk::SelectShared<kSelectWaves> sh;
+    __shared__ int info[3];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    int32_t *dst = idx + b * max_topk;
+    int64_t n, m;
+    if (!decode_row_ok(ctx_len, topk_b, max_ctx, max_topk, b, &n, &m)) {
+        if (tid == 0) flag_error(err, SA_DEVERR_TOPK);
+        for (int i = tid; i < max_topk; i += kThreads) dst[i] = -1;
+        return;
+    }
+    if (m == n) {
+        for (int i = tid; i < max_topk; i += kThreads) dst[i] = i < n ? i : -1;
+        return;
+    }
+    if (tid < kWave) {
+        int above, upto;
+        const int bin = topk::threshold_bin(hist_g + b * kBins, (int)m, &above, &upto);
+        if (tid == 0) {
+            info[0] = bin;
+            info[1] = above;
+            info[2] = upto;
+        }
+    }
+    __syncthreads();
+    const int bin = info[0], above = info[1], upto = info[2];
+    if (upto <= kCap && cand_count[b] <= kCap) {
+        // join the chunk segments in chunk order (each is in token order)
+        const int used = (int)((n + kChunkScores - 1) / kChunkScores);
+        int at = 0;
+        for (int c = 0; c < used; ++c) {
+            const int2 sg = seg[b * n_chunks + c];
+            for (int j = tid; j < sg.y; j += kThreads) {
+                const uint2 v = cands[b * kCap + sg.x + j];
+                ck[at + j] = v.x;
+                ci[at + j] = (int32_t)v.y;
+            }
+            at += sg.y;
+        }
+        __syncthreads();
+        topk::select_and_emit(sh, topk::LdsCands{ck, ci}, at, bin, above, (int)m, dst);
+    } else {
+        topk::select_and_emit(sh, topk::GlobalScores{scores + b * ld}, (int)n, bin, above, (int)m, dst);
+    }
+    for (int i = (int)m + tid; i < max_topk; i += kThreads) dst[i] = -1;
+}
+
+}  // namespace
+
+DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
+{
+    DecodeTopkLayout l;
+    l.ld = (max_ctx + 63) / 64 * 64;
+    l.n_chunks = (max_ctx + kChunkScores - 1) / kChunkScores;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t off = at;
+        at += (bytes + 255) / 256 * 256;
+        return off;
+    };
+    l.scores = take((size_t)B * l.ld * sizeof(float));
+    l.hist = take((size_t)B * kBins * sizeof(uint32_t));
+    l.cands = take((size_t)B * kCap * sizeof(uint2));
+    l.cand_count = take((size_t)B * sizeof(int32_t));
+    l.seg = take((size_t)B * l.n_chunks * sizeof(int2));
+    l.total = at;
+    return l;
+}
+
+hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                      const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
+                                      int32_t *idx, void *ws, hipStream_t st)
+{
+    const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
+    char *base = reinterpret_cast<char *>(ws);
+    float *scores = reinterpret_cast<float *>(base + l.scores);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(base + l.hist);
+    uint2 *cands = reinterpret_cast<uint2 *>(base + l.cands);
+    int32_t *cand_count = reinterpret_cast<int32_t *>(base + l.cand_count);
+    int2 *seg = reinterpret_cast<int2 *>(base + l.seg);
+    const int32_t max_topk = h.cfg.max_topk;
+    {
+        const int64_t nz = (int64_t)B * kBins;
+        hipLaunchKernelGGL(decode_reset_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist,
+                           cand_count, (int64_t)B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        KernelTimer timer(h, SA_KERNEL_INDEXER, st);
+        dim3 grid((unsigned)((max_ctx + kKeysPerBlock - 1) / kKeysPerBlock), (unsigned)B);
+        hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(kIdxThreads), 0, st,
+                           reinterpret_cast<const uint16_t *>(q_idx), w,
+                           reinterpret_cast<const uint16_t *>(kidx_pages), n_pages, block_table, max_blocks,
+                           ctx_len, max_ctx, scores, l.ld, hist, h.d_err);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    KernelTimer timer(h, SA_KERNEL_TOPK, st);
+    hipLaunchKernelGGL(decode_collect_kernel, dim3((unsigned)l.n_chunks, (unsigned)B), dim3(kCollectThreads), 0,
+                       st, scores, l.ld, ctx_len, max_ctx, topk_b, max_topk, hist, cands, cand_count, seg,
+                       (int)l.n_chunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)B), dim3(kSelectWaves * kWave), 0, st, scores, l.ld,
+                       ctx_len, max_ctx, topk_b, max_topk, hist, cands, cand_count, seg, (int)l.n_chunks, idx,
+                       h.d_err);
+    return hipGetLastError();
+}
+
+}  // namespace sa

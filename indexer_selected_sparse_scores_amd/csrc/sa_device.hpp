@@ -55,6 +55,13 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// max(x, 0) as one signed-integer max on the bits: a float with the sign bit set is a
+// negative int and becomes +0; fmaxf would first canonicalise x (one more instruction).
+__device__ __forceinline__ float relu(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 __device__ __forceinline__ void flag_error(uint32_t *err, uint32_t bit)
 {
     if (err) atomicOr(err, bit);

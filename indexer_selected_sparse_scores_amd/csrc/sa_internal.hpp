@@ -17,6 +17,7 @@ struct sa_handle_s {
     int device;
     int n_cu;               // compute units of the device (sizes persistent grids)
     bool fast_indexer;      // bf16, H_I = 64, d_I = 128: MFMA indexer kernels
+    bool fast_decode;       // fast_indexer with 64-token pages: the paged decode kernels
     bool fast_attn;         // bf16, H = 16, H_kv = 1, d_qk = 576, d_v = 512, v_from_k
     std::string last_error;
 
@@ -97,6 +98,19 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows,
 size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L);
 hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
                                int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st);
+
+// ---- paged decode indexer + per-sequence top-k (bf16, H_I = 64, d_I = 128, 64-token pages) --
+struct DecodeTopkLayout {
+    int64_t ld;          // score row stride (floats)
+    int64_t n_chunks;    // 8192-score chunks per sequence
+    size_t scores, hist, cands, cand_count, seg, total;  // byte offsets in the workspace
+};
+DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx);
+// idx [B, max_topk] gets each sequence's selection; ws holds decode_topk_layout(B, max_ctx).total
+hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                      const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
+                                      int32_t *idx, void *ws, hipStream_t st);
 
 // Workspace bytes launch_attention needs for n_rows decode rows (split partials).
 size_t attention_workspace(const sa_handle_s &h, int64_t n_rows, bool decode);

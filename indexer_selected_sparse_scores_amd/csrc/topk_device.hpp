@@ -1,0 +1,211 @@
+// Device building blocks of the exact per-row top-k shared by the prefill and decode kernels.
+//
+// Selection order: larger score first, ties to the lower token index -- the per-query
+// token selection of "Sparse Attention and RL Optimization: Three Technical Breakthroughs in
+// LLM Post-Training", section 2.3.  Scores are compared through order_key(), an order-
+// preserving map of fp32 to uint32.  The top 11 key bits (2048 bins) give a histogram from
+// which the bin holding the m-th largest score is found; the final choice inside that bin is
+// an MSD radix select over the remaining 21 bits, and an ordered compaction emits the
+// selection in ascending token order.
+#pragma once
+
+#include "sa_device.hpp"
+
+namespace sa {
+namespace topk {
+
+constexpr int kBins = 2048;         // histogram bins over the key's top 11 bits
+constexpr int kBinShift = 21;
+constexpr int kCap = 8192;          // candidates held in LDS for the final selection
+constexpr int kPerThread = 16;      // consecutive candidates per thread in ordered passes
+
+// Workgroup-shared scratch of the selection helpers (kWaves waves).
+template <int kWaves>
+struct SelectShared {
+    uint32_t radix[128];
+    int wave_sums[kWaves];
+    uint32_t digit;
+    int need;
+};
+
+// Exclusive prefix sum over the kWaves * 64 threads (thread order); *total gets the sum.
+template <int kWaves>
+__device__ __forceinline__ int block_scan(int v, int *wave_sums, int *total)
+{
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int s = wave_sums[i];
+        before += i < wave ? s : 0;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return x - v + before;
+}
+
+// One wave: the highest bin b of a 2048-bin histogram (LDS or global memory) such that the
+// bins >= b hold at least m entries.  Returns -1 if the whole histogram holds fewer than m.
+// *above = entries in bins > b, *upto = entries in bins >= b (either may be NULL).  Every
+// lane returns the same values.
+__device__ __forceinline__ int threshold_bin(const uint32_t *hist, int m, int *above, int *upto)
+{
+    const int lane = lane_id();
+    // lane l covers bins [kBins - 32 (l + 1), kBins - 32 l): lane 0 holds the top bins
+    const uint32_t *hb = hist + kBins - 32 * (lane + 1);
+    uint32_t c[32];
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(hb + i);
+        c[i] = v.x;
+        c[i + 1] = v.y;
+        c[i + 2] = v.z;
+        c[i + 3] = v.w;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sum += (int)c[i];
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    const uint64_t hit = __ballot(incl >= m);
+    if (hit == 0) {
+        if (above) *above = 0;
+        if (upto) *upto = __shfl(incl, kWave - 1);
+        return -1;
+    }
+    const int src = __builtin_ctzll(hit);
+    // every lane walks its own bins from the top (only lane src's answer is used)
+    int cum = incl - sum, bin = -1, ab = 0, up = 0;
+#pragma unroll
+    for (int i = 31; i >= 0; --i) {
+        const int ci = (int)c[i];
+        const bool here = bin < 0 && cum + ci >= m;
+        bin = here ? kBins - 32 * (lane + 1) + i : bin;
+        ab = here ? cum : ab;
+        up = here ? cum + ci : up;
+        cum += ci;
+    }
+    if (above) *above = __shfl(ab, src);
+    if (upto) *upto = __shfl(up, src);
+    return __shfl(bin, src);
+}
+
+// Candidate sources for select_and_emit: element j has key k(j) and token index i(j); the
+// elements are in ascending token order.
+struct LdsCands {
+    const uint32_t *key;
+    const int32_t *idx;
+    __device__ uint32_t k(int j) const { return key[j]; }
+    __device__ int32_t i(int j) const { return idx[j]; }
+};
+struct GlobalCands {
+    const uint2 *c;  // (key, index)
+    __device__ uint32_t k(int j) const { return c[j].x; }
+    __device__ int32_t i(int j) const { return (int32_t)c[j].y; }
+};
+struct GlobalScores {
+    const float *s;  // a score row; element j is token j
+    __device__ uint32_t k(int j) const { return order_key(s[j]); }
+    __device__ int32_t i(int j) const { return j; }
+};
+
+// Exact selection of the `need` largest keys among the n candidates whose top bits equal
+// `bin` (the ones in higher bins are all taken: `above` of them), then an ordered emit of the
+// m = above + need selected indices (ascending) into dst[0, m).  Candidates in lower bins are
+// skipped.  Every thread of the workgroup calls this.
+template <int kWaves, class Src>
+__device__ __noinline__ void select_and_emit(SelectShared<kWaves> &sh, const Src &src, int n, int bin,
+                                             int above, int m, int32_t *dst)
+{
+    constexpr int kThreads = kWaves * kWave;
+    const int tid = threadIdx.x;
+    int need = m - above;  // >= 1
+    uint32_t prefix = (uint32_t)bin << kBinShift, mask = 0xFFFFFFFFu << kBinShift;
+#pragma unroll 1
+    for (int shift = 14; shift >= 0; shift -= 7) {
+        if (tid < 128) sh.radix[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += kThreads) {
+            const uint32_t key = src.k(j);
+            if ((key & mask) == prefix) atomicAdd(&sh.radix[(key >> shift) & 127u], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l looks at digits 127 - 2l and 126 - 2l (descending)
+            const int c_hi = (int)sh.radix[127 - 2 * tid], c_lo = (int)sh.radix[126 - 2 * tid];
+            const int c = c_hi + c_lo;
+            int incl = c;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (tid >= off) incl += y;
+            }
+            const int excl = incl - c;
+            if (excl < need && need <= incl) {
+                if (need <= excl + c_hi) {
+                    sh.digit = 127u - 2u * tid;
+                    sh.need = need - excl;
+                } else {
+                    sh.digit = 126u - 2u * tid;
+                    sh.need = need - excl - c_hi;
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= sh.digit << shift;
+        mask |= 127u << shift;
+        need = sh.need;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;  // exact key of the m-th largest score
+
+    // ordered emit: every key > tau, then the first `need` keys == tau (lowest indices)
+    int eq_before = 0, out_before = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += kThreads * kPerThread) {
+        const int j0 = base + tid * kPerThread;
+        uint32_t gt = 0, eq = 0;  // bit i: candidate j0 + i
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int j = j0 + i;
+            if (j < n) {
+                const uint32_t key = src.k(j);
+                gt |= (key > tau ? 1u : 0u) << i;
+                eq |= (key == tau ? 1u : 0u) << i;
+            }
+        }
+        int eq_total;
+        int eq_rank = block_scan<kWaves>(__popc(eq), sh.wave_sums, &eq_total) + eq_before;
+        uint32_t take = gt;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            if ((eq >> i) & 1u) {
+                if (eq_rank < need) take |= 1u << i;
+                ++eq_rank;
+            }
+        }
+        int take_total;
+        int pos = block_scan<kWaves>(__popc(take), sh.wave_sums, &take_total) + out_before;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+            if (((take >> i) & 1u) && pos < m) dst[pos++] = src.i(j0 + i);
+        eq_before += eq_total;
+        out_before += take_total;
+    }
+}
+
+}  // namespace topk
+}  // namespace sa

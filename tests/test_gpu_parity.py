@@ -325,6 +325,36 @@ def test_decode_b64_sampled():
     _check_decode(d, out, lse, idx, sorted(set(seqs)), 512, "decode_b64")
 
 
+def test_decode_b64_128k_sampled():
+    """The decode step exactly as the benchmark runs it (64 sequences at 131072 tokens)."""
+    wl = inputs.WORKLOADS["decode_b64_128k"]
+    say("decode decode_b64_128k B=64 ctx=131072 topk=2048 (4 sequences checked)")
+    d = inputs.decode_inputs(wl, DEV)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _decode(h, d)
+    _check_decode(d, out, lse, idx, [0, 21, 42, 63], 512, "decode_b64_128k")
+    del out, lse, idx, d
+    torch.cuda.empty_cache()
+
+
+def test_decode_all_scores_tied():
+    """q_idx = 0 makes every score exactly 0: each sequence selects its lowest k_b tokens.  The
+    long sequences have more tied candidates than the on-chip buffer holds."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [5, 300, 2049, 9000, 20000]
+    say(f"decode all-tied scores ctx={ctx} topk=2048")
+    d = inputs.decode_inputs(inputs.small(wl, topk=2048), DEV, ctx=ctx, seed=9)
+    d["q_idx"] = torch.zeros_like(d["q_idx"])
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _decode(h, d)
+    gi = to_np(idx)
+    for b, n in enumerate(ctx):
+        m = min(2048, n)
+        assert np.array_equal(gi[b][:m], np.arange(m)), f"seq {b}"
+        assert np.all(gi[b][m:] == -1)
+    _check_decode(d, out, lse, idx, np.arange(len(ctx)), 512, "decode all-tied")
+
+
 @pytest.mark.parametrize("n", [1024, 5120, 32768])
 def test_decode_rl_sweep_step(n):
     wl = inputs.WORKLOADS["decode_rl_sweep"]
