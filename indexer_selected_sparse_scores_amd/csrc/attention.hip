@@ -63,20 +63,23 @@ __device__ __forceinline__ int64_t token_offset(const RowSource &src, int64_t b,
 constexpr int kLH = 16;         // query heads
 constexpr int kLDqk = 576;      // key width
 constexpr int kLDv = 512;       // value width (leading columns of the key row)
-constexpr int kChunk = 64;      // selected rows per chunk
-constexpr int kAThreads = 512;  // 8 waves
-constexpr int kRowBytes = kLDqk * 2;
+constexpr int kChunk = 32;      // selected rows per chunk
+constexpr int kAWaves = 4;
+constexpr int kAThreads = kAWaves * kWave;
 constexpr int kLdsRow = kLDv * 2 + 16;                  // padded LDS row of the value part (bytes)
 constexpr int kKSteps = kLDqk / 32;                     // 18 k-steps of the logits MFMA
-constexpr int kKHalf = kKSteps / 2;                     // each wave group takes half of them
+constexpr int kKHalf = kKSteps / 2;                     // each wave pair takes half of them
 constexpr int kLogitLd = kChunk + 4;                    // padded per-head row of logits (floats)
 constexpr int kVPieces = kLDv / 8;                      // 16-byte pieces of the value part (64)
+constexpr int kColsPerWave = kLDv / kAWaves;            // 128 value columns per wave
+constexpr int kNTiles = kColsPerWave / 16;              // 8 MFMA column tiles per wave
+constexpr int kHeadsPerWave = kLH / kAWaves;            // softmax heads owned by a wave (4)
 
 struct AttnShared {
-    unsigned char rows[kChunk * kLdsRow];   // value part of the current chunk's rows
+    unsigned char vrows[kChunk * kLdsRow];  // value part of the current chunk's rows
     float logits[2][kLH * kLogitLd];        // partial logits of the two K-halves, [head][slot]
-    uint4 p_hi[2][kLH][4];                  // P as the A operand of P.V: [half][head][lane group]
-    uint4 p_lo[2][kLH][4];                  //   (8 bf16 each), hi part and bf16 residual
+    uint4 p_hi[kLH][4];                     // P as the A operand of P.V: [head][lane group]
+    uint4 p_lo[kLH][4];                     //   (8 bf16 each), hi part and bf16 residual
     float alpha[kLH];                       // per-head rescale of this chunk
     float inv_l[kLH];                       // per-head 1 / softmax sum (end of the row)
     int64_t row_off[2][kChunk];             // element offsets of a chunk's rows (-1: none)
@@ -95,11 +98,11 @@ __device__ __forceinline__ int64_t slot_offset(const RowSource &kv, const int32_
     return off;
 }
 
-// The P.V contraction runs over the 64 rows of a chunk in an order of our choosing, as long
-// as P and V agree.  MFMA k index 8 g + j (lane group g = lane / 16, j = 0..7) of a 32-row
-// half is row 8 g + 2 j (j < 4) or 8 g + 2 (j - 4) + 1 (j >= 4): the V fragment is then two
-// transposing LDS reads over rows two apart, which fall in disjoint banks.  slot_of_row
-// inverts the map; logits are stored at their slot so that P is produced in k order.
+// The P.V contraction runs over the 32 rows of a chunk in an order of our choosing, as long
+// as P and V agree.  MFMA k index 8 g + j (lane group g = lane / 16, j = 0..7) is row 8 g + 2 j
+// (j < 4) or 8 g + 2 (j - 4) + 1 (j >= 4): the V fragment is then two transposing LDS reads
+// over rows two apart, which fall in disjoint banks.  slot_of_row inverts the map; logits are
+// stored at their slot so that P is produced in k order.
 __device__ __forceinline__ int slot_of_row(int row)
 {
     const int w = row & 7;
@@ -117,18 +120,36 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char *p)
         (__attribute__((address_space(3))) s16x4 *)(reinterpret_cast<uintptr_t>(p)));
 }
 
-// One workgroup = one query row (all 16 heads) and a range of its selected rows, processed
-// in chunks of 64 rows.  Wave w computes the logits of rows 16 (w % 4) .. +15 over half
-// w / 4 of the 576-wide contraction (v_mfma_f32_16x16x32_bf16, q fragments in registers);
-// each thread gathers exactly the nine 16-byte pieces of K its own MFMAs consume, so the
-// logits come straight from registers, and only the value part of the rows goes through LDS.
-// The gather of chunk c+1, the page lookup of chunk c+2 and the index of chunk c+3 are in
-// flight while chunk c is computed.  Wave w owns the online softmax of heads 2w and 2w+1
-// (running max / sum, exp2 with log2(e) folded into the scale) and publishes P as bf16 hi +
-// residual, so the weights keep ~16 mantissa bits; every wave then accumulates P.V for 64 of
-// the 512 value columns, with V fragments from transposing LDS reads.
+// Max / sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp_mov<kDppXor1>(x));
+    x = fmaxf(x, dpp_mov<kDppXor2>(x));
+    x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+    return fmaxf(x, dpp_mov<kDppRowMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    x += dpp_mov<kDppRowHalfMirror>(x);
+    return x + dpp_mov<kDppRowMirror>(x);
+}
+
+// One 4-wave workgroup = one query row (all 16 heads) and a range of its selected rows, in
+// chunks of 32 rows; three workgroups share a compute unit, so one's barriers and memory
+// waits overlap the others' work.  Per chunk:
+//  * logits: wave w takes rows 16 (w % 2) .. +15 over half w / 2 of the 576-wide contraction
+//    (v_mfma_f32_16x16x32_bf16, q fragments in registers).  Each thread gathers exactly the
+//    nine 16-byte pieces of K its own MFMAs consume (16-byte loads, one chunk ahead), so the
+//    logits come straight from registers; only the value part of the rows goes through LDS.
+//  * online softmax: wave w owns heads 4w .. 4w+3 (running max / sum, exp2 with log2(e)
+//    folded into the scale) and publishes P as bf16 hi + residual (~16 mantissa bits).
+//  * P.V: every wave accumulates 128 of the 512 value columns, with V fragments from
+//    transposing LDS reads.
+// Row offsets run two chunks ahead (index load, then page lookup, then use).
 template <bool kSplit>
-__global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
+__global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     const uint16_t *__restrict__ q, int64_t n_rows, RowSource kv, Visibility vis, Selection sel,
     float scale_log2, float *__restrict__ out, float *__restrict__ lse, int split_rows, int n_splits,
     float *__restrict__ part_o, float *__restrict__ part_ml, uint32_t *err)
@@ -150,16 +171,15 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
     const uint16_t *kv_base = reinterpret_cast<const uint16_t *>(kv.base);
     const int n_chunks = (int)((j_end - j_begin + kChunk - 1) / kChunk);
 
-    // logits: wave w covers rows 16 (w % 4) .. +15 and k-steps 9 (w / 4) .. +8
-    const int nt_qk = wave & 3, kh = wave >> 2;
-    const int my_row = 16 * nt_qk + hh;             // the chunk row this lane's K pieces come from
+    const int nt_qk = wave & 1, kh = wave >> 1;
+    const int my_row = 16 * nt_qk + hh;  // the chunk row whose K pieces this lane gathers
     bf16x8 qa[kKHalf];
     const uint16_t *qr = q + (r * kLH + hh) * kLDqk;
 #pragma unroll
     for (int i = 0; i < kKHalf; ++i) qa[i] = as_bf16x8(load16(qr + 32 * (kKHalf * kh + i) + 8 * grp));
 
     // offsets of chunks 0 and 1; the index of chunk 2 waits in a register
-    int64_t pend_j = j_begin + 2 * kChunk + tid;   // slot whose index `pend_s` holds
+    int64_t pend_j = j_begin + 2 * kChunk + tid;  // slot whose index `pend_s` holds
     int64_t pend_s = -1;
     if (tid < kChunk) {
         sh.row_off[0][tid] = slot_offset(kv, idx_row, r, j_begin + tid, j_end, visible, err);
@@ -168,13 +188,18 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
     }
     __syncthreads();
 
-    // piece i of this thread: 16 bytes at dims 32 (9 kh + i) + 8 grp of row my_row
+    // piece i of this thread: 16 bytes at dims 32 (9 kh + i) + 8 grp of row my_row; an unused
+    // slot reads the first row of the source and is zeroed (no branch around the loads)
     uint4 g[kKHalf];
     auto gather = [&](int buf) {
         const int64_t off = sh.row_off[buf][my_row];
+        const uint16_t *src = kv_base + (off >= 0 ? off : 0) + 32 * kKHalf * kh + 8 * grp;
 #pragma unroll
-        for (int i = 0; i < kKHalf; ++i)
-            g[i] = off >= 0 ? load16(kv_base + off + 32 * (kKHalf * kh + i) + 8 * grp) : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < kKHalf; ++i) g[i] = load16(src + 32 * i);
+        if (off < 0) {
+#pragma unroll
+            for (int i = 0; i < kKHalf; ++i) g[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
     };
     // the value part (pieces 0..63 of a row) goes to LDS for P.V
     auto stash = [&]() {
@@ -182,26 +207,23 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
         for (int i = 0; i < kKHalf; ++i) {
             const int piece = 4 * (kKHalf * kh + i) + grp;
             if (piece < kVPieces)
-                *reinterpret_cast<uint4 *>(sh.rows + my_row * kLdsRow + piece * 16) = g[i];
+                *reinterpret_cast<uint4 *>(sh.vrows + my_row * kLdsRow + piece * 16) = g[i];
         }
     };
     gather(0);
     stash();
-    uint4 kf[kKHalf];  // K pieces of the chunk being computed
-#pragma unroll
-    for (int i = 0; i < kKHalf; ++i) kf[i] = g[i];
 
     const float neg_inf = -__builtin_inff();
-    // softmax state of head 2 wave + lane / 32 (log2 domain), owned by this wave
-    const int sm_head = 2 * wave + lane / 32;
+    // softmax state of head 4 wave + lane / 16 (log2 domain), owned by this wave
+    const int sm_head = kHeadsPerWave * wave + grp;
     float m_run = neg_inf, l_run = 0.f;
-    f32x4 acc[4];  // O[4 grp + i][64 wave + 16 nt + hh]
+    f32x4 acc[kNTiles];  // O[4 grp + i][128 wave + 16 nt + hh]
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kNTiles; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll 1
     for (int c = 0; c < n_chunks; ++c) {
-        // rows = values of chunk c, kf = K pieces of chunk c, row_off[c & 1] = chunk c,
+        // vrows = values of chunk c, kf = K pieces of chunk c, row_off[c & 1] = chunk c,
         // row_off[(c + 1) & 1] = chunk c + 1
         const bool more = c + 1 < n_chunks;
         // Slot pend_j (chunk c + 2): its index arrived during the previous chunk; its page
@@ -225,17 +247,18 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
         pend_j += kChunk;
         pend_s = -1;
         if (tid < kChunk && pend_j < j_end) pend_s = idx_row[pend_j];
-        if (more) gather((c + 1) & 1);
 
-        // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh
+        // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh; g holds
+        // this chunk's K pieces until the MFMAs have taken them, then the next chunk's gather
         {
             f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = {0.f, 0.f, 0.f, 0.f};  // two chains
 #pragma unroll
             for (int i = 0; i < kKHalf; i += 2) {
-                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], as_bf16x8(kf[i]), sa0, 0, 0, 0);
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], as_bf16x8(g[i]), sa0, 0, 0, 0);
                 if (i + 1 < kKHalf)
-                    sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i + 1], as_bf16x8(kf[i + 1]), sa1, 0, 0, 0);
+                    sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i + 1], as_bf16x8(g[i + 1]), sa1, 0, 0, 0);
             }
+            if (more) gather((c + 1) & 1);
             const f32x4 sacc = sa0 + sa1;
             // output (head 4 grp + i, row my_row)
             const bool valid = sh.row_off[c & 1][my_row] >= 0;
@@ -245,58 +268,58 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
         }
         __syncthreads();
 
-        // online softmax of head sm_head over the 64 slots: this lane takes slots l % 32 and
-        // 32 + l % 32
+        // online softmax of head sm_head over the 32 slots: this lane takes slots l % 16 and
+        // 16 + l % 16
         {
-            const int sl = lane % 32;
-            const float* lg0 = &sh.logits[0][sm_head * kLogitLd];
-            const float* lg1 = &sh.logits[1][sm_head * kLogitLd];
+            const int sl = hh;
+            const float *lg0 = &sh.logits[0][sm_head * kLogitLd];
+            const float *lg1 = &sh.logits[1][sm_head * kLogitLd];
             const float x0 = (lg0[sl] + lg1[sl]) * scale_log2;
-            const float x1 = (lg0[32 + sl] + lg1[32 + sl]) * scale_log2;
-            const float cmax = half_wave_max(fmaxf(x0, x1));
+            const float x1 = (lg0[16 + sl] + lg1[16 + sl]) * scale_log2;
+            const float cmax = row16_max(fmaxf(x0, x1));
             const float m_new = fmaxf(m_run, cmax);
             const bool any = m_new != neg_inf;
             const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
             const float p0 = any ? __builtin_amdgcn_exp2f(x0 - m_new) : 0.f;
             const float p1 = any ? __builtin_amdgcn_exp2f(x1 - m_new) : 0.f;
-            const float psum = half_wave_sum(p0 + p1);
+            const float psum = row16_sum(p0 + p1);
             l_run = l_run * alpha + psum;
             m_run = m_new;
-            // slot sl is MFMA k index sl of half 0 (lane group sl / 8, element sl % 8)
+            // slot s is MFMA k index s (lane group s / 8, element s % 8)
             const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
             const __bf16 r0 = (__bf16)(p0 - (float)h0), r1 = (__bf16)(p1 - (float)h1);
-            __bf16 *ph = reinterpret_cast<__bf16 *>(&sh.p_hi[0][sm_head][0]);
-            __bf16 *pl = reinterpret_cast<__bf16 *>(&sh.p_lo[0][sm_head][0]);
+            __bf16 *ph = reinterpret_cast<__bf16 *>(&sh.p_hi[sm_head][0]);
+            __bf16 *pl = reinterpret_cast<__bf16 *>(&sh.p_lo[sm_head][0]);
             ph[sl] = h0;
             pl[sl] = r0;
-            ph[kLH * 32 + sl] = h1;  // half 1
-            pl[kLH * 32 + sl] = r1;
+            ph[16 + sl] = h1;
+            pl[16 + sl] = r1;
             if (sl == 0) sh.alpha[sm_head] = alpha;
         }
         __syncthreads();
 
-        // rescale the accumulator rows (heads 4 grp + i), then P.V over the 64 rows
+        // rescale the accumulator rows (heads 4 grp + i), then P.V over the 32 rows
         {
             const float4 al = *reinterpret_cast<const float4 *>(&sh.alpha[4 * grp]);
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
+            for (int nt = 0; nt < kNTiles; ++nt) {
                 acc[nt][0] *= al.x;
                 acc[nt][1] *= al.y;
                 acc[nt][2] *= al.z;
                 acc[nt][3] *= al.w;
             }
         }
-        // B fragment of lane (hh, grp): rows 32 ks + 8 grp + {0, 2, 4, 6} then {1, 3, 5, 7},
-        // column 64 wave + 16 nt + hh, via two transposing reads whose lanes point at row
-        // 32 ks + 8 grp + 2 (hh / 4) (+1) and columns 64 wave + 16 nt + 4 (hh % 4) .. +3.
+        // B fragment of lane (hh, grp): rows 8 grp + {0, 2, 4, 6} then {1, 3, 5, 7}, column
+        // 128 wave + 16 nt + hh, via two transposing reads whose lanes point at row
+        // 8 grp + 2 (hh / 4) (+1) and columns 128 wave + 16 nt + 4 (hh % 4) .. +3.
+        {
+            const bf16x8 pa_hi = as_bf16x8(sh.p_hi[hh][grp]);
+            const bf16x8 pa_lo = as_bf16x8(sh.p_lo[hh][grp]);
+            const unsigned char *vb0 = sh.vrows + (8 * grp + 2 * (hh / 4)) * kLdsRow +
+                                       2 * (kColsPerWave * wave + 4 * (hh % 4));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 pa_hi = as_bf16x8(sh.p_hi[ks][hh][grp]);
-            const bf16x8 pa_lo = as_bf16x8(sh.p_lo[ks][hh][grp]);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const unsigned char *vb = sh.rows + (32 * ks + 8 * grp + 2 * (hh / 4)) * kLdsRow +
-                                          2 * (64 * wave + 16 * nt + 4 * (hh % 4));
+            for (int nt = 0; nt < kNTiles; ++nt) {
+                const unsigned char *vb = vb0 + 2 * 16 * nt;
                 const s16x4 lo4 = lds_read_tr16(vb);
                 const s16x4 hi4 = lds_read_tr16(vb + kLdsRow);
                 const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -304,9 +327,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, b, acc[nt], 0, 0, 0);
             }
         }
-        // row_off[c & 1] was last read by this chunk's logits (before the barrier above); it
-        // now takes chunk c + 2, which the gather of the next iteration reads after the
-        // barrier below
+        // row_off[c & 1] was last read by this chunk's logits (before the barriers above); it
+        // now takes chunk c + 2, which the next iteration's gather reads after the barrier below
         if (page_pending) {
             if (page >= 0 && page < kv.n_pages) {
                 off_next = ((int64_t)page * kv.page_size + s_next % kv.page_size) * kv.row_elems;
@@ -315,36 +337,31 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_latent_mfma_kernel(
             }
         }
         if (tid < kChunk) sh.row_off[c & 1][tid] = off_next;
-        __syncthreads();  // every wave is done with rows, logits and P; row_off is published
-        if (more) {
-            stash();
-#pragma unroll
-            for (int i = 0; i < kKHalf; ++i) kf[i] = g[i];
-        }
+        __syncthreads();  // every wave is done with vrows, logits and P; row_off is published
+        if (more) stash();
     }
 
     if (!kSplit) {
-        if (lane % 32 == 0) sh.inv_l[sm_head] = l_run > 0.f ? 1.f / l_run : 0.f;
-        if (lse && lane % 32 == 0)
-            lse[r * kLH + sm_head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
+        if (hh == 0) sh.inv_l[sm_head] = l_run > 0.f ? 1.f / l_run : 0.f;
+        if (lse && hh == 0) lse[r * kLH + sm_head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
         __syncthreads();
         const float4 iv = *reinterpret_cast<const float4 *>(&sh.inv_l[4 * grp]);
         const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float *orow = out + (r * kLH + 4 * grp + i) * kLDv + 64 * wave + hh;
+            float *orow = out + (r * kLH + 4 * grp + i) * kLDv + kColsPerWave * wave + hh;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) orow[16 * nt] = acc[nt][i] * ivs[i];
+            for (int nt = 0; nt < kNTiles; ++nt) orow[16 * nt] = acc[nt][i] * ivs[i];
         }
     } else {
         const int64_t slot = r * n_splits + split;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float *prow = part_o + (slot * kLH + 4 * grp + i) * kLDv + 64 * wave + hh;
+            float *prow = part_o + (slot * kLH + 4 * grp + i) * kLDv + kColsPerWave * wave + hh;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) prow[16 * nt] = acc[nt][i];
+            for (int nt = 0; nt < kNTiles; ++nt) prow[16 * nt] = acc[nt][i];
         }
-        if (lane % 32 == 0) {
+        if (hh == 0) {
             part_ml[(slot * kLH + sm_head) * 2 + 0] = m_run;
             part_ml[(slot * kLH + sm_head) * 2 + 1] = l_run;
         }
