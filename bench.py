@@ -8,21 +8,30 @@ attention over the selected rows of the paged cache).  Inputs are seeded synthet
 resident in HBM before timing starts.
 
 Prints one JSON line: `value` is prefill tokens/s at 128K context; decode tokens/s, the
-per-kernel times (HIP events recorded by the library on the launch stream), the roofline
-of the dominant kernel and the CPU oracle's throughput on a bounded sample ride along.
+per-kernel times (HIP events the library records around each launch on the launch stream),
+the roofline of the dominant kernel (the fused prefill indexer / top-k) and of the decode
+kernels, and the CPU oracle's throughput on a bounded sample ride along.
+
+HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
+calibrated on the 1 GiB copy it performs after the warm-up, and stored in
+profiles/traffic.json together with a hash of the kernel sources; it is reported only while
+the sources still match.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "decode tokens/s and prefill tokens/s at 128K ctx, top-k=2048; % of MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CALIBRATION_BYTES = 1 << 30  # the plain copy whose counters calibrate FETCH_SIZE / WRITE_SIZE
+CSRC = os.path.join(ROOT, "indexer_selected_sparse_scores_amd", "csrc")
 
 
 def log(*a):
@@ -41,7 +50,29 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     return ap.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in sorted(files):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str):
+    """Calibrated HBM bytes per launch of `kernel` from profiles/traffic.json, or None when
+    absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(kernel)
+    if not rec or rec.get("source_sha256") != source_hash(rec["sources"]):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def main():
@@ -104,6 +135,15 @@ def main():
     sa.sparse_attn_check(h_pre)
     sa.sparse_attn_check(h_dec)
 
+    # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the traffic counters
+    cal_src = torch.ones(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    peaks = None if args.no_peaks else measured_peaks(torch)
+
     profile = not args.no_profile
     if profile:
         sa.sparse_attn_profile(h_pre, True)
@@ -130,18 +170,21 @@ def main():
 
     # algorithmic work (per step)
     pairs = L * (L + 1) // 2
-    idx_flops = pairs * 2 * s.n_idx_heads * s.d_idx
+    flop_per_pair = 2 * s.n_idx_heads * s.d_idx
+    idx_flops = pairs * flop_per_pair
     ctx_total = int(D["ctx_np"].sum())
-    dec_idx_bytes = ctx_total * s.d_idx * 2
+    key_bytes = s.d_idx * 2
+    dec_idx_bytes = ctx_total * key_bytes
     sel_rows = int(np.minimum(D["ctx_np"], K).sum())
-    dec_gather_bytes = sel_rows * s.d_qk * 2
+    row_bytes = s.d_qk * 2
+    dec_gather_bytes = sel_rows * row_bytes
 
     def per_launch(kern, kind):
         ms, n = kern.get(kind, (0.0, 0))
         return (ms / n, n, ms) if n else (None, 0, 0.0)
 
     kernels = {}
-    roofline = roofline_dec = None
+    roofline = roofline_dec_idx = roofline_dec_attn = None
     if profile:
         for name, kern in (("prefill", kern_pre), ("decode", kern_dec)):
             for kind in sa.KERNEL_KINDS:
@@ -152,25 +195,31 @@ def main():
                                                  "ms_per_step": round(tot / args.steps, 4)}
         avg, n, tot = per_launch(kern_pre, "indexer")
         if n:
-            tflops = idx_flops * args.steps / (tot * 1e-3) / 1e12
-            roofline = {"kernel": "indexer_mfma_kernel (prefill)", "bound": "mfma",
+            tflops = idx_flops / (avg * 1e-3) / 1e12
+            roofline = {"kernel": "indexer_topk_prefill_kernel", "bound": "mfma",
                         "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                        "algorithmic_per_step": f"{idx_flops:.4g} flop = {pairs} causal pairs x "
-                                                f"{2 * s.n_idx_heads * s.d_idx} flop"}
+                        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                        "traffic": stored_traffic("indexer_topk_prefill_kernel"),
+                        "algorithmic_per_launch": f"{idx_flops:.4g} flop = {pairs} causal (t,s) pairs x "
+                                                  f"{flop_per_pair} flop (2 H_I d_I)"}
         avg, n, tot = per_launch(kern_dec, "indexer")
         if n:
-            gbs = dec_idx_bytes * args.steps / (tot * 1e-3) / 1e9
-            roofline_dec = {"kernel": "indexer_mfma_kernel (paged decode)", "bound": "hbm",
-                            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                            "algorithmic_per_step": f"{dec_idx_bytes} B = {ctx_total} context tokens x "
-                                                    f"{s.d_idx * 2} B of index key"}
+            gbs = dec_idx_bytes / (avg * 1e-3) / 1e9
+            roofline_dec_idx = {"kernel": "indexer_decode_kernel", "bound": "hbm",
+                                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": stored_traffic("indexer_decode_kernel"),
+                                "algorithmic_per_launch": f"{dec_idx_bytes} B = {ctx_total} cached tokens x "
+                                                          f"{key_bytes} B of index key"}
         avg, n, tot = per_launch(kern_dec, "attention")
         if n:
-            gbs = dec_gather_bytes * args.steps / (tot * 1e-3) / 1e9
-            kernels["decode.attention"]["achieved_GBs"] = round(gbs, 1)
-            kernels["decode.attention"]["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+            gbs = dec_gather_bytes / (avg * 1e-3) / 1e9
+            roofline_dec_attn = {"kernel": "attn_latent_mfma_kernel<true> (paged decode gather)",
+                                 "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                 "traffic": stored_traffic("attn_latent_mfma_kernel<true>"),
+                                 "algorithmic_per_launch": f"{dec_gather_bytes} B = {sel_rows} selected rows x "
+                                                           f"{row_bytes} B latent row"}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -189,22 +238,55 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"prefill L={L} + decode B={B} ctx={N}", "topk": K,
+        "config": {"workload": f"prefill L={L} (prefill_128k) + paged decode B={B} at ctx={N} "
+                               f"(decode_b64_128k)", "topk": K,
                    "index_heads": s.n_idx_heads, "d_index": s.d_idx, "heads": s.n_heads,
-                   "d_qk": s.d_qk, "d_v": s.d_v, "page_size": s.page_size,
-                   "prefill_workload": "prefill_128k", "decode_workload": "decode_b64_128k"},
+                   "d_qk": s.d_qk, "d_v": s.d_v, "page_size": s.page_size},
         "prefill_tokens_per_s": round(L / (pre_ms * 1e-3), 1),
         "decode_tokens_per_s": round(B / (dec_ms * 1e-3), 1),
         "prefill_ms": round(pre_ms, 4),
         "decode_ms": round(dec_ms, 4),
         "roofline": roofline,
-        "roofline_decode": roofline_dec,
+        "roofline_decode_indexer": roofline_dec_idx,
+        "roofline_decode_gather": roofline_dec_attn,
         "kernels": kernels,
+        "peaks_measured": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
     h_pre.close()
     h_dec.close()
+
+
+def measured_peaks(torch):
+    """The chip's attainable rates on this machine: a large bf16 GEMM (hipBLASLt through torch)
+    and a 4 GiB device-to-device copy, as references beside the spec peaks."""
+    n = 8192
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_8192_tflops": round(gemm_tflops, 1), "copy_4GiB_read_plus_write_gbs": round(copy_gbs, 1)}
 
 
 def cpu_baseline(P, wl, K, seconds):
