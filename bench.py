@@ -55,10 +55,13 @@ def parse():
 
 
 def source_hash(files):
+    """sha256 over the code of `files` (line comments, trailing blanks and empty lines
+    dropped, so that an edit of comments alone keeps stored counters valid)."""
     h = hashlib.sha256()
     for f in sorted(files):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            code = [ln.split("//", 1)[0].rstrip() for ln in fh]
+        h.update(f.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()
 
 

@@ -8,15 +8,15 @@
 // cache are read (that page, section 2.3).
 //
 // attn_latent_mfma_kernel serves the latent layout (bf16, 16 heads sharing one 576-wide
-// row per token whose first 512 columns are the value).  A 512-thread workgroup walks the
-// selected rows of one query in chunks of 64, gathered into LDS with 16-byte loads (1152
-// bytes per row, read once for all 16 heads); the next chunk's gather is in flight in
-// registers while the current one is computed.  Logits and P.V run on
-// v_mfma_f32_16x16x32_bf16 with an online softmax (running max / sum per head, exp2 with the
-// log2(e) factor folded into the scale).  P enters the MFMA as a bf16 hi part plus a bf16
-// residual, so the weights keep ~16 mantissa bits.  In decode the selected rows of one
-// sequence are split across workgroups and a second kernel merges the partial (max, sum,
-// accumulator) states.
+// row per token whose first 512 columns are the value).  A 4-wave workgroup walks the
+// selected rows of one query in chunks of 32; each thread gathers with 16-byte loads the
+// pieces of K that its own logits MFMAs consume (the next chunk's pieces in flight while the
+// current one is computed), so every 1152-byte row is read once for all 16 heads and only
+// its value part passes through LDS.  Logits and P.V run on v_mfma_f32_16x16x32_bf16 with
+// an online softmax (running max / sum per head, exp2 with the log2(e) factor folded into
+// the scale).  P enters the MFMA as a bf16 hi part plus a bf16 residual, so the weights keep
+// ~16 mantissa bits.  In decode the selected rows of one sequence are split across
+// workgroups and a second kernel merges the partial (max, sum, accumulator) states.
 //
 // attn_generic_kernel serves every other shape (fp32 or bf16): one workgroup per (row,
 // head), logits in LDS, two-pass softmax.

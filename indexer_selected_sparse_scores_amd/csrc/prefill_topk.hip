@@ -10,10 +10,12 @@
 //  * Persistent workgroups of 8 waves pull tiles of 8 query rows from an atomic counter,
 //    latest rows (most keys) first.  Wave w owns query row q0 + w for the whole tile: its
 //    A operand (64 heads x 128 dims of q, 64 VGPRs) and head weights stay in registers.
-//  * Keys stream through LDS in 64-key tiles (16 KB, double-buffered, 16-byte chunks XOR-
-//    swizzled so that the MFMA fragment reads are free of bank conflicts).  Per tile each
-//    wave issues 32 v_mfma_f32_32x32x16_bf16: heads on M (2 tiles of 32), keys on N (2 tiles
-//    of 32), d_I on K.  fp32 accumulation.
+//  * Keys stream through LDS in 64-key tiles (16 KB, three buffers) stored in MFMA fragment
+//    order, so that a B fragment is one linear, conflict-free 16-byte read per lane.  Per
+//    tile each wave issues 32 v_mfma_f32_32x32x16_bf16: heads on M (2 tiles of 32), keys on
+//    N (2 tiles of 32), d_I on K, fp32 accumulation.  B fragments flow through a 4-deep
+//    register ring read 3 k-steps ahead; the third buffer lets the ring run into the next
+//    tile before the tile barrier.
 //  * Epilogue in registers: each lane holds 16 head rows of one key column per 32x32 tile;
 //    ReLU, the weight and the head sum run in-lane, one v_permlane32_swap finishes the head
 //    sum and leaves lane l with the score of key tile_base + l.
@@ -40,9 +42,14 @@ constexpr int kRows = 8;            // query rows per tile = waves per workgroup
 constexpr int kThreads = kRows * kWave;
 constexpr int kKT = 64;             // keys per LDS tile
 constexpr int kHalves = kKT / 32;   // 32-key MFMA column blocks per tile
+constexpr int kSteps = kHalves * (kD / 16);  // k-steps (B fragments) per tile (16)
+constexpr int kRing = 4;            // B fragments in flight per wave
+constexpr int kBufs = 3;            // LDS key tiles
 constexpr int kTileLoads = kKT * 16 / 512;  // 16-byte chunks each thread moves per tile
 constexpr int kChunks = kD * 2 / 16;  // 16-byte chunks per key row (16)
 constexpr int kRefresh = 8;         // key tiles between running-threshold refreshes
+static_assert(kSteps % kRing == 0, "ring slots repeat every tile");
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited on
 using topk::kBins;
 using topk::kBinShift;
 using topk::kCap;
@@ -51,7 +58,7 @@ using topk::kPerThread;
 static_assert(kRows * kBins * 4 == kCap * 8, "the histogram region holds the candidates");
 
 struct Shared {
-    uint4 keys[2][kKT * kChunks];        // double-buffered key tiles
+    uint4 keys[kBufs][kKT * kChunks];    // key tiles in fragment order
     uint32_t region[kRows * kBins];      // 64 KB: histograms, then candidate (key, index)
     topk::SelectShared<kRows> sel;
     int info[kRows][4];                  // per row: b*, count in bins > b*, count in bins >= b*,
@@ -59,19 +66,28 @@ struct Shared {
     int tile;
 };
 
-// Scheduling pattern of one 32-key half-tile: its 8 B-fragment reads, then the 16 MFMAs
-// interleaved with the 64 VALU ops of the previous half-tile's epilogue.
-template <int kId>
-__device__ __forceinline__ void interleave_half()
+// Key tile layout: the 16-byte piece holding dims 8 j .. 8 j + 7 of key r sits at
+// ((r / 32) * 8 + j / 2) * 64 + (j % 2) * 32 + r % 32, so that the B fragment of k-step i of a
+// tile (keys 32 (i / 8) + l % 32, dims 16 (i % 8) + 8 (l / 32)) is piece 64 i + l of lane l.
+__device__ __forceinline__ int piece_slot(int r, int j)
 {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, kId);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, kId);
-#pragma unroll
-    for (int i = 0; i < 14; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, kId);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, kId);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, kId);
+    return ((r >> 5) * 8 + (j >> 1)) * 64 + (j & 1) * 32 + (r & 31);
+}
+
+// Chunk c of a tile load (c = thread + 512 u): 16 consecutive lanes take 16 consecutive keys
+// at one 16-byte column, so the fragment-order LDS store of a wave is conflict-free.
+__device__ __forceinline__ int chunk_key(int c) { return (c & 15) + 16 * ((c >> 6) & 3); }
+__device__ __forceinline__ int chunk_col(int c) { return ((c >> 4) & 3) + 4 * (c >> 8); }
+
+// Scheduling pattern of one k-step: two MFMAs with 4 epilogue VALU ops after each, and the
+// ring read of a later k-step after the MFMAs that free its slot.
+__device__ __forceinline__ void step_pattern()
+{
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
@@ -116,27 +132,32 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 for (int g = 0; g < 16; ++g)
                     wv[mt][g] = w[qrow * kH + 32 * mt + 8 * (g / 4) + 4 * (lane / 32) + g % 4];
 
-            // key tile loader: thread i moves chunks i and i + 512 of the 1024 in a tile;
-            // LDS slot (r, j) holds chunk j ^ (r % 16) of key row r
+            // key tile loader: thread i moves chunks i and i + 512 of the 1024 in a tile
             const int n_kt = (int)(t_last / kKT) + 1;
             auto load_tile = [&](int kt, uint4 (&v)[kTileLoads]) {
 #pragma unroll
                 for (int u = 0; u < kTileLoads; ++u) {
                     const int c = tid + u * kThreads;
-                    const int r = c / kChunks, j = c % kChunks;
-                    int64_t s = (int64_t)kt * kKT + r;
+                    int64_t s = (int64_t)kt * kKT + chunk_key(c);
                     if (s > t_last) s = t_last;
-                    v[u] = load16(k_idx + s * kD + 8 * (j ^ (r % 16)));
+                    v[u] = load16(k_idx + s * kD + 8 * chunk_col(c));
                 }
             };
             auto store_tile = [&](int buf, const uint4 (&v)[kTileLoads]) {
 #pragma unroll
-                for (int u = 0; u < kTileLoads; ++u) sh.keys[buf][tid + u * kThreads] = v[u];
+                for (int u = 0; u < kTileLoads; ++u) {
+                    const int c = tid + u * kThreads;
+                    sh.keys[buf][piece_slot(chunk_key(c), chunk_col(c))] = v[u];
+                }
             };
             {
                 uint4 v[kTileLoads];
                 load_tile(0, v);
                 store_tile(0, v);
+                if (n_kt > 1) {
+                    load_tile(1, v);
+                    store_tile(1, v);
+                }
             }
             uint32_t *hist = sh.region + wave * kBins;
             int run_bin = 0;  // running threshold bin: scores in lower bins are dropped
@@ -171,60 +192,55 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 n_cand += __popcll(ballot);
             };
 
+            // B fragment ring: slot i % kRing holds k-step i of the tile being multiplied
+            bf16x8 ring[kRing];
+            // q and the weights have arrived: no wait on them is left inside the loop, where it
+            // would also wait for the key loads in flight
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();  // tiles 0 and 1 stored
+#pragma unroll
+            for (int i = 0; i < kRing; ++i) ring[i] = as_bf16x8(sh.keys[0][64 * i + lane]);
+
 #pragma unroll 1
             for (int kt = 0; kt < n_kt; ++kt) {
-                __syncthreads();
+                // tile kt + 1 is in LDS; the buffer of tile kt + 2 is no longer read
+                if (kt > 0) __syncthreads();
                 uint4 nxt[kTileLoads];
-                const bool more = kt + 1 < n_kt;
-                if (more) load_tile(kt + 1, nxt);
+                const bool more = kt + 2 < n_kt;
+                if (more) load_tile(kt + 2, nxt);
                 if (selects) {
-                    const uint4 *kb = sh.keys[kt & 1];
-                    float part_odd = 0.f;
+                    const int cur = kt % kBufs, nb = (kt + 1) % kBufs;
+                    const uint4 *kc = sh.keys[cur] + lane;
+                    const uint4 *kn = sh.keys[nb] + lane;
+                    float part_odd = 0.f, p = 0.f;
 #pragma unroll
-                    for (int hf = 0; hf < kHalves; ++hf) {
-                        const int st = hf & 1;  // accumulator pair of this half-tile
-                        // B fragments of half-tile hf: key 32 hf + l % 32, dims 16 ks + 8 (l / 32)
-                        bf16x8 b[kD / 16];
-#pragma unroll
-                        for (int ks = 0; ks < kD / 16; ++ks) {
-                            const int r = 32 * hf + lane % 32;
-                            const int j = (2 * ks + lane / 32) ^ (r % 16);
-                            b[ks] = as_bf16x8(kb[r * kChunks + j]);
-                        }
+                    for (int i = 0; i < kSteps; ++i) {
+                        const int hf = i / 8, ks = i % 8, st = hf;
+                        if (ks == 0) p = 0.f;
+                        const bf16x8 b = ring[i % kRing];
+                        acc[st][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][ks], b, ks == 0 ? f32x16{} : acc[st][0], 0, 0, 0);
+                        acc[st][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][ks], b, ks == 0 ? f32x16{} : acc[st][1], 0, 0, 0);
+                        // the ring slot just freed takes k-step i + kRing (of the next tile
+                        // past the end of this one; harmless stale data after the last tile)
+                        ring[i % kRing] = as_bf16x8(i + kRing < kSteps ? kc[64 * (i + kRing)] : kn[64 * (i + kRing - kSteps)]);
                         // epilogue of the previous half-tile (the other accumulator pair):
                         // register g of lane l is head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4
-                        float p = 0.f;
 #pragma unroll
-                        for (int g = 0; g < 16; ++g) {
+                        for (int g = 2 * ks; g < 2 * ks + 2; ++g) {
                             p = fmaf(wv[0][g], relu(acc[st ^ 1][0][g]), p);
                             p = fmaf(wv[1][g], relu(acc[st ^ 1][1][g]), p);
                         }
-                        acc[st][0] = f32x16{};
-                        acc[st][1] = f32x16{};
-#pragma unroll
-                        for (int ks = 0; ks < kD / 16; ++ks)
-#pragma unroll
-                            for (int mt = 0; mt < 2; ++mt)
-                                acc[st][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks],
-                                                                                      acc[st][mt], 0, 0, 0);
-                        // 8 fragment reads, then one MFMA per 4 VALU of the epilogue
-                        if (hf == 0) interleave_half<0>();
-                        else if (hf == 1) interleave_half<1>();
-                        else if (hf == 2) interleave_half<2>();
-                        else interleave_half<3>();
-                        if (st == 0) {
-                            part_odd = p;  // odd half-tile before this one
-                        } else {
-                            // window: odd half-tile hf - 2 and even half-tile hf - 1
-                            finish_window(part_odd, p, (int64_t)kt * kKT + 32 * (hf - 2) + lane);
-                        }
+                        if (ks == 7 && hf == 0) part_odd = p;  // odd half-tile of tile kt - 1
+                        step_pattern();
                     }
+                    // window: odd half-tile of tile kt - 1 and even half-tile of tile kt
+                    finish_window(part_odd, p, (int64_t)kt * kKT - 32 + lane);
                     if ((kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
                         const int b = topk::threshold_bin(hist, m, nullptr, nullptr);
                         if (b > run_bin) run_bin = b;
                     }
                 }
-                if (more) store_tile((kt + 1) & 1, nxt);
+                if (more) store_tile((kt + 2) % kBufs, nxt);
             }
             if (selects) {  // the odd half of the last tile
                 float p = 0.f;
