@@ -224,6 +224,14 @@ def main():
                                  "algorithmic_per_launch": f"{dec_gather_bytes} B = {sel_rows} selected rows x "
                                                            f"{row_bytes} B latent row"}
 
+    # the same achieved rates against the peaks measured on this machine (bf16 GEMM, 4 GiB copy)
+    if peaks:
+        for rf, key in ((roofline, "bf16_gemm_8192_tflops"), (roofline_dec_idx, "copy_4GiB_read_plus_write_gbs"),
+                        (roofline_dec_attn, "copy_4GiB_read_plus_write_gbs")):
+            if rf and peaks.get(key):
+                rf["frac_of_measured"] = round(rf["achieved"] / peaks[key], 4)
+                rf["measured_peak"] = key
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(P, pre_wl, K, args.cpu_seconds)

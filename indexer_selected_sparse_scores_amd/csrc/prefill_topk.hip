@@ -208,11 +208,11 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 uint4 nxt[kTileLoads];
                 const bool more = kt + 2 < n_kt;
                 if (more) load_tile(kt + 2, nxt);
+                float part_odd = 0.f, p = 0.f;
                 if (selects) {
                     const int cur = kt % kBufs, nb = (kt + 1) % kBufs;
                     const uint4 *kc = sh.keys[cur] + lane;
                     const uint4 *kn = sh.keys[nb] + lane;
-                    float part_odd = 0.f, p = 0.f;
 #pragma unroll
                     for (int i = 0; i < kSteps; ++i) {
                         const int hf = i / 8, ks = i % 8, st = hf;
@@ -233,6 +233,11 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                         if (ks == 7 && hf == 0) part_odd = p;  // odd half-tile of tile kt - 1
                         step_pattern();
                     }
+                }
+                // the next key tile goes to LDS before any candidate store is issued: its wait
+                // for the key loads must not also wait for a store
+                if (more) store_tile((kt + 2) % kBufs, nxt);
+                if (selects) {
                     // window: odd half-tile of tile kt - 1 and even half-tile of tile kt
                     finish_window(part_odd, p, (int64_t)kt * kKT - 32 + lane);
                     if ((kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
@@ -240,7 +245,6 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                         if (b > run_bin) run_bin = b;
                     }
                 }
-                if (more) store_tile((kt + 2) % kBufs, nxt);
             }
             if (selects) {  // the odd half of the last tile
                 float p = 0.f;
