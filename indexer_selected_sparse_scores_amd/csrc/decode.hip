@@ -12,7 +12,8 @@
 // Fast path (bf16, H_I = 64, d_I = 128, 64-token pages), three kernels:
 //  * indexer_decode_kernel: grid (1024-key blocks, sequences).  Each wave streams 4 pages of
 //    index keys straight into v_mfma_f32_32x32x16_bf16 B fragments (next half-page in flight
-//    while the current one is multiplied; q and the head weights stay in registers), applies
+//    while the current one is multiplied; q fragments and head weights are read from LDS, which
+//    leaves room for four waves per SIMD and so more key bytes in flight), applies
 //    ReLU / weights / head sum in registers, writes the fp32 scores and counts them in a
 //    2048-bin LDS histogram that is added to the sequence's histogram in global memory.  The
 //    scan over index keys is the HBM-bound part of decode (256 bytes per cached token).
@@ -60,13 +61,21 @@ __global__ void decode_reset_kernel(uint32_t *hist, int32_t *cand_count, int64_t
     if (i < B) cand_count[i] = 0;
 }
 
-__global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
+// q (as MFMA A fragments) and the head weights of the workgroup's sequence live in LDS, so a wave holds
+// only its key fragments and accumulators and four waves fit on a SIMD: more key bytes in flight.
+struct DecodeIdxShared {
+    uint4 qf[2 * (kD / 16) * kWave];  // fragment (mt, ks) of lane l at (8 mt + ks) * 64 + l: 16 KB
+    float4 wq[kH / 4];                // the 64 head weights
+    uint32_t hist[kBins];
+};
+
+__global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ kidx_pages,
     int64_t n_pages, const int32_t *__restrict__ block_table, int32_t max_blocks,
     const int32_t *__restrict__ ctx_len, int32_t max_ctx, float *__restrict__ scores, int64_t ld,
     uint32_t *__restrict__ hist_g, uint32_t *err)
 {
-    __shared__ uint32_t hist[kBins];
+    __shared__ DecodeIdxShared sh;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int64_t b = blockIdx.y;
     const int64_t n = ctx_len[b];
@@ -76,23 +85,6 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
     }
     const int64_t key0 = (int64_t)blockIdx.x * kKeysPerBlock;
     if (key0 >= n) return;
-    for (int i = tid; i < kBins; i += kIdxThreads) hist[i] = 0;
-    __syncthreads();
-
-    // A operand (64 heads x 128 dims of q) and the head weights in the accumulator layout
-    bf16x8 a[2][kD / 16];
-    float wv[2][16];
-    const uint16_t *qr = q_idx + b * (int64_t)kH * kD;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks)
-            a[mt][ks] = as_bf16x8(load16(qr + (32 * mt + lane % 32) * kD + 16 * ks + 8 * (lane / 32)));
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int g = 0; g < 16; ++g)
-            wv[mt][g] = w[b * kH + 32 * mt + 8 * (g / 4) + 4 * (lane / 32) + g % 4];
 
     // this wave's pages: logical pages lp0 .. lp0 + 3
     const int64_t lp0 = key0 / kPage + (int64_t)kPagesPerWave * wave;
@@ -115,7 +107,20 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
         for (int ks = 0; ks < kD / 16; ++ks) bf[ks] = as_bf16x8(load16(src + 16 * ks));
     };
     bf16x8 bc[kD / 16], bn[kD / 16];
-    load_half(0, bc);
+    load_half(0, bc);  // the first keys are in flight while q goes to LDS
+
+    // q fragments: thread i moves fragments i, i + 256, i + 512, i + 768 (fragment f = (8 mt + ks) * 64 + l
+    // holds q row 32 mt + l % 32, dims 16 ks + 8 (l / 32))
+    const uint16_t *qr = q_idx + b * (int64_t)kH * kD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int f = tid + u * kIdxThreads, l = f % kWave, mk = f / kWave;
+        sh.qf[f] = load16(qr + (32 * (mk / 8) + l % 32) * kD + 16 * (mk % 8) + 8 * (l / 32));
+    }
+    if (tid < kH / 4) sh.wq[tid] = *reinterpret_cast<const float4 *>(w + b * kH + 4 * tid);
+    for (int i = tid; i < kBins; i += kIdxThreads) sh.hist[i] = 0;
+    __syncthreads();
+
 #pragma unroll
     for (int h = 0; h < 2 * kPagesPerWave; ++h) {
         const int64_t kbase = (lp0 + h / 2) * kPage + 32 * (h % 2);
@@ -124,15 +129,25 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
             f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
             for (int ks = 0; ks < kD / 16; ++ks) {
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][ks], bc[ks], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][ks], bc[ks], acc1, 0, 0, 0);
+                const bf16x8 a0 = as_bf16x8(sh.qf[ks * kWave + lane]);
+                const bf16x8 a1 = as_bf16x8(sh.qf[(8 + ks) * kWave + lane]);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bc[ks], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bc[ks], acc1, 0, 0, 0);
             }
             // register g of lane l: head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4, key l % 32
             float part = 0.f;
 #pragma unroll
-            for (int g = 0; g < 16; ++g) {
-                part = fmaf(wv[0][g], relu(acc0[g]), part);
-                part = fmaf(wv[1][g], relu(acc1[g]), part);
+            for (int gq = 0; gq < 4; ++gq) {
+                const float4 w0 = sh.wq[8 * gq / 4 + lane / 32];
+                const float4 w1 = sh.wq[(32 + 8 * gq) / 4 + lane / 32];
+                part = fmaf(w0.x, relu(acc0[4 * gq]), part);
+                part = fmaf(w0.y, relu(acc0[4 * gq + 1]), part);
+                part = fmaf(w0.z, relu(acc0[4 * gq + 2]), part);
+                part = fmaf(w0.w, relu(acc0[4 * gq + 3]), part);
+                part = fmaf(w1.x, relu(acc1[4 * gq]), part);
+                part = fmaf(w1.y, relu(acc1[4 * gq + 1]), part);
+                part = fmaf(w1.z, relu(acc1[4 * gq + 2]), part);
+                part = fmaf(w1.w, relu(acc1[4 * gq + 3]), part);
             }
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
                                                              false, false);
@@ -141,7 +156,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
             const int64_t s = kbase + lane;
             if (lane < 32 && s < n) {
                 scores[b * ld + s] = score;
-                atomicAdd(&hist[order_key(score) >> kBinShift], 1u);
+                atomicAdd(&sh.hist[order_key(score) >> kBinShift], 1u);
             }
         }
 #pragma unroll
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_decode_kernel(
     }
     __syncthreads();
     for (int i = tid; i < kBins; i += kIdxThreads) {
-        const uint32_t c = hist[i];
+        const uint32_t c = sh.hist[i];
         if (c) atomicAdd(&hist_g[b * kBins + i], c);
     }
 }
