@@ -47,7 +47,7 @@ constexpr int kRing = 4;            // B fragments in flight per wave
 constexpr int kBufs = 3;            // LDS key tiles
 constexpr int kTileLoads = kKT * 16 / 512;  // 16-byte chunks each thread moves per tile
 constexpr int kChunks = kD * 2 / 16;  // 16-byte chunks per key row (16)
-constexpr int kRefresh = 8;         // key tiles between running-threshold refreshes
+constexpr int kRefresh = 16;        // key tiles between running-threshold refreshes
 static_assert(kSteps % kRing == 0, "ring slots repeat every tile");
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited on
 using topk::kBins;
@@ -175,11 +175,14 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
 
             // all keys of a window go through the histogram; the ones at or above the running
             // threshold bin are appended to the row's candidate list in key order
-            auto finish_window = [&](float part_odd, float part_even, int64_t s) {
+            // the window's keys are s = sb - 32 (sb >= 0; 32-bit is enough: row < 2^31)
+            const uint32_t vis_hi = (uint32_t)row + 32u;
+            auto finish_window = [&](float part_odd, float part_even, uint32_t sb) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part_odd),
                                                                  __float_as_uint(part_even), false, false);
                 const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                const bool vis = s >= 0 && s <= row;
+                const bool vis = sb >= 32u && sb <= vis_hi;
+                const uint32_t s = sb - 32u;
                 const uint32_t key = order_key(score);
                 atomicAdd(&hist[key >> kBinShift], vis ? 1u : 0u);
                 const bool keep = vis && (int)(key >> kBinShift) >= run_bin;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 if (keep) {
                     const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
-                    my_cands[n_cand + rank] = make_uint2(key, (uint32_t)s);
+                    my_cands[n_cand + rank] = make_uint2(key, s);
                 }
                 n_cand += __popcll(ballot);
             };
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 if (more) store_tile((kt + 2) % kBufs, nxt);
                 if (selects) {
                     // window: odd half-tile of tile kt - 1 and even half-tile of tile kt
-                    finish_window(part_odd, p, (int64_t)kt * kKT - 32 + lane);
+                    finish_window(part_odd, p, (uint32_t)kt * kKT + lane);
                     if ((kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
                         const int b = topk::threshold_bin(hist, m, nullptr, nullptr);
                         if (b > run_bin) run_bin = b;
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                     p = fmaf(wv[0][g], relu(acc[1][0][g]), p);
                     p = fmaf(wv[1][g], relu(acc[1][1][g]), p);
                 }
-                finish_window(p, 0.f, (int64_t)n_kt * kKT - 32 + lane);
+                finish_window(p, 0.f, (uint32_t)n_kt * kKT + lane);
             }
         }
         // final threshold per row (each wave its own row), then free the histograms

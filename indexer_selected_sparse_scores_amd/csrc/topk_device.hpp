@@ -53,54 +53,53 @@ __device__ __forceinline__ int block_scan(int v, int *wave_sums, int *total)
     return x - v + before;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane 0 first) on DPP: row shifts by 1, 2, 4
+// and 8 within each 16-lane row (lanes shifted in from outside the row read 0), then the last
+// lane of row 0 added into row 1 (and of row 2 into row 3), then lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // One wave: the highest bin b of a 2048-bin histogram (LDS or global memory) such that the
-// bins >= b hold at least m entries.  Returns -1 if the whole histogram holds fewer than m.
+// bins >= b hold at least m >= 1 entries.  Returns -1 if the whole histogram holds fewer than m.
 // *above = entries in bins > b, *upto = entries in bins >= b (either may be NULL).  Every
 // lane returns the same values.
 __device__ __forceinline__ int threshold_bin(const uint32_t *hist, int m, int *above, int *upto)
 {
     const int lane = lane_id();
-    // lane l covers bins [kBins - 32 (l + 1), kBins - 32 l): lane 0 holds the top bins
+    // lane l sums bins [kBins - 32 (l + 1), kBins - 32 l): lane 0 holds the top bins
     const uint32_t *hb = hist + kBins - 32 * (lane + 1);
-    uint32_t c[32];
+    int sum = 0;
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
         const uint4 v = *reinterpret_cast<const uint4 *>(hb + i);
-        c[i] = v.x;
-        c[i + 1] = v.y;
-        c[i + 2] = v.z;
-        c[i + 3] = v.w;
+        sum += (int)(v.x + v.y + v.z + v.w);
     }
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sum += (int)c[i];
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
+    const int incl = wave_incl_scan(sum);
     const uint64_t hit = __ballot(incl >= m);
     if (hit == 0) {
         if (above) *above = 0;
-        if (upto) *upto = __shfl(incl, kWave - 1);
+        if (upto) *upto = __builtin_amdgcn_readlane(incl, kWave - 1);
         return -1;
     }
+    // lane src's range holds the answer; its 32 bins, top first, go one per lane to lanes 0..31
     const int src = __builtin_ctzll(hit);
-    // every lane walks its own bins from the top (only lane src's answer is used)
-    int cum = incl - sum, bin = -1, ab = 0, up = 0;
-#pragma unroll
-    for (int i = 31; i >= 0; --i) {
-        const int ci = (int)c[i];
-        const bool here = bin < 0 && cum + ci >= m;
-        bin = here ? kBins - 32 * (lane + 1) + i : bin;
-        ab = here ? cum : ab;
-        up = here ? cum + ci : up;
-        cum += ci;
-    }
-    if (above) *above = __shfl(ab, src);
-    if (upto) *upto = __shfl(up, src);
-    return __shfl(bin, src);
+    const int base = __builtin_amdgcn_readlane(incl - sum, src);  // entries above that range
+    const int top = kBins - 32 * src - 1;
+    const int c = lane < 32 ? (int)hist[top - (lane & 31)] : 0;
+    const int cum = base + wave_incl_scan(c);
+    const int j = __builtin_ctzll(__ballot(lane < 32 && cum >= m));
+    const int up = __builtin_amdgcn_readlane(cum, j);
+    if (above) *above = up - __builtin_amdgcn_readlane(c, j);
+    if (upto) *upto = up;
+    return top - j;
 }
 
 // Candidate sources for select_and_emit: element j has key k(j) and token index i(j); the
