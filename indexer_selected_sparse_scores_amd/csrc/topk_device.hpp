@@ -28,31 +28,6 @@ struct SelectShared {
     int need;
 };
 
-// Exclusive prefix sum over the kWaves * 64 threads (thread order); *total gets the sum.
-template <int kWaves>
-__device__ __forceinline__ int block_scan(int v, int *wave_sums, int *total)
-{
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == kWave - 1) wave_sums[wave] = x;
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        const int s = wave_sums[i];
-        before += i < wave ? s : 0;
-        all += s;
-    }
-    __syncthreads();
-    *total = all;
-    return x - v + before;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave (lane 0 first) on DPP: row shifts by 1, 2, 4
 // and 8 within each 16-lane row (lanes shifted in from outside the row read 0), then the last
 // lane of row 0 added into row 1 (and of row 2 into row 3), then lane 31 into rows 2 and 3.
@@ -65,6 +40,26 @@ __device__ __forceinline__ int wave_incl_scan(int x)
     x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
     x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
     return x;
+}
+
+// Exclusive prefix sum over the kWaves * 64 threads (thread order); *total gets the sum.
+template <int kWaves>
+__device__ __forceinline__ int block_scan(int v, int *wave_sums, int *total)
+{
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int x = wave_incl_scan(v);
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int s = wave_sums[i];
+        before += i < wave ? s : 0;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return x - v + before;
 }
 
 // One wave: the highest bin b of a 2048-bin histogram (LDS or global memory) such that the
@@ -146,12 +141,7 @@ __device__ __noinline__ void select_and_emit(SelectShared<kWaves> &sh, const Src
             // lane l looks at digits 127 - 2l and 126 - 2l (descending)
             const int c_hi = (int)sh.radix[127 - 2 * tid], c_lo = (int)sh.radix[126 - 2 * tid];
             const int c = c_hi + c_lo;
-            int incl = c;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (tid >= off) incl += y;
-            }
+            const int incl = wave_incl_scan(c);
             const int excl = incl - c;
             if (excl < need && need <= incl) {
                 if (need <= excl + c_hi) {
