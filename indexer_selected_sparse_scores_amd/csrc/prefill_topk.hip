@@ -28,6 +28,8 @@
 //    candidates in bins >= b* are gathered into LDS (at most kCap; otherwise the list is
 //    scanned in global memory), an MSD radix select over the remaining 21 key bits finds the
 //    exact m-th key, and an ordered compaction writes the selection in ascending key order.
+#include <type_traits>
+
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 #include "topk_device.hpp"
@@ -204,20 +206,24 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
 #pragma unroll
             for (int i = 0; i < kRing; ++i) ring[i] = as_bf16x8(sh.keys[0][64 * i + lane]);
 
+            // One barrier per tile, between its two halves: by then every wave has finished tile
+            // kt - 1 (so the buffer of tile kt + 2 is free) and stored tile kt + 1 (which the ring
+            // starts reading at k-step 12).  A wave that finishes its half-tiles early does its
+            // tile store and window finish while the other wave of its SIMD still multiplies.
 #pragma unroll 1
             for (int kt = 0; kt < n_kt; ++kt) {
-                // tile kt + 1 is in LDS; the buffer of tile kt + 2 is no longer read
-                if (kt > 0) __syncthreads();
                 uint4 nxt[kTileLoads];
                 const bool more = kt + 2 < n_kt;
                 if (more) load_tile(kt + 2, nxt);
                 float part_odd = 0.f, p = 0.f;
-                if (selects) {
-                    const int cur = kt % kBufs, nb = (kt + 1) % kBufs;
-                    const uint4 *kc = sh.keys[cur] + lane;
-                    const uint4 *kn = sh.keys[nb] + lane;
+                const int cur = kt % kBufs, nb = (kt + 1) % kBufs;
+                const uint4 *kc = sh.keys[cur] + lane;
+                const uint4 *kn = sh.keys[nb] + lane;
+                // k-steps [i0, i1) of this tile
+                auto steps = [&](auto i0c, auto i1c) {
+                    constexpr int i0 = decltype(i0c)::value, i1 = decltype(i1c)::value;
 #pragma unroll
-                    for (int i = 0; i < kSteps; ++i) {
+                    for (int i = i0; i < i1; ++i) {
                         const int hf = i / 8, ks = i % 8, st = hf;
                         if (ks == 0) p = 0.f;
                         const bf16x8 b = ring[i % kRing];
@@ -236,7 +242,10 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                         if (ks == 7 && hf == 0) part_odd = p;  // odd half-tile of tile kt - 1
                         step_pattern();
                     }
-                }
+                };
+                if (selects) steps(std::integral_constant<int, 0>{}, std::integral_constant<int, kSteps / 2>{});
+                __syncthreads();  // every wave, selecting or not, passes it once per tile
+                if (selects) steps(std::integral_constant<int, kSteps / 2>{}, std::integral_constant<int, kSteps>{});
                 // the next key tile goes to LDS before any candidate store is issued: its wait
                 // for the key loads must not also wait for a store
                 if (more) store_tile((kt + 2) % kBufs, nxt);
