@@ -180,7 +180,9 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
 
     // offsets of chunks 0 and 1; the index of chunk 2 waits in a register
     int64_t pend_j = j_begin + 2 * kChunk + tid;  // slot whose index `pend_s` holds
-    int64_t pend_s = -1;
+    // 32-bit as loaded: widened only where it is used, a chunk later (widening it at the load
+    // would make the wave wait for the load right there)
+    int32_t pend_s = -1;
     if (tid < kChunk) {
         sh.row_off[0][tid] = slot_offset(kv, idx_row, r, j_begin + tid, j_end, visible, err);
         sh.row_off[1][tid] = slot_offset(kv, idx_row, r, j_begin + kChunk + tid, j_end, visible, err);
@@ -212,6 +214,8 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     };
     gather(0);
     stash();
+#pragma unroll
+    for (int i = 0; i < kKHalf; ++i) asm volatile("" : : "v"(g[i].x));  // complete before the loop
 
     const float neg_inf = -__builtin_inff();
     // softmax state of head 4 wave + lane / 16 (log2 domain), owned by this wave
@@ -233,13 +237,14 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
         int32_t page = 0;
         bool page_pending = false;
         if (tid < kChunk && pend_j < j_end) {
-            if (pend_s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
-            if (pend_s >= 0 && pend_s < visible) {
+            const int64_t ps = pend_s;
+            if (ps >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
+            if (ps >= 0 && ps < visible) {
                 if (kv.block_table) {
-                    page = kv.block_table[r * kv.max_blocks + pend_s / kv.page_size];
+                    page = kv.block_table[r * kv.max_blocks + ps / kv.page_size];
                     page_pending = true;
                 } else {
-                    off_next = pend_s * kv.row_elems;
+                    off_next = ps * kv.row_elems;
                 }
             }
         }
@@ -328,7 +333,10 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
             }
         }
         // row_off[c & 1] was last read by this chunk's logits (before the barriers above); it
-        // now takes chunk c + 2, which the next iteration's gather reads after the barrier below
+        // now takes chunk c + 2, which the next iteration's gather reads after the barrier below.
+        // The page lookup is consumed here on every path, so no wait for it is left pending
+        // into the next chunk (where `page` is reset).
+        asm volatile("" : : "v"(page));
         if (page_pending) {
             if (page >= 0 && page < kv.n_pages) {
                 off_next = ((int64_t)page * kv.page_size + s_next % kv.page_size) * kv.row_elems;
@@ -338,7 +346,13 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
         }
         if (tid < kChunk) sh.row_off[c & 1][tid] = off_next;
         __syncthreads();  // every wave is done with vrows, logits and P; row_off is published
-        if (more) stash();
+        // unconditional (after the last chunk it stores values nothing reads), and every piece is
+        // consumed here, so that the gathered pieces are complete at the top of the loop on every
+        // path: the logits MFMAs then wait for nothing, not even for the index and page loads
+        // issued before them
+        stash();
+#pragma unroll
+        for (int i = 0; i < kKHalf; ++i) asm volatile("" : : "v"(g[i].x));
     }
 
     if (!kSplit) {
