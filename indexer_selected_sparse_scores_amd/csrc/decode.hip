@@ -14,9 +14,10 @@
 //    index keys straight into v_mfma_f32_32x32x16_bf16 B fragments (next half-page in flight
 //    while the current one is multiplied; q fragments and head weights are read from LDS, which
 //    leaves room for four waves per SIMD and so more key bytes in flight), applies
-//    ReLU / weights / head sum in registers, writes the fp32 scores and counts them in a
-//    2048-bin LDS histogram that is added to the sequence's histogram in global memory.  The
-//    scan over index keys is the HBM-bound part of decode (256 bytes per cached token).
+//    ReLU / weights / head sum in registers, counts the fp32 scores in a 2048-bin LDS histogram
+//    that is added to the sequence's histogram in global memory, and gathers each wave's 256
+//    scores in LDS for one store at its end.  The scan over index keys is the HBM-bound part
+//    of decode (256 bytes per cached token).
 //  * decode_collect_kernel: grid (8192-score chunks, sequences).  From the histogram, the bin
 //    b* holding the k_b-th largest score; every score in bins >= b* is appended, in token
 //    order, to a segment of the sequence's candidate list (segments in chunk order).
@@ -67,6 +68,7 @@ struct DecodeIdxShared {
     uint4 qf[2 * (kD / 16) * kWave];  // fragment (mt, ks) of lane l at (8 mt + ks) * 64 + l: 16 KB
     float4 wq[kH / 4];                // the 64 head weights
     uint32_t hist[kBins];
+    float4 sc[kIdxThreads / kWave][kPagesPerWave * kPage / 4];  // each wave's 256 scores, stored at the end
 };
 
 __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
@@ -155,12 +157,27 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
             if (!page_ok[h / 2]) score = -__builtin_inff();
             const int64_t s = kbase + lane;
             if (lane < 32 && s < n) {
-                scores[b * ld + s] = score;
+                reinterpret_cast<float *>(sh.sc[wave])[32 * h + lane] = score;
                 atomicAdd(&sh.hist[order_key(score) >> kBinShift], 1u);
             }
         }
 #pragma unroll
         for (int ks = 0; ks < kD / 16; ++ks) bc[ks] = bn[ks];
+    }
+    // The scores leave in one 1 KB store per wave, after the loop: a store issued between the halves
+    // would be waited for before the next half's MFMAs (loads and stores share one counter).  The store
+    // is non-temporal: the scores are read once, by the next kernel.
+    {
+        const float4 v = sh.sc[wave][lane];  // the wave's own LDS rows: no barrier needed
+        const int64_t s0 = lp0 * kPage + 4 * lane;
+        float *dst = scores + b * ld + s0;
+        if (s0 + 3 < n) {
+            __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(dst));
+        } else {
+            if (s0 < n) dst[0] = v.x;
+            if (s0 + 1 < n) dst[1] = v.y;
+            if (s0 + 2 < n) dst[2] = v.z;
+        }
     }
     __syncthreads();
     for (int i = tid; i < kBins; i += kIdxThreads) {
