@@ -9,7 +9,7 @@
 // Breakthroughs in LLM Post-Training", section 2.2); selection keeps the largest scores,
 // ties to the lower token index (section 2.3).
 //
-// Fast path (bf16, H_I = 64, d_I = 128, 64-token pages), three kernels:
+// Fast path (bf16, H_I = 64, d_I = 128, 64-token pages), two kernels after a histogram reset:
 //  * indexer_decode_kernel: grid (1024-key blocks, sequences).  Each wave streams 4 pages of
 //    index keys straight into v_mfma_f32_32x32x16_bf16 B fragments (next half-page in flight
 //    while the current one is multiplied; q fragments and head weights are read from LDS, which
@@ -18,12 +18,12 @@
 //    that is added to the sequence's histogram in global memory, and gathers each wave's 256
 //    scores in LDS for one store at its end.  The scan over index keys is the HBM-bound part
 //    of decode (256 bytes per cached token).
-//  * decode_collect_kernel: grid (8192-score chunks, sequences).  From the histogram, the bin
+//  * decode_topk_kernel: one 1024-thread workgroup per sequence.  From the histogram, the bin
 //    b* holding the k_b-th largest score; every score in bins >= b* is appended, in token
-//    order, to a segment of the sequence's candidate list (segments in chunk order).
-//  * decode_select_kernel: one workgroup per sequence joins the segments in LDS, finds the
-//    exact k_b-th key with an MSD radix select and writes the selection in ascending order;
-//    a sequence whose candidates exceed the LDS buffer is selected from its full score row.
+//    order, to a candidate list in LDS (the scores stream in coalesced rounds); the exact
+//    k_b-th key then comes from an MSD radix select and the selection is written in ascending
+//    order.  A sequence whose candidates exceed the LDS list is selected from its full score
+//    row.
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 #include "topk_device.hpp"
@@ -38,9 +38,11 @@ constexpr int kPage = 64;              // tokens per page
 constexpr int kIdxThreads = 256;       // indexer workgroup (4 waves)
 constexpr int kPagesPerWave = 4;
 constexpr int kKeysPerBlock = kPage * kPagesPerWave * (kIdxThreads / kWave);  // 1024
-constexpr int kCollectThreads = 256;
-constexpr int kChunkScores = 8192;     // scores per collect workgroup
-constexpr int kSelectWaves = 8;
+constexpr int kTopkWaves = 16;                      // selection workgroup: one per sequence
+constexpr int kTopkThreads = kTopkWaves * kWave;
+constexpr int kSubRounds = 4;                       // float4 loads per thread per round
+constexpr int kRoundScores = kSubRounds * 4 * kTopkThreads;  // 16384 scores per round
+static_assert(kSubRounds * kTopkWaves == kWave, "one (sub-round, wave) count per lane");
 using topk::kBins;
 using topk::kBinShift;
 using topk::kCap;
@@ -55,11 +57,10 @@ __device__ __forceinline__ bool decode_row_ok(const int32_t *ctx_len, const int3
     return true;
 }
 
-__global__ void decode_reset_kernel(uint32_t *hist, int32_t *cand_count, int64_t B)
+__global__ void decode_reset_kernel(uint32_t *hist, int64_t B)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < B * kBins) hist[i] = 0;
-    if (i < B) cand_count[i] = 0;
 }
 
 // q (as MFMA A fragments) and the head weights of the workgroup's sequence live in LDS, so a wave holds
@@ -186,93 +187,56 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
     }
 }
 
-// Candidates of one chunk of a sequence's scores: those in bins >= b*, in token order.
-__global__ __launch_bounds__(kCollectThreads) void decode_collect_kernel(
+// One workgroup per sequence: the threshold bin b* from the sequence's histogram, then every score
+// in bins >= b* appended to an LDS list in token order, then the exact selection of the m largest.
+// The scores stream in rounds of 16384 (4 coalesced float4 loads per thread, two more rounds in
+// flight while one is compacted); one barrier per round orders the candidates:
+// sub-round u of a round covers 4096 consecutive tokens in thread order, and the per-(sub-round,
+// wave) counts published in LDS give each wave its offset.  A sequence whose candidates exceed the
+// LDS list is selected from its full score row.
+__global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ctx_len, int32_t max_ctx,
     const int32_t *__restrict__ topk_b, int32_t max_topk, const uint32_t *__restrict__ hist_g,
-    uint2 *__restrict__ cands, int32_t *__restrict__ cand_count, int2 *__restrict__ seg, int n_chunks)
+    int32_t *__restrict__ idx, uint32_t *err)
 {
-    constexpr int kWaves = kCollectThreads / kWave;
-    constexpr int kPer = kChunkScores / kCollectThreads;  // 32 consecutive scores per thread
-    __shared__ int wave_sums[kWaves];
-    __shared__ int sh_bin, sh_base;
-    const int tid = threadIdx.x;
-    const int64_t b = blockIdx.y;
-    const int c = blockIdx.x;
-    int64_t n, m;
-    if (!decode_row_ok(ctx_len, topk_b, max_ctx, max_topk, b, &n, &m)) return;
-    if (m == n) return;  // every visible token is selected
-    const int64_t lo = (int64_t)c * kChunkScores;
-    if (lo >= n) return;
-    if (tid < kWave) {
-        const int bin = topk::threshold_bin(hist_g + b * kBins, (int)m, nullptr, nullptr);
-        if (tid == 0) sh_bin = bin;
-    }
-    __syncthreads();
-    const uint32_t key_lo = (uint32_t)sh_bin << kBinShift;
-
-    // this thread's 32 consecutive scores: positions lo + 32 tid ..
-    const int64_t s0 = lo + (int64_t)kPer * tid;
-    uint32_t keys[kPer];
-    uint32_t sel = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; i += 4) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (s0 + i + 3 < n) {
-            v = *reinterpret_cast<const float4 *>(scores + b * ld + s0 + i);
-        } else {
-            if (s0 + i < n) v.x = scores[b * ld + s0 + i];
-            if (s0 + i + 1 < n) v.y = scores[b * ld + s0 + i + 1];
-            if (s0 + i + 2 < n) v.z = scores[b * ld + s0 + i + 2];
-        }
-        keys[i] = order_key(v.x);
-        keys[i + 1] = order_key(v.y);
-        keys[i + 2] = order_key(v.z);
-        keys[i + 3] = order_key(v.w);
-    }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) sel |= (s0 + i < n && keys[i] >= key_lo ? 1u : 0u) << i;
-    int total;
-    int pos = topk::block_scan<kWaves>(__popc(sel), wave_sums, &total);
-    if (tid == 0) {
-        sh_base = atomicAdd(&cand_count[b], total);
-        seg[b * n_chunks + c] = make_int2(sh_base, total);
-    }
-    __syncthreads();
-    uint2 *dst = cands + b * kCap;
-    pos += sh_base;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if ((sel >> i) & 1u) {
-            if (pos < kCap) dst[pos] = make_uint2(keys[i], (uint32_t)(s0 + i));
-            ++pos;
-        }
-}
-
-__global__ __launch_bounds__(kSelectWaves *kWave) void decode_select_kernel(
-    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ctx_len, int32_t max_ctx,
-    const int32_t *__restrict__ topk_b, int32_t max_topk, const uint32_t *__restrict__ hist_g,
-    const uint2 *__restrict__ cands, const int32_t *__restrict__ cand_count, const int2 *__restrict__ seg,
-    int n_chunks, int32_t *__restrict__ idx, uint32_t *err)
-{
-    constexpr int kThreads = kSelectWaves * kWave;
     __shared__ uint32_t ck[kCap];
     __shared__ int32_t ci[kCap];
-    __shared__ topk::SelectShared<kSelectWaves> sh;
+    __shared__ topk::SelectShared<kTopkWaves> sh;
+    __shared__ int counts[2][kSubRounds][kTopkWaves];
     __shared__ int info[3];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int64_t b = blockIdx.x;
     int32_t *dst = idx + b * max_topk;
     int64_t n, m;
     if (!decode_row_ok(ctx_len, topk_b, max_ctx, max_topk, b, &n, &m)) {
         if (tid == 0) flag_error(err, SA_DEVERR_TOPK);
-        for (int i = tid; i < max_topk; i += kThreads) dst[i] = -1;
+        for (int i = tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
         return;
     }
-    if (m == n) {
-        for (int i = tid; i < max_topk; i += kThreads) dst[i] = i < n ? i : -1;
+    if (m == n) {  // every visible token is selected
+        for (int i = tid; i < max_topk; i += kTopkThreads) dst[i] = i < n ? i : -1;
         return;
     }
+    const float *row = scores + b * ld;
+
+    // Sub-round u of the round at `base`: thread t holds tokens base + 4096 u + 4 t .. +3.  Three
+    // rounds are in flight in three register buffers (the round loop is unrolled by three, so no
+    // buffer is copied).  Every load is issued, also past the row's end (it then reads the row's
+    // first 16 bytes, never used): a fixed number of loads in flight lets each round wait for its own.
+    const int32_t n32 = (int32_t)n;  // n <= max_ctx < 2^31
+    float4 v0[kSubRounds], v1[kSubRounds], v2[kSubRounds];
+    auto load_round = [&](float4 (&v)[kSubRounds], int32_t base) {
+        int t = tid;  // recomputed per call rather than held in registers
+        asm volatile("" : "+v"(t));
+#pragma unroll
+        for (int u = 0; u < kSubRounds; ++u) {
+            const int32_t p = base + u * 4 * kTopkThreads + 4 * t;
+            v[u] = *reinterpret_cast<const float4 *>(row + (p < n32 ? p : 0));
+        }
+    };
+    load_round(v0, 0);  // in flight while wave 0 finds the threshold bin
+    load_round(v1, kRoundScores);
+    load_round(v2, 2 * kRoundScores);
     if (tid < kWave) {
         int above, upto;
         const int bin = topk::threshold_bin(hist_g + b * kBins, (int)m, &above, &upto);
@@ -284,25 +248,94 @@ __global__ __launch_bounds__(kSelectWaves *kWave) void decode_select_kernel(
     }
     __syncthreads();
     const int bin = info[0], above = info[1], upto = info[2];
-    if (upto <= kCap && cand_count[b] <= kCap) {
-        // join the chunk segments in chunk order (each is in token order)
-        const int used = (int)((n + kChunkScores - 1) / kChunkScores);
-        int at = 0;
-        for (int c = 0; c < used; ++c) {
-            const int2 sg = seg[b * n_chunks + c];
-            for (int j = tid; j < sg.y; j += kThreads) {
-                const uint2 v = cands[b * kCap + sg.x + j];
-                ck[at + j] = v.x;
-                ci[at + j] = (int32_t)v.y;
+    if (upto > kCap) {
+        topk::select_and_emit(sh, topk::GlobalScores{row}, (int)n, bin, above, (int)m, dst);
+        for (int i = (int)m + tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
+        return;
+    }
+
+    // order_key(f) >= key_lo as one unsigned compare on the raw bits u of f: (u ^ X) >= Y.  Above
+    // the +0.0 bin it is a signed compare of u with key_lo's magnitude; at or below it, u <= C (the
+    // +0.0 bin also takes -0.0, which order_key maps to +0.0).
+    const uint32_t key_lo = (uint32_t)bin << kBinShift;
+    uint32_t X, Y;
+    if (key_lo > 0x80000000u) {
+        X = 0x80000000u;
+        Y = (key_lo & 0x7FFFFFFFu) ^ 0x80000000u;
+    } else {
+        const uint32_t C = key_lo == 0x80000000u ? 0x80000000u : ~key_lo;
+        X = 0xFFFFFFFFu;
+        Y = ~C;
+    }
+    int total = 0;  // candidates appended so far
+    int rnd = 0;    // rounds done (the parity picks the counts buffer)
+    // append the candidates of the round at `base` (held in v)
+    auto compact_round = [&](const float4 (&v)[kSubRounds], int32_t base) {
+        const int par = rnd & 1;
+        const bool tail = base + kRoundScores > n32;  // uniform: only then may tokens lie past n
+        uint32_t selm = 0;  // bit 4 u + i: token base + 4096 u + 4 tid + i is a candidate
+#pragma unroll
+        for (int u = 0; u < kSubRounds; ++u) {
+            const int32_t p = base + u * 4 * kTopkThreads + 4 * tid;
+            const uint32_t w[4] = {__float_as_uint(v[u].x), __float_as_uint(v[u].y), __float_as_uint(v[u].z),
+                                   __float_as_uint(v[u].w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bool pass = (w[i] ^ X) >= Y;
+                if (tail) pass = pass && p + i < n32;
+                selm |= (pass ? 1u : 0u) << (4 * u + i);
             }
-            at += sg.y;
+        }
+        int pre[kSubRounds];  // candidates of sub-round u in this wave's lower lanes
+#pragma unroll
+        for (int u = 0; u < kSubRounds; ++u) {
+            const int c = __popc((selm >> (4 * u)) & 0xFu);
+            const int incl = topk::wave_incl_scan(c);
+            pre[u] = incl - c;
+            if (lane == kWave - 1) counts[par][u][wave] = incl;
         }
         __syncthreads();
-        topk::select_and_emit(sh, topk::LdsCands{ck, ci}, at, bin, above, (int)m, dst);
-    } else {
-        topk::select_and_emit(sh, topk::GlobalScores{scores + b * ld}, (int)n, bin, above, (int)m, dst);
+        // Offsets in (sub-round, wave) order: lane l of every wave takes the count of sub-round l / 16,
+        // wave l % 16, and one scan over the wave gives all 64 offsets.  counts[par] is rewritten two
+        // rounds later, after the next round's barrier, which every reader here has passed.
+        const int cl = counts[par][lane / kTopkWaves][lane % kTopkWaves];
+        const int cincl = topk::wave_incl_scan(cl);
+        const int cexcl = cincl - cl;
+#pragma unroll
+        for (int u = 0; u < kSubRounds; ++u) {
+            int pos = total + __builtin_amdgcn_readlane(cexcl, kTopkWaves * u + wave) + pre[u];
+            const int32_t p = base + u * 4 * kTopkThreads + 4 * tid;
+            const uint32_t w0 = __float_as_uint(v[u].x), w1 = __float_as_uint(v[u].y);
+            const uint32_t w2 = __float_as_uint(v[u].z), w3 = __float_as_uint(v[u].w);
+            for (uint32_t bits = (selm >> (4 * u)) & 0xFu; bits; bits &= bits - 1) {
+                const int i = __builtin_ctz(bits);
+                // element i picked with masks, not a select (which the compiler may turn into an
+                // indexed access that forces the buffer out of registers)
+                const uint32_t f = (w0 & (0u - (i == 0))) | (w1 & (0u - (i == 1))) | (w2 & (0u - (i == 2))) |
+                                   (w3 & (0u - (i == 3)));
+                if (pos < kCap) {
+                    ck[pos] = order_key(__uint_as_float(f));
+                    ci[pos] = p + i;
+                }
+                ++pos;
+            }
+        }
+        total += __builtin_amdgcn_readlane(cincl, kWave - 1);
+        ++rnd;
+    };
+    for (int32_t base = 0; base < n32; base += 3 * kRoundScores) {
+        compact_round(v0, base);
+        load_round(v0, base + 3 * kRoundScores);
+        if (base + kRoundScores >= n32) break;
+        compact_round(v1, base + kRoundScores);
+        load_round(v1, base + 4 * kRoundScores);
+        if (base + 2 * kRoundScores >= n32) break;
+        compact_round(v2, base + 2 * kRoundScores);
+        load_round(v2, base + 5 * kRoundScores);
     }
-    for (int i = (int)m + tid; i < max_topk; i += kThreads) dst[i] = -1;
+    __syncthreads();
+    topk::select_and_emit(sh, topk::LdsCands{ck, ci}, total < kCap ? total : kCap, bin, above, (int)m, dst);
+    for (int i = (int)m + tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
 }
 
 }  // namespace
@@ -311,7 +344,6 @@ DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
 {
     DecodeTopkLayout l;
     l.ld = (max_ctx + 63) / 64 * 64;
-    l.n_chunks = (max_ctx + kChunkScores - 1) / kChunkScores;
     size_t at = 0;
     auto take = [&](size_t bytes) {
         const size_t off = at;
@@ -320,9 +352,6 @@ DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
     };
     l.scores = take((size_t)B * l.ld * sizeof(float));
     l.hist = take((size_t)B * kBins * sizeof(uint32_t));
-    l.cands = take((size_t)B * kCap * sizeof(uint2));
-    l.cand_count = take((size_t)B * sizeof(int32_t));
-    l.seg = take((size_t)B * l.n_chunks * sizeof(int2));
     l.total = at;
     return l;
 }
@@ -336,14 +365,11 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
     char *base = reinterpret_cast<char *>(ws);
     float *scores = reinterpret_cast<float *>(base + l.scores);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base + l.hist);
-    uint2 *cands = reinterpret_cast<uint2 *>(base + l.cands);
-    int32_t *cand_count = reinterpret_cast<int32_t *>(base + l.cand_count);
-    int2 *seg = reinterpret_cast<int2 *>(base + l.seg);
     const int32_t max_topk = h.cfg.max_topk;
     {
         const int64_t nz = (int64_t)B * kBins;
         hipLaunchKernelGGL(decode_reset_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist,
-                           cand_count, (int64_t)B);
+                           (int64_t)B);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -358,14 +384,8 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
         if (e != hipSuccess) return e;
     }
     KernelTimer timer(h, SA_KERNEL_TOPK, st);
-    hipLaunchKernelGGL(decode_collect_kernel, dim3((unsigned)l.n_chunks, (unsigned)B), dim3(kCollectThreads), 0,
-                       st, scores, l.ld, ctx_len, max_ctx, topk_b, max_topk, hist, cands, cand_count, seg,
-                       (int)l.n_chunks);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_select_kernel, dim3((unsigned)B), dim3(kSelectWaves * kWave), 0, st, scores, l.ld,
-                       ctx_len, max_ctx, topk_b, max_topk, hist, cands, cand_count, seg, (int)l.n_chunks, idx,
-                       h.d_err);
+    hipLaunchKernelGGL(decode_topk_kernel, dim3((unsigned)B), dim3(kTopkThreads), 0, st, scores, l.ld, ctx_len,
+                       max_ctx, topk_b, max_topk, hist, idx, h.d_err);
     return hipGetLastError();
 }
 

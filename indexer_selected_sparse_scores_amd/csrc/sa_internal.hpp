@@ -102,8 +102,7 @@ hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w
 // ---- paged decode indexer + per-sequence top-k (bf16, H_I = 64, d_I = 128, 64-token pages) --
 struct DecodeTopkLayout {
     int64_t ld;          // score row stride (floats)
-    int64_t n_chunks;    // 8192-score chunks per sequence
-    size_t scores, hist, cands, cand_count, seg, total;  // byte offsets in the workspace
+    size_t scores, hist, total;  // byte offsets in the workspace
 };
 DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx);
 // idx [B, max_topk] gets each sequence's selection; ws holds decode_topk_layout(B, max_ctx).total
