@@ -7,16 +7,20 @@
 // Verifiable Synthetic Data", section 2.4.  In decode only the selected rows of the paged
 // cache are read (that page, section 2.3).
 //
-// attn_latent_mfma_kernel serves the latent layout (bf16, 16 heads sharing one 576-wide
-// row per token whose first 512 columns are the value).  A 4-wave workgroup walks the
-// selected rows of one query in chunks of 32; each thread gathers with 16-byte loads the
+// attn_latent_mfma_kernel serves the latent layout in prefill (bf16, 16 heads sharing one
+// 576-wide row per token whose first 512 columns are the value).  A 4-wave workgroup walks
+// the selected rows of one query in chunks of 32; each thread gathers with 16-byte loads the
 // pieces of K that its own logits MFMAs consume (the next chunk's pieces in flight while the
 // current one is computed), so every 1152-byte row is read once for all 16 heads and only
 // its value part passes through LDS.  Logits and P.V run on v_mfma_f32_16x16x32_bf16 with
 // an online softmax (running max / sum per head, exp2 with the log2(e) factor folded into
 // the scale).  P enters the MFMA as a bf16 hi part plus a bf16 residual, so the weights keep
-// ~16 mantissa bits.  In decode the selected rows of one sequence are split across
-// workgroups and a second kernel merges the partial (max, sum, accumulator) states.
+// ~16 mantissa bits.
+//
+// attn_decode_lds_kernel serves the latent layout in decode: the same math per chunk, with
+// the selected rows of one sequence split into 512-row ranges across workgroups, each range
+// staged whole rows at a time into LDS by direct global-to-LDS loads; attn_merge_kernel then
+// merges the partial (max, sum, accumulator) states.
 //
 // attn_generic_kernel serves every other shape (fp32 or bf16): one workgroup per (row,
 // head), logits in LDS, two-pass softmax.
@@ -148,25 +152,20 @@ __device__ __forceinline__ float row16_sum(float x)
 //  * P.V: every wave accumulates 128 of the 512 value columns, with V fragments from
 //    transposing LDS reads.
 // Row offsets run two chunks ahead (index load, then page lookup, then use).
-template <bool kSplit>
 __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     const uint16_t *__restrict__ q, int64_t n_rows, RowSource kv, Visibility vis, Selection sel,
-    float scale_log2, float *__restrict__ out, float *__restrict__ lse, int split_rows, int n_splits,
-    float *__restrict__ part_o, float *__restrict__ part_ml, uint32_t *err)
+    float scale_log2, float *__restrict__ out, float *__restrict__ lse, uint32_t *err)
 {
     __shared__ __attribute__((aligned(16))) AttnShared sh;
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int hh = lane % 16, grp = lane / 16;
     const int64_t r = blockIdx.x;
-    const int split = kSplit ? (int)blockIdx.y : 0;
-    uint32_t *err0 = (tid == 0 && split == 0) ? err : nullptr;
+    uint32_t *err0 = tid == 0 ? err : nullptr;
     const int64_t visible = visible_len(vis, r, err0);
     const int64_t kr = budget(sel, r, err0);
     const int64_t m = kr < visible ? kr : visible;
-    const int64_t j_begin = kSplit ? (int64_t)split * split_rows : 0;
-    const int64_t j_end = kSplit ? (j_begin + split_rows < m ? j_begin + split_rows : m) : m;
-    if (kSplit && j_begin >= m) return;  // the merge kernel ignores unused splits
+    const int64_t j_begin = 0, j_end = m;
     const int32_t *idx_row = sel.idx + r * sel.idx_ld;
     const uint16_t *kv_base = reinterpret_cast<const uint16_t *>(kv.base);
     const int n_chunks = (int)((j_end - j_begin + kChunk - 1) / kChunk);
@@ -355,30 +354,282 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
         for (int i = 0; i < kKHalf; ++i) asm volatile("" : : "v"(g[i].x));
     }
 
-    if (!kSplit) {
-        if (hh == 0) sh.inv_l[sm_head] = l_run > 0.f ? 1.f / l_run : 0.f;
-        if (lse && hh == 0) lse[r * kLH + sm_head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
-        __syncthreads();
-        const float4 iv = *reinterpret_cast<const float4 *>(&sh.inv_l[4 * grp]);
-        const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
+    if (hh == 0) sh.inv_l[sm_head] = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (lse && hh == 0) lse[r * kLH + sm_head] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : neg_inf;
+    __syncthreads();
+    const float4 iv = *reinterpret_cast<const float4 *>(&sh.inv_l[4 * grp]);
+    const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float *orow = out + (r * kLH + 4 * grp + i) * kLDv + kColsPerWave * wave + hh;
+    for (int i = 0; i < 4; ++i) {
+        float *orow = out + (r * kLH + 4 * grp + i) * kLDv + kColsPerWave * wave + hh;
 #pragma unroll
-            for (int nt = 0; nt < kNTiles; ++nt) orow[16 * nt] = acc[nt][i] * ivs[i];
+        for (int nt = 0; nt < kNTiles; ++nt) orow[16 * nt] = acc[nt][i] * ivs[i];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Latent layout, decode: selected rows staged in LDS by direct loads
+// ---------------------------------------------------------------------------------------
+constexpr int kDSplitRows = 512;                  // selected rows per decode workgroup
+constexpr int kRing = 3;                          // chunk slots in LDS: two chunks in flight
+constexpr int kRowBytes = kLDqk * 2;              // 1152
+constexpr int kSlotBytes = kChunk * kRowBytes;    // 36864
+constexpr int kBlkBytes = 8 * kRowBytes;          // rows 8w .. 8w + 7 of a chunk
+constexpr int kSegs = kRowBytes / 128;            // direct loads per wave per chunk
+constexpr size_t kRingBytes = (size_t)kRing * kSlotBytes;
+
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kLDqk];  // source of unused slots (zeros)
+
+// Byte offset of byte b of row R of a chunk in its LDS slot.  Rows 8w .. 8w + 7 form block w;
+// bytes 128 s .. 128 s + 127 of the block's rows form its 1 KB segment s, inside which row r = R % 8
+// keeps its 16-byte piece p at position 8 (r ^ (w & 1)) + (p ^ r).  One direct load (64 lanes x
+// 16 bytes, written lane after lane) fills one segment from 128 contiguous bytes of each of 8 rows;
+// the swizzle spreads the operand reads below (one piece of 16 rows from two blocks, or 8-byte
+// pieces of 8 rows) over distinct LDS banks.
+__device__ __forceinline__ uint32_t slot_byte(int R, int b)
+{
+    const int w = R >> 3, r = R & 7, p = b >> 4;
+    return (uint32_t)(kBlkBytes * w + 1024 * (p >> 3) + 16 * (8 * (r ^ (w & 1)) + ((p & 7) ^ r)) + (b & 15));
+}
+
+// Workgroup barrier ordering LDS accesses only: __syncthreads would also wait for every direct load
+// in flight (its fence waits for the whole memory counter).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt for the memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Decode attention over one sequence's selected rows, split in ranges of 512 across workgroups
+// (partials merged by attn_merge_kernel).  The rows of a 32-row chunk reach LDS through direct
+// global-to-LDS loads, 128 contiguous bytes of a row per lane octet, two chunks ahead of the one
+// being computed, so no register holds a row in flight and every row is read once at the full
+// gather rate.  Per chunk the math is that of attn_latent_mfma_kernel: logits on
+// v_mfma_f32_16x16x32_bf16 with K read from LDS, online softmax per head, P.V with V fragments from
+// transposing LDS reads.  The ring is read only through inline asm: the compiler cannot tell which
+// slot an in-flight direct load writes, and would otherwise wait for all of them before every read.
+__global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
+    const uint16_t *__restrict__ q, RowSource kv, Visibility vis, Selection sel, float scale_log2,
+    int n_splits, float *__restrict__ part_o, float *__restrict__ part_ml, uint32_t *err)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char ring[];  // kRing slots of kSlotBytes
+    __shared__ int64_t rows[kDSplitRows];  // pool row of each selected slot of the range (-1: none)
+    __shared__ float logits[2][kLH * kLogitLd];
+    __shared__ uint4 p_hi[kLH][4], p_lo[kLH][4];
+    __shared__ float alpha_s[kLH];
+
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const int hh = lane % 16, grp = lane / 16;
+    const int64_t r = blockIdx.x;
+    const int split = (int)blockIdx.y;
+    uint32_t *err0 = (tid == 0 && split == 0) ? err : nullptr;
+    const int64_t visible = visible_len(vis, r, err0);
+    const int64_t kr = budget(sel, r, err0);
+    const int64_t m = kr < visible ? kr : visible;
+    const int64_t j_begin = (int64_t)split * kDSplitRows;
+    if (j_begin >= m) return;  // the merge kernel ignores unused splits
+    const int n_here = (int)(m - j_begin < kDSplitRows ? m - j_begin : kDSplitRows);
+    const int n_chunks = (n_here + kChunk - 1) / kChunk;
+    const int32_t *idx_row = sel.idx + r * sel.idx_ld + j_begin;
+
+    const int nt_qk = wave & 1, kh = wave >> 1;
+    bf16x8 qa[kKHalf];
+    const uint16_t *qr = q + (r * kLH + hh) * kLDqk;
+#pragma unroll
+    for (int i = 0; i < kKHalf; ++i) qa[i] = as_bf16x8(load16(qr + 32 * (kKHalf * kh + i) + 8 * grp));
+
+    // pool row of every selected slot of the range: all indices, then all page lookups
+    {
+        int32_t sv[kDSplitRows / kAThreads];
+#pragma unroll
+        for (int k = 0; k < kDSplitRows / kAThreads; ++k) {
+            const int j = tid + kAThreads * k;
+            sv[k] = j < n_here ? idx_row[j] : -1;
         }
-    } else {
-        const int64_t slot = r * n_splits + split;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float *prow = part_o + (slot * kLH + 4 * grp + i) * kLDv + kColsPerWave * wave + hh;
+        for (int k = 0; k < kDSplitRows / kAThreads; ++k) {
+            const int j = tid + kAThreads * k;
+            const int64_t s = sv[k];
+            int64_t row = -1;
+            if (j < n_here) {
+                if (s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
+                if (s >= 0 && s < visible) {
+                    if (kv.block_table) {
+                        const int32_t page = kv.block_table[r * kv.max_blocks + s / kv.page_size];
+                        if (page >= 0 && page < kv.n_pages)
+                            row = (int64_t)page * kv.page_size + s % kv.page_size;
+                        else
+                            flag_error(err, SA_DEVERR_BLOCK_TABLE);
+                    } else {
+                        row = s;
+                    }
+                }
+            }
+            rows[j] = row;
+        }
+    }
+    __syncthreads();
+
+    // direct loads of chunk c into slot c % kRing: lane l of wave w copies, of chunk row 8w + dr,
+    // the pieces dp, dp + 8, ..., dp + 64 (one 128-byte segment per load); unused slots copy zeros
+    const int dr = (lane >> 3) ^ (wave & 1), dp = (lane & 7) ^ dr;
+    const unsigned char *kv_bytes = reinterpret_cast<const unsigned char *>(kv.base);
+    auto issue = [&](int c) {
+        const int jr = kChunk * c + 8 * wave + dr;
+        const int64_t row = jr < n_here ? rows[jr] : -1;
+        const unsigned char *src = (row >= 0 ? kv_bytes + row * kRowBytes
+                                             : reinterpret_cast<const unsigned char *>(g_zero_row)) + 16 * dp;
+        unsigned char *dst = ring + (c % kRing) * kSlotBytes + kBlkBytes * wave;
 #pragma unroll
-            for (int nt = 0; nt < kNTiles; ++nt) prow[16 * nt] = acc[nt][i];
+        for (int i = 0; i < kSegs; ++i)
+            __builtin_amdgcn_global_load_lds(src + 128 * i, (__attribute__((address_space(3))) void *)(dst + 1024 * i),
+                                             16, 0, 0);
+    };
+
+    // this lane's operand offsets within a slot: K pieces of the logits MFMAs (row 16 nt_qk + hh,
+    // piece 4 (9 kh + i) + grp) and the 8-byte V pieces of the P.V fragments (rows 8 grp + 2 (hh / 4)
+    // and +1, columns 128 wave + 16 nt + 4 (hh % 4) .. +3)
+    uint32_t koff[kKHalf], voff[kNTiles][2];
+#pragma unroll
+    for (int i = 0; i < kKHalf; ++i) koff[i] = slot_byte(16 * nt_qk + hh, 16 * (4 * (kKHalf * kh + i) + grp));
+#pragma unroll
+    for (int nt = 0; nt < kNTiles; ++nt) {
+        const int col = kColsPerWave * wave + 16 * nt + 4 * (hh % 4);
+        voff[nt][0] = slot_byte(8 * grp + 2 * (hh / 4), 2 * col);
+        voff[nt][1] = slot_byte(8 * grp + 2 * (hh / 4) + 1, 2 * col);
+    }
+    const uint32_t ring_lds = (uint32_t)reinterpret_cast<uintptr_t>(ring);
+
+    const float neg_inf = -__builtin_inff();
+    const int sm_head = kHeadsPerWave * wave + grp;  // softmax state owned by this lane group
+    float m_run = neg_inf, l_run = 0.f;
+    f32x4 acc[kNTiles];  // O[4 grp + i][128 wave + 16 nt + hh]
+#pragma unroll
+    for (int nt = 0; nt < kNTiles; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int c = 0; c < kRing - 1; ++c)
+        if (c < n_chunks) issue(c);
+#pragma unroll 1
+    for (int c = 0; c < n_chunks; ++c) {
+        // this wave's loads of chunk c are done once only the later chunks' are outstanding (no other
+        // memory instruction is issued in the loop); the barrier makes every wave's part visible and
+        // closes the previous chunk, whose slot takes chunk c + kRing - 1
+        static_assert(kRing >= 2 && kRing <= 4, "waits below");
+        const int later = n_chunks - 1 - c < kRing - 2 ? n_chunks - 1 - c : kRing - 2;  // chunks issued after c
+        if (later >= 2)
+            wait_vmcnt<2 * kSegs>();
+        else if (later == 1)
+            wait_vmcnt<kSegs>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();
+        if (c + kRing - 1 < n_chunks) issue(c + kRing - 1);
+        const uint32_t sb = ring_lds + (uint32_t)((c % kRing) * kSlotBytes);
+
+        // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh
+        {
+            bf16x8 kf[kKHalf];
+#pragma unroll
+            for (int i = 0; i < kKHalf; ++i) asm volatile("ds_read_b128 %0, %1" : "=v"(kf[i]) : "v"(sb + koff[i]));
+            // the wait is tied to the loaded registers, so nothing that reads them moves above it
+            static_assert(kKHalf == 9, "one operand per piece below");
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(kf[0]), "+v"(kf[1]), "+v"(kf[2]), "+v"(kf[3]), "+v"(kf[4]), "+v"(kf[5]), "+v"(kf[6]),
+                           "+v"(kf[7]), "+v"(kf[8])
+                         :
+                         : "memory");
+            f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = {0.f, 0.f, 0.f, 0.f};  // two chains
+#pragma unroll
+            for (int i = 0; i < kKHalf; i += 2) {
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], kf[i], sa0, 0, 0, 0);
+                if (i + 1 < kKHalf) sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i + 1], kf[i + 1], sa1, 0, 0, 0);
+            }
+            const f32x4 sacc = sa0 + sa1;
+            const int my_row = 16 * nt_qk + hh;
+            const int jr = kChunk * c + my_row;
+            const bool valid = jr < n_here && rows[jr] >= 0;
+            const int slot = slot_of_row(my_row);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) logits[kh][(4 * grp + i) * kLogitLd + slot] = valid ? sacc[i] : neg_inf;
         }
-        if (hh == 0) {
-            part_ml[(slot * kLH + sm_head) * 2 + 0] = m_run;
-            part_ml[(slot * kLH + sm_head) * 2 + 1] = l_run;
+        lds_barrier();
+
+        // online softmax of head sm_head over the 32 slots (this lane: slots l % 16 and 16 + l % 16)
+        {
+            const int sl = hh;
+            const float *lg0 = &logits[0][sm_head * kLogitLd];
+            const float *lg1 = &logits[1][sm_head * kLogitLd];
+            const float x0 = (lg0[sl] + lg1[sl]) * scale_log2;
+            const float x1 = (lg0[16 + sl] + lg1[16 + sl]) * scale_log2;
+            const float cmax = row16_max(fmaxf(x0, x1));
+            const float m_new = fmaxf(m_run, cmax);
+            const bool any = m_new != neg_inf;
+            const float alpha = any ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            const float p0 = any ? __builtin_amdgcn_exp2f(x0 - m_new) : 0.f;
+            const float p1 = any ? __builtin_amdgcn_exp2f(x1 - m_new) : 0.f;
+            const float psum = row16_sum(p0 + p1);
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+            const __bf16 r0 = (__bf16)(p0 - (float)h0), r1 = (__bf16)(p1 - (float)h1);
+            __bf16 *ph = reinterpret_cast<__bf16 *>(&p_hi[sm_head][0]);
+            __bf16 *pl = reinterpret_cast<__bf16 *>(&p_lo[sm_head][0]);
+            ph[sl] = h0;
+            pl[sl] = r0;
+            ph[16 + sl] = h1;
+            pl[16 + sl] = r1;
+            if (sl == 0) alpha_s[sm_head] = alpha;
         }
+        lds_barrier();
+
+        // rescale the accumulator rows (heads 4 grp + i), then P.V over the 32 rows
+        {
+            const float4 al = *reinterpret_cast<const float4 *>(&alpha_s[4 * grp]);
+#pragma unroll
+            for (int nt = 0; nt < kNTiles; ++nt) {
+                acc[nt][0] *= al.x;
+                acc[nt][1] *= al.y;
+                acc[nt][2] *= al.z;
+                acc[nt][3] *= al.w;
+            }
+            const bf16x8 pa_hi = as_bf16x8(p_hi[hh][grp]);
+            const bf16x8 pa_lo = as_bf16x8(p_lo[hh][grp]);
+            s16x4 vlo[kNTiles], vhi[kNTiles];
+#pragma unroll
+            for (int nt = 0; nt < kNTiles; ++nt) {
+                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vlo[nt]) : "v"(sb + voff[nt][0]));
+                asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vhi[nt]) : "v"(sb + voff[nt][1]));
+            }
+            static_assert(kNTiles == 8, "one operand per fragment below");
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(vlo[0]), "+v"(vlo[1]), "+v"(vlo[2]), "+v"(vlo[3]), "+v"(vlo[4]), "+v"(vlo[5]),
+                           "+v"(vlo[6]), "+v"(vlo[7]), "+v"(vhi[0]), "+v"(vhi[1]), "+v"(vhi[2]), "+v"(vhi[3]),
+                           "+v"(vhi[4]), "+v"(vhi[5]), "+v"(vhi[6]), "+v"(vhi[7])
+                         :
+                         : "memory");
+#pragma unroll
+            for (int nt = 0; nt < kNTiles; ++nt) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[nt], vhi[nt], 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, b, acc[nt], 0, 0, 0);
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, b, acc[nt], 0, 0, 0);
+            }
+        }
+    }
+
+    const int64_t slot = r * n_splits + split;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float *prow = part_o + (slot * kLH + 4 * grp + i) * kLDv + kColsPerWave * wave + hh;
+#pragma unroll
+        for (int nt = 0; nt < kNTiles; ++nt) prow[16 * nt] = acc[nt][i];
+    }
+    if (hh == 0) {
+        part_ml[(slot * kLH + sm_head) * 2 + 0] = m_run;
+        part_ml[(slot * kLH + sm_head) * 2 + 1] = l_run;
     }
 }
 
@@ -507,14 +758,12 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
     if (lse && threadIdx.x == 0) lse[r * H + h] = sum > 0.f ? (mx + __log2f(sum)) * kLn2 : neg_inf;
 }
 
-constexpr int kSplitRows = 256;
-
 }  // namespace
 
 size_t attention_workspace(const sa_handle_s &h, int64_t n_rows, bool decode)
 {
     if (!decode || !h.fast_attn) return 0;
-    const int64_t n_splits = (h.cfg.max_topk + kSplitRows - 1) / kSplitRows;
+    const int64_t n_splits = (h.cfg.max_topk + kDSplitRows - 1) / kDSplitRows;
     return (size_t)n_rows * n_splits * kLH * (kLDv + 2) * sizeof(float);
 }
 
@@ -529,25 +778,27 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSo
         const uint16_t *qq = reinterpret_cast<const uint16_t *>(q);
         if (!decode) {
             KernelTimer timer(h, SA_KERNEL_ATTENTION, st);
-            hipLaunchKernelGGL(attn_latent_mfma_kernel<false>, dim3((unsigned)n_rows), dim3(kAThreads), 0, st,
-                               qq, n_rows, kv, vis, sel, scale_log2, out, lse, 0, 1, nullptr, nullptr,
-                               h.d_err);
+            hipLaunchKernelGGL(attn_latent_mfma_kernel, dim3((unsigned)n_rows), dim3(kAThreads), 0, st, qq, n_rows,
+                               kv, vis, sel, scale_log2, out, lse, h.d_err);
             return hipGetLastError();
         }
-        const int n_splits = (h.cfg.max_topk + kSplitRows - 1) / kSplitRows;
+        // decode: the selected rows staged in LDS by direct loads, 512-row ranges per workgroup, then the merge
+        const int n_splits = (h.cfg.max_topk + kDSplitRows - 1) / kDSplitRows;
         float *part_o = reinterpret_cast<float *>(ws);
         float *part_ml = part_o + (size_t)n_rows * n_splits * kLH * kLDv;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_decode_lds_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRingBytes);
+        if (e != hipSuccess) return e;
         {
             KernelTimer timer(h, SA_KERNEL_ATTENTION, st);
-            hipLaunchKernelGGL(attn_latent_mfma_kernel<true>, dim3((unsigned)n_rows, (unsigned)n_splits),
-                               dim3(kAThreads), 0, st, qq, n_rows, kv, vis, sel, scale_log2, out, lse,
-                               kSplitRows, n_splits, part_o, part_ml, h.d_err);
-            hipError_t e = hipGetLastError();
+            hipLaunchKernelGGL(attn_decode_lds_kernel, dim3((unsigned)n_rows, (unsigned)n_splits), dim3(kAThreads),
+                               kRingBytes, st, qq, kv, vis, sel, scale_log2, n_splits, part_o, part_ml, h.d_err);
+            e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         KernelTimer timer(h, SA_KERNEL_MERGE, st);
         hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(n_rows * kLH)), dim3(kLDv / 4), 0, st, vis, sel,
-                           kSplitRows, n_splits, part_o, part_ml, out, lse);
+                           kDSplitRows, n_splits, part_o, part_ml, out, lse);
         return hipGetLastError();
     }
     const sa_config_t &c = h.cfg;
