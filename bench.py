@@ -217,10 +217,10 @@ def main():
         avg, n, tot = per_launch(kern_dec, "attention")
         if n:
             gbs = dec_gather_bytes / (avg * 1e-3) / 1e9
-            roofline_dec_attn = {"kernel": "attn_latent_mfma_kernel<true> (paged decode gather)",
+            roofline_dec_attn = {"kernel": "attn_decode_lds_kernel (paged decode gather)",
                                  "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                 "traffic": stored_traffic("attn_latent_mfma_kernel<true>"),
+                                 "traffic": stored_traffic("attn_decode_lds_kernel"),
                                  "algorithmic_per_launch": f"{dec_gather_bytes} B = {sel_rows} selected rows x "
                                                            f"{row_bytes} B latent row"}
 
