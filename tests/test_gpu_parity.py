@@ -422,3 +422,44 @@ def test_device_checks_flag_bad_block_table():
         assert e.value.status == sa.SA_ERR_DEVICE_CHECK
         assert sa.sparse_attn_check(h) == 0  # cleared
         assert torch.isfinite(out).all()
+
+
+@pytest.mark.gpu
+def test_decode_selected_tokens_on_a_bad_page_get_no_weight():
+    """k >= n selects every visible token, including the 64 whose block-table entry is corrupted: the
+    entry is flagged and those tokens get no weight, so the output equals attention over the others
+    (two 512-row ranges and a partial last chunk for the longer sequence)."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [300, 700]
+    say(f"decode, k >= n, bad block-table entry selected ctx={ctx}")
+    d = inputs.decode_inputs(inputs.small(wl, topk=1024), DEV, ctx=ctx, seed=13)
+    good = to_np(d["block_table"]).copy()
+    bt = d["block_table"].clone()
+    bt[0, 2] = 10 ** 6  # tokens 128..191 of sequence 0
+    d["block_table"] = bt
+    with sa.Handle(inputs.library_config(wl, max_topk=1024)) as h:
+        B = len(ctx)
+        out = torch.empty((B, 16, 512), device=DEV)
+        lse = torch.empty((B, 16), device=DEV)
+        idx = torch.empty((B, 1024), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_DECODE, B, d["max_ctx"])
+        sa.sparse_attn_decode(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], None, d["kidx_pages"],
+                              d["block_table"], d["ctx_len"], d["topk"], d["max_ctx"], out, lse, idx, ws)
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_check(h)
+        assert e.value.status == sa.SA_ERR_DEVICE_CHECK
+    gi = to_np(idx)
+    for b, n in enumerate(ctx):
+        assert np.array_equal(gi[b][:n], np.arange(n)) and np.all(gi[b][n:] == -1), f"seq {b}"
+    kv_pool, tab = compact_pages(d["kv_pages"], good, np.asarray(ctx))
+    ref_out = np.empty((B, 16, 512))
+    ref_lse = np.empty((B, 16))
+    for b, n in enumerate(ctx):
+        keep = np.arange(n) if b else np.concatenate([np.arange(128), np.arange(192, n)])
+        sel = np.full((1, 1024), -1, dtype=np.int32)
+        sel[0, :len(keep)] = keep
+        K = oracle.depage(kv_pool, tab[b], n)
+        o, l = oracle.attention_rows(to_np(d["q"])[b:b + 1], K, None, sel, oracle.default_scale(576), d_v=512)
+        ref_out[b], ref_lse[b] = o[0], l[0]
+    err = check_attention(to_np(out), to_np(lse), ref_out, ref_lse, what="bad page selected")
+    say(f"bad page selected: max|dO|={err:.2e}")
