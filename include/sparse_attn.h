@@ -86,6 +86,7 @@ typedef struct {
 #define SA_OP_PREFILL 1  /* n = L (sequence length), max_ctx ignored                    */
 #define SA_OP_DECODE  2  /* n = B (batch), max_ctx = upper bound of every ctx_len[b]     */
 #define SA_OP_TOPK    3  /* n = rows, max_ctx = cols                                      */
+#define SA_OP_PROJECT 4  /* n = L rows of indexer_project_q, max_ctx ignored              */
 
 /* Create a handle for one configuration.  Validates the config, allocates the 4-byte
  * device error word on the current device (the only device allocation the library makes)
@@ -180,6 +181,44 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
                                int32_t max_ctx, float *out, float *lse, int32_t *idx_out,
                                void *ws, size_t ws_bytes, void *stream);
 
+/* Index-space projections -- the first lines of the "Sparse Attention and RL Optimization...",
+ * section 2.5 pseudocode: the index query and key are linear maps of the attention query and
+ * key (i_q = W_iq(q), i_k = W_ik(k)); the head weights w(t, j) of the section 2.2 score are one
+ * more linear map of the query.  bf16 handles only (SA_ERR_UNSUPPORTED otherwise).  Weights are
+ * row-major [out, in] bf16; accumulation is fp32; bf16 outputs are rounded to nearest even.
+ *
+ * indexer_project_q, for each of the L query rows q[t] (H * d_qk values, [L, H, d_qk]):
+ *   q_idx[t] = W_iq q[t]   W_iq [H_I * d_I, H * d_qk]  ->  q_idx [L, H_I, d_I] bf16
+ *   w[t]     = W_w  q[t]   W_w  [H_I, H * d_qk]        ->  w [L, H_I] fp32
+ *   Either pair (W_iq, q_idx) or (W_w, w) may be NULL to skip it.  Two plain GEMMs, run by
+ *   hipBLASLt on `stream`; its handle is created on the first call of this handle (which may
+ *   synchronise and may allocate device memory of hipBLASLt's own) and released by
+ *   sparse_attn_destroy.  ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_PROJECT, L).
+ * Errors: SA_ERR_INVALID_ARG (NULL q, L < 1, both pairs NULL, a pair half NULL, misaligned),
+ * SA_ERR_UNSUPPORTED (not bf16), SA_ERR_WORKSPACE, SA_ERR_HIP (hipBLASLt failure, in last_error). */
+sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const void *W_iq, const void *W_w,
+                              void *q_idx, float *w, void *ws, size_t ws_bytes, void *stream);
+
+/* indexer_project_k: k_idx[t] = W_ik k[t] for the L key rows k[t] (the H_kv * d_qk key row:
+ * the latent row when H_kv = 1), W_ik [d_I, H_kv * d_qk] bf16, bf16 out.  Needs d_I = 128 and
+ * H_kv * d_qk a multiple of 16.
+ *   block_table == NULL: k_idx is [L, d_I], row t = token t.
+ *   block_table != NULL ([n_seqs, max_blocks] int32): k_idx is the paged index-key pool
+ *   [n_pages, page_size, d_I] of sparse_attn_decode, and row t is the token at position
+ *   p = row_pos[t] (or pos0 + t when row_pos is NULL) of sequence b = row_seq[t] (or 0 when
+ *   row_seq is NULL): it goes to page block_table[b * max_blocks + p / page_size], slot
+ *   p % page_size.  A prefill of one sequence
+ *   passes row_seq = row_pos = NULL and its first position pos0; a decode step passes one row
+ *   per sequence with row_seq[t] = t and row_pos[t] = ctx_len[t] - 1.  A row whose page entry
+ *   is outside [0, n_pages) (or whose sequence is outside [0, n_seqs), or whose position is
+ *   negative or beyond max_blocks pages) is not written and sets SA_DEVERR_BLOCK_TABLE.
+ * Needs no workspace.  Errors: SA_ERR_INVALID_ARG (NULL k / W_ik / k_idx, L < 1, misaligned,
+ * n_seqs, max_blocks or n_pages < 1 with a block table), SA_ERR_UNSUPPORTED (not bf16,
+ * d_I != 128, width not a multiple of 16). */
+sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const void *W_ik, void *k_idx,
+                              const int32_t *block_table, int32_t n_seqs, int32_t max_blocks, int64_t n_pages,
+                              const int32_t *row_seq, const int32_t *row_pos, int64_t pos0, void *stream);
+
 /* Kernel timing, a tracing aid for benchmarks.  While enabled, every kernel the handle
  * launches is bracketed by a pair of hipEvents recorded on the launch stream, and the
  * elapsed times are summed per kernel kind.  Enabling resets the sums; it creates events
@@ -191,7 +230,8 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
 #define SA_KERNEL_TOPK      1  /* per-row top-k selection                                 */
 #define SA_KERNEL_ATTENTION 2  /* attention over the selected rows                        */
 #define SA_KERNEL_MERGE     3  /* merge of split decode attention states                  */
-#define SA_KERNEL_COUNT     4
+#define SA_KERNEL_PROJECT   4  /* index-space projections (indexer_project_q / _k)         */
+#define SA_KERNEL_COUNT     5
 sa_status_t sparse_attn_profile(sa_handle_t h, int enable);
 sa_status_t sparse_attn_profile_read(sa_handle_t h, double *total_ms, int64_t *launches);
 

@@ -25,15 +25,15 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_DEVICE_CHECK = range(6)
 SA_F32, SA_BF16 = 0, 1
-SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK = 1, 2, 3
+SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK, SA_OP_PROJECT = 1, 2, 3, 4
 SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK = 1, 2, 4, 8
 
 # Every symbol include/sparse_attn.h declares.
 EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error",
             "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
-            "sparse_attn_prefill", "sparse_attn_decode", "sparse_attn_profile",
-            "sparse_attn_profile_read")
-KERNEL_KINDS = ("indexer", "topk", "attention", "merge")
+            "sparse_attn_prefill", "sparse_attn_decode", "indexer_project_q", "indexer_project_k",
+            "sparse_attn_profile", "sparse_attn_profile_read")
+KERNEL_KINDS = ("indexer", "topk", "attention", "merge", "project")
 
 
 class SparseAttnError(RuntimeError):
@@ -94,6 +94,8 @@ def load_library() -> ctypes.CDLL:
         "topk_select": ([P, P, i64, i64, i64, P, P, i32, P, P], st),
         "sparse_attn_prefill": ([P, P, P, P, P, P, P, i64, i32, P, P, P, P, sz, P], st),
         "sparse_attn_decode": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, P, P, P, P, sz, P], st),
+        "indexer_project_q": ([P, P, i64, P, P, P, P, P, sz, P], st),
+        "indexer_project_k": ([P, P, i64, P, P, P, i32, i32, i64, P, P, i64, P], st),
         "sparse_attn_profile": ([P, ctypes.c_int], st),
         "sparse_attn_profile_read": ([P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
     }
@@ -219,6 +221,24 @@ def sparse_attn_decode(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, bl
         h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
         _ptr(block_table), max_blocks, _ptr(ctx_len), _ptr(topk), B, int(max_ctx), _ptr(out), _ptr(lse),
         _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def indexer_project_q(h: Handle, q, W_iq, W_w, q_idx, w, ws=None, stream=None) -> None:
+    """q_idx = q W_iq^T (bf16) and w = q W_w^T (fp32) per query row; either pair may be None."""
+    L = q.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(h.ptr, load_library().indexer_project_q(h.ptr, _ptr(q), L, _ptr(W_iq), _ptr(W_w), _ptr(q_idx),
+                                                   _ptr(w), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def indexer_project_k(h: Handle, k, W_ik, k_idx, block_table=None, n_pages: int = 0, row_seq=None,
+                      row_pos=None, pos0: int = 0, stream=None) -> None:
+    """k_idx = k W_ik^T per key row, contiguous or into the paged index-key pool (block_table given)."""
+    L = k.shape[0]
+    n_seqs, max_blocks = (0, 0) if block_table is None else block_table.shape
+    _check(h.ptr, load_library().indexer_project_k(h.ptr, _ptr(k), L, _ptr(W_ik), _ptr(k_idx), _ptr(block_table),
+                                                   n_seqs, max_blocks, int(n_pages), _ptr(row_seq), _ptr(row_pos),
+                                                   int(pos0), _stream(stream)))
 
 
 def sparse_attn_profile(h: Handle, enable: bool) -> None:

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attention.hip", "prefill_topk.hip", "decode.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attention.hip", "prefill_topk.hip", "decode.hip",
+           "projections.hip"]
 ARCH = os.environ.get("SA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -40,7 +41,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    # the query projections call hipBLASLt
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp, "-L/opt/rocm/lib", "-lhipblaslt",
+           "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

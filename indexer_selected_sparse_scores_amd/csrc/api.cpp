@@ -232,6 +232,7 @@ void sparse_attn_destroy(sa_handle_t h)
     (void)hipDeviceSynchronize();
     (void)sa::drain_profile(*h);
     for (hipEvent_t e : h->spare_events) (void)hipEventDestroy(e);
+    sa::destroy_projection_state(*h);
     (void)hipFree(h->d_err);
     delete h;
 }
@@ -282,6 +283,9 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
         return SA_OK;
     case SA_OP_TOPK:
         *bytes = 0;
+        return SA_OK;
+    case SA_OP_PROJECT:
+        *bytes = sa::projection_workspace();
         return SA_OK;
     default:
         return fail(h, SA_ERR_INVALID_ARG, "unknown op %d", op);
@@ -459,6 +463,50 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
     sa::Selection sel{idx, c.max_topk, c.max_topk, topk};
     return hip_status(h, sa::launch_attention(*h, q, B, kv, vv, vis, sel, out, lse, base + lay.attn, st),
                       "attention launch");
+}
+
+sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const void *W_iq, const void *W_w,
+                              void *q_idx, float *w, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!q) return fail(h, SA_ERR_INVALID_ARG, "q is NULL");
+    if (L < 1) return fail(h, SA_ERR_INVALID_ARG, "L must be >= 1");
+    if (!W_iq && !W_w) return fail(h, SA_ERR_INVALID_ARG, "nothing to project: W_iq and W_w are both NULL");
+    if (!W_iq != !q_idx || !W_w != !w)
+        return fail(h, SA_ERR_INVALID_ARG, "W_iq / q_idx and W_w / w must be given (or left NULL) in pairs");
+    if (h->cfg.dtype != SA_BF16) return fail(h, SA_ERR_UNSUPPORTED, "the projections take bf16 handles only");
+    if (!aligned16(q) || (W_iq && (!aligned16(W_iq) || !aligned16(q_idx))) || (W_w && (!aligned16(W_w) || !aligned16(w))))
+        return fail(h, SA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (!ws || ws_bytes < sa::projection_workspace())
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", sa::projection_workspace(), ws_bytes);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    // on failure the launcher has put hipBLASLt's reason in last_error
+    return sa::launch_project_q(*h, q, L, W_iq, W_w, q_idx, w, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const void *W_ik, void *k_idx,
+                              const int32_t *block_table, int32_t n_seqs, int32_t max_blocks, int64_t n_pages,
+                              const int32_t *row_seq, const int32_t *row_pos, int64_t pos0, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!k || !W_ik || !k_idx) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (L < 1) return fail(h, SA_ERR_INVALID_ARG, "L must be >= 1");
+    const sa_config_t &c = h->cfg;
+    if (c.dtype != SA_BF16) return fail(h, SA_ERR_UNSUPPORTED, "the projections take bf16 handles only");
+    if (c.d_idx != 128) return fail(h, SA_ERR_UNSUPPORTED, "the key projection needs d_idx = 128 (got %d)", c.d_idx);
+    if ((c.n_kv_heads * c.d_qk) % 16 != 0)
+        return fail(h, SA_ERR_UNSUPPORTED, "the key row width (%d) must be a multiple of 16", c.n_kv_heads * c.d_qk);
+    if (!aligned16(k) || !aligned16(W_ik) || !aligned16(k_idx)) return fail(h, SA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if (block_table && (n_seqs < 1 || max_blocks < 1 || n_pages < 1))
+        return fail(h, SA_ERR_INVALID_ARG, "a block table needs n_seqs, max_blocks and n_pages >= 1");
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    return hip_status(h, sa::launch_project_k(*h, k, L, W_ik, k_idx, block_table, n_seqs, max_blocks, n_pages, row_seq,
+                                              row_pos, pos0, reinterpret_cast<hipStream_t>(stream)),
+                      "key projection launch");
 }
 
 }  // extern "C"

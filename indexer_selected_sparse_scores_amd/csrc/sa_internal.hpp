@@ -19,6 +19,7 @@ struct sa_handle_s {
     bool fast_indexer;      // bf16, H_I = 64, d_I = 128: MFMA indexer kernels
     bool fast_decode;       // fast_indexer with 64-token pages: the paged decode kernels
     bool fast_attn;         // bf16, H = 16, H_kv = 1, d_qk = 576, d_v = 512, v_from_k
+    void *blt = nullptr;    // hipBLASLt state of the query projections (created on first use)
     std::string last_error;
 
     // kernel timing (sparse_attn_profile)
@@ -110,6 +111,15 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
                                       int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
                                       const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
                                       int32_t *idx, void *ws, hipStream_t st);
+
+// ---- index-space projections (bf16) ---------------------------------------------------
+size_t projection_workspace();
+sa_status_t launch_project_q(sa_handle_s &h, const void *q, int64_t L, const void *W_iq, const void *W_w,
+                             void *q_idx, float *w, void *ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_project_k(sa_handle_s &h, const void *k, int64_t L, const void *W_ik, void *k_idx,
+                            const int32_t *block_table, int32_t n_seqs, int32_t max_blocks, int64_t n_pages,
+                            const int32_t *row_seq, const int32_t *row_pos, int64_t pos0, hipStream_t st);
+void destroy_projection_state(sa_handle_s &h);
 
 // Workspace bytes launch_attention needs for n_rows decode rows (split partials).
 size_t attention_workspace(const sa_handle_s &h, int64_t n_rows, bool decode);

@@ -19,6 +19,9 @@ Stable Reinforcement Learning, and Verifiable Synthetic Data"):
 * ``decode`` -- one new token per sequence against a paged cache: the pages are first
   laid out contiguously through the block table ([P3] section 2.3: only the selected k
   entries are read, and this composes with paged KV management), then the same steps.
+* ``project`` / ``round_bf16`` / ``paged_slot`` -- the index projections of the [P1] section
+  2.5 pseudocode (i_q = W_iq(q), i_k = W_ik(k)) as plain linear maps in double, the rounding
+  of their bf16 outputs, and where a projected key lands in the paged index cache.
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py``; none is unpinned.
 """
@@ -235,3 +238,40 @@ def decode(q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len, top
     if with_scores:
         res["scores"] = scores
     return res
+
+
+# ---------------------------------------------------------------------------------------
+# Index-space projections
+# ---------------------------------------------------------------------------------------
+def project(x, W) -> np.ndarray:
+    """Row-wise linear map y[t] = W x[t] in double: the index projections of the [P1] section 2.5
+    pseudocode (i_q = W_iq(q), i_k = W_ik(k)); the head weights w(t, j) of the [P1] section 2.2
+    score are read as one more such map of the query row.  x [L, in], W [out, in] -> [L, out].
+    A library matmul serves as the step."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+def project_abs(x, W) -> np.ndarray:
+    """sum_c |W[o, c] x[t, c]|: the size of the terms behind each projected value (tolerances)."""
+    return np.abs(np.asarray(x, dtype=np.float64)) @ np.abs(np.asarray(W, dtype=np.float64)).T
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits), ties to even, of finite doubles in bf16's normal
+    range: x = m 2^e with 0.5 <= |m| < 1, and m is rounded to a multiple of 2^-8."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def paged_slot(block_table, seq: int, pos: int, page_size: int, n_pages: int):
+    """(page, slot) of position pos of sequence seq in a paged cache ([P3] section 2.3, paged KV
+    management): page block_table[seq][pos // page_size], slot pos % page_size; None when the
+    position or its page entry is out of range."""
+    bt = np.asarray(block_table)
+    if pos < 0 or seq < 0 or seq >= bt.shape[0] or pos // page_size >= bt.shape[1]:
+        return None
+    page = int(bt[seq, pos // page_size])
+    if page < 0 or page >= n_pages:
+        return None
+    return page, pos % page_size
