@@ -51,6 +51,7 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
+    ap.add_argument("--no-projections", action="store_true", help="skip the index-projection measurement")
     return ap.parse_args()
 
 
@@ -232,6 +233,8 @@ def main():
                 rf["frac_of_measured"] = round(rf["achieved"] / peaks[key], 4)
                 rf["measured_peak"] = key
 
+    projections = None if args.no_projections else measure_projections(h_pre, P, L, args.steps, torch)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(P, pre_wl, K, args.cpu_seconds)
@@ -262,11 +265,61 @@ def main():
         "roofline_decode_gather": roofline_dec_attn,
         "kernels": kernels,
         "peaks_measured": peaks,
+        "projections": projections,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
     h_pre.close()
     h_dec.close()
+
+
+def measure_projections(h, P, L, steps, torch):
+    """The index projections at the prefill shape (not part of `value`): q_idx and w from the L
+    attention query rows (two bf16 GEMMs on hipBLASLt) and k_idx from the L latent rows (the
+    library's MFMA kernel), with synthetic N(0, 1/width) bf16 weights."""
+    import indexer_selected_sparse_scores_amd as sa
+    dev = "cuda"
+    s = h.cfg
+    kq = s.n_heads * s.d_qk
+    kk = s.n_kv_heads * s.d_qk
+    g = torch.Generator(device=dev).manual_seed(20261202)
+    W_iq = (torch.randn((s.n_idx_heads * s.d_idx, kq), generator=g, device=dev) * kq ** -0.5).to(torch.bfloat16)
+    W_w = (torch.randn((s.n_idx_heads, kq), generator=g, device=dev) * kq ** -0.5).to(torch.bfloat16)
+    W_ik = (torch.randn((s.d_idx, kk), generator=g, device=dev) * kk ** -0.5).to(torch.bfloat16)
+    q_idx = torch.empty((L, s.n_idx_heads, s.d_idx), dtype=torch.bfloat16, device=dev)
+    w = torch.empty((L, s.n_idx_heads), dtype=torch.float32, device=dev)
+    k_idx = torch.empty((L, s.d_idx), dtype=torch.bfloat16, device=dev)
+    ws = sa.workspace(h, sa.SA_OP_PROJECT, L)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    log(f"[bench] index projections L={L}")
+    q_ms = timed(lambda: sa.indexer_project_q(h, P["q"], W_iq, W_w, q_idx, w, ws))
+    k_ms = timed(lambda: sa.indexer_project_k(h, P["k"], W_ik, k_idx))
+    sa.sparse_attn_check(h)
+    q_flop = 2.0 * L * kq * (s.n_idx_heads * s.d_idx + s.n_idx_heads)
+    k_bytes = L * (2 * kk + 2 * s.d_idx) + 2 * s.d_idx * kk
+    q_tf = q_flop / (q_ms * 1e-3) / 1e12
+    k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    return {
+        "query": {"ms": round(q_ms, 4), "bound": "mfma", "achieved": round(q_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(q_tf / PEAK_BF16_TFLOPS, 4),
+                  "algorithmic_per_launch": f"{q_flop:.4g} flop = {L} rows x 2 x {kq} x "
+                                            f"({s.n_idx_heads * s.d_idx} + {s.n_idx_heads}) (q_idx and w)"},
+        "key": {"ms": round(k_ms, 4), "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4),
+                "algorithmic_per_launch": f"{k_bytes} B = {L} rows x ({2 * kk} B latent row read + "
+                                          f"{2 * s.d_idx} B index key written) + W_ik"},
+    }
 
 
 def measured_peaks(torch):

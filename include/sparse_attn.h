@@ -201,7 +201,7 @@ sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const voi
 
 /* indexer_project_k: k_idx[t] = W_ik k[t] for the L key rows k[t] (the H_kv * d_qk key row:
  * the latent row when H_kv = 1), W_ik [d_I, H_kv * d_qk] bf16, bf16 out.  Needs d_I = 128 and
- * H_kv * d_qk a multiple of 16.
+ * a key row H_kv * d_qk of 128, 256, 512 or 576 elements (W_ik is held in LDS).
  *   block_table == NULL: k_idx is [L, d_I], row t = token t.
  *   block_table != NULL ([n_seqs, max_blocks] int32): k_idx is the paged index-key pool
  *   [n_pages, page_size, d_I] of sparse_attn_decode, and row t is the token at position
@@ -214,7 +214,7 @@ sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const voi
  *   negative or beyond max_blocks pages) is not written and sets SA_DEVERR_BLOCK_TABLE.
  * Needs no workspace.  Errors: SA_ERR_INVALID_ARG (NULL k / W_ik / k_idx, L < 1, misaligned,
  * n_seqs, max_blocks or n_pages < 1 with a block table), SA_ERR_UNSUPPORTED (not bf16,
- * d_I != 128, width not a multiple of 16). */
+ * d_I != 128, another key-row width). */
 sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const void *W_ik, void *k_idx,
                               const int32_t *block_table, int32_t n_seqs, int32_t max_blocks, int64_t n_pages,
                               const int32_t *row_seq, const int32_t *row_pos, int64_t pos0, void *stream);

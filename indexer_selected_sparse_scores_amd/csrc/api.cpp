@@ -497,8 +497,9 @@ sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const voi
     const sa_config_t &c = h->cfg;
     if (c.dtype != SA_BF16) return fail(h, SA_ERR_UNSUPPORTED, "the projections take bf16 handles only");
     if (c.d_idx != 128) return fail(h, SA_ERR_UNSUPPORTED, "the key projection needs d_idx = 128 (got %d)", c.d_idx);
-    if ((c.n_kv_heads * c.d_qk) % 16 != 0)
-        return fail(h, SA_ERR_UNSUPPORTED, "the key row width (%d) must be a multiple of 16", c.n_kv_heads * c.d_qk);
+    const int kw = c.n_kv_heads * c.d_qk;
+    if (kw != 576 && kw != 512 && kw != 256 && kw != 128)
+        return fail(h, SA_ERR_UNSUPPORTED, "the key projection serves key rows of 128, 256, 512 or 576 elements (got %d)", kw);
     if (!aligned16(k) || !aligned16(W_ik) || !aligned16(k_idx)) return fail(h, SA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
     if (block_table && (n_seqs < 1 || max_blocks < 1 || n_pages < 1))
         return fail(h, SA_ERR_INVALID_ARG, "a block table needs n_seqs, max_blocks and n_pages >= 1");

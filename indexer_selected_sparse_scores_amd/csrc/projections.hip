@@ -7,10 +7,12 @@
 //  * q side: q_idx = q W_iq^T (bf16 out) and w = q W_w^T (fp32 out) are plain GEMMs over the
 //    H * d_qk query row (9216 wide for the latent shapes): they run on hipBLASLt, bf16 inputs
 //    with fp32 accumulation.
-//  * k side: k_idx = k W_ik^T over the 576-wide latent row, one v_mfma_f32_32x32x16_bf16 tile
-//    of 32 tokens x 32 index dims per wave, written straight to its destination row: the
-//    contiguous [L, d_I] array, or the token's slot of the paged index-key cache.
+//  * k side: k_idx = k W_ik^T over the 576-wide latent row on v_mfma_f32_32x32x16_bf16, W_ik
+//    held in LDS by persistent workgroups, each projected row written straight to where it
+//    belongs: the contiguous [L, d_I] array, or the token's slot of the paged index-key cache.
 #include <hipblaslt/hipblaslt.h>
+
+#include <type_traits>
 
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
@@ -20,62 +22,132 @@ namespace sa {
 namespace {
 
 constexpr int kPD = 128;                 // index dims (d_I) of the key projection kernel
-constexpr int kPRows = 32;               // tokens per workgroup
-constexpr int kPThreads = 4 * kWave;     // wave w makes index dims 32 w .. 32 w + 31
-constexpr int kTileLd = kPD + 8;         // padded LDS row of the output tile (bf16)
+constexpr int kPWaves = 8;                // two waves per SIMD
+constexpr int kPThreads = kPWaves * kWave;
+constexpr int kPRows = 32;               // tokens per wave tile
 
-// k_idx of tokens r0 .. r0 + 31.  A operand: token r0 + l % 32 (clamped to the last row),
-// k-elements 16 s + 8 (l / 32) .. +7; B operand: W_ik row 32 w + l % 32 (index dim), same
-// k-elements.  The fp32 tile is rounded to bf16 and staged in LDS, then written as whole
-// 256-byte rows: contiguous, or to page block_table[seq, pos / page_size], slot
-// pos % page_size, with (seq, pos) = (row_seq[r], row_pos[r]), defaulting to (0, pos0 + r); a row whose
-// sequence, position or page entry is out of range is skipped and flagged.
-__global__ __launch_bounds__(kPThreads) void project_k_kernel(
-    const uint16_t *__restrict__ k, int64_t L, int K, const uint16_t *__restrict__ W, uint16_t *__restrict__ out,
+// Destination of projected key row r (a lane's token; r < L): the contiguous [L, d_I] array, or
+// page block_table[seq, pos / page_size], slot pos % page_size with (seq, pos) = (row_seq[r],
+// row_pos[r]), defaulting to (0, pos0 + r); nullptr when any part is out of range (the caller
+// flags it).  The block-table load is made for every lane, at a clamped index, so that no load
+// sits behind a lane-dependent branch.
+template <bool PAGED>
+__device__ __forceinline__ uint16_t *key_row_dst(int64_t r, uint16_t *out, const int32_t *block_table, int32_t n_seqs,
+                                                 int32_t max_blocks, int32_t page_size, int64_t n_pages,
+                                                 const int32_t *row_seq, const int32_t *row_pos, int64_t pos0)
+{
+    if (!PAGED) return out + r * kPD;
+    const int64_t seq = row_seq ? row_seq[r] : 0;
+    const int64_t pos = row_pos ? (int64_t)row_pos[r] : pos0 + r;
+    const int64_t lp = pos >= 0 ? pos / page_size : -1;
+    const bool ok = lp >= 0 && lp < max_blocks && seq >= 0 && seq < n_seqs;
+    const int32_t page = block_table[ok ? seq * max_blocks + lp : 0];
+    if (!ok || page < 0 || page >= n_pages) return nullptr;
+    return out + ((int64_t)page * page_size + pos % page_size) * kPD;
+}
+
+// Persistent: each workgroup copies W_ik once into LDS, in MFMA B-fragment order (fragment
+// (nt, s) = index dims 32 nt .. +31, k-elements 16 s .. +15, one linear 1 KB block: lane l holds
+// dim 32 nt + l % 32, elements 16 s + 8 (l / 32) .. +7), then its waves take 32-token tiles in
+// turn.  A wave multiplies its tile's rows by all 128 index dims (four 32x32 accumulators).  Its
+// A fragments (token l % 32, elements 16 s + 8 (l / 32) .. +7) stream through a ring of KD
+// k-steps of registers: the load for k-step s + KD (of this tile, or of the wave's next tile) is
+// issued as soon as k-step s's products are, so KD KB per wave stay in flight across tiles; the
+// B fragments are read from LDS one k-step ahead.  The fp32 results are rounded to bf16 and each
+// row is stored where it belongs.
+template <int KS, bool PAGED>  // K / 16 k-steps; destination in the paged cache or contiguous
+__global__ __launch_bounds__(kPThreads, 1) void project_k_kernel(
+    const uint16_t *__restrict__ k, int64_t L, const uint16_t *__restrict__ W, uint16_t *__restrict__ out,
     const int32_t *__restrict__ block_table, int32_t n_seqs, int32_t max_blocks, int32_t page_size, int64_t n_pages,
     const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos, int64_t pos0, uint32_t *err)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kPRows][kTileLd];
+    constexpr int K = 16 * KS;
+    constexpr int KD = KS >= 16 ? KS / 2 : KS;  // ring depth in k-steps; divides KS
+    static_assert(KS % KD == 0, "a tile must fill the ring a whole number of times");
+    typedef __attribute__((address_space(1))) uint32_t global_u32;
+    extern __shared__ __attribute__((aligned(16))) uint4 wfrag[];  // 4 KS fragments of 64 x 16 bytes
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-    const int64_t r0 = (int64_t)blockIdx.x * kPRows;
-    int64_t arow = r0 + lane % 32;
-    if (arow >= L) arow = L - 1;
-    const uint16_t *ap = k + arow * (int64_t)K + 8 * (lane / 32);
-    const uint16_t *bp = W + (int64_t)(32 * wave + lane % 32) * K + 8 * (lane / 32);
-    f32x16 acc = {};
-#pragma unroll 6
-    for (int s = 0; s < K / 16; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(load16(ap + 16 * s)), as_bf16x8(load16(bp + 16 * s)),
-                                                      acc, 0, 0, 0);
-    // register i of lane l: token 8 (i / 4) + 4 (l / 32) + i % 4, index dim 32 wave + l % 32
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const __bf16 v = (__bf16)acc[i];
-        tile[8 * (i / 4) + 4 * (lane / 32) + i % 4][32 * wave + lane % 32] = __builtin_bit_cast(uint16_t, v);
+    for (int f = wave; f < 4 * KS; f += kPWaves) {
+        const int nt = f / KS, st = f % KS;
+        wfrag[f * kWave + lane] = load16(W + (int64_t)(32 * nt + lane % 32) * K + 16 * st + 8 * (lane / 32));
     }
     __syncthreads();
-    // thread t writes bytes 32 (t % 8) .. +31 of token row t / 8
-    const int row = tid / 8, part = tid % 8;
-    const int64_t r = r0 + row;
-    if (r >= L) return;
-    uint16_t *dst;
-    if (!block_table) {
-        dst = out + r * kPD;
-    } else {
-        const int64_t seq = row_seq ? row_seq[r] : 0;
-        const int64_t pos = row_pos ? (int64_t)row_pos[r] : pos0 + r;
-        const int64_t lp = pos >= 0 ? pos / page_size : -1;
-        const int32_t page = lp >= 0 && lp < max_blocks && seq >= 0 && seq < n_seqs ? block_table[seq * max_blocks + lp] : -1;
-        if (page < 0 || page >= n_pages) {
-            if (part == 0) flag_error(err, SA_DEVERR_BLOCK_TABLE);
-            return;
-        }
-        dst = out + ((int64_t)page * page_size + pos % page_size) * kPD;
+
+    const int64_t n_tiles = (L + kPRows - 1) / kPRows;
+    const int64_t stride = (int64_t)gridDim.x * kPWaves;
+    // token rows are clamped into [0, L): a tile past the end loads row L - 1 and is never used
+    auto a_ptr = [&](int64_t tile) {
+        int64_t arow = tile * kPRows + lane % 32;
+        if (arow >= L) arow = L - 1;
+        return k + arow * (int64_t)K + 8 * (lane / 32);
+    };
+    bf16x8 a[KD];
+    int64_t tile = (int64_t)blockIdx.x * kPWaves + wave;
+    const uint16_t *cp = a_ptr(tile);
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+        a[s] = as_bf16x8(load16(cp + 16 * s));
+        __builtin_amdgcn_sched_barrier(0);  // issued in k-step order, the order the loop consumes them
     }
-    const uint4 *src = reinterpret_cast<const uint4 *>(&tile[row][16 * part]);
-    uint4 *d = reinterpret_cast<uint4 *>(dst + 16 * part);
-    d[0] = src[0];
-    d[1] = src[1];
+    const bool odd = lane & 1;
+    for (; tile < n_tiles; tile += stride) {
+        const int64_t r0 = tile * kPRows;
+        const bool mine = r0 + lane % 32 < L;
+        // every lane resolves its token's destination (the lanes of both halves alike) before the
+        // products, so the loads involved are long done by the stores
+        uint16_t *my_dst = key_row_dst<PAGED>(mine ? r0 + lane % 32 : L - 1, out, block_table, n_seqs, max_blocks,
+                                              page_size, n_pages, row_seq, row_pos, pos0);
+        const uint16_t *np = a_ptr(tile + stride);
+        // opaque per tile, so the fragment reads (the same every tile) are not hoisted out of the loop
+        int wl = lane;
+        asm volatile("" : "+v"(wl));
+        f32x16 acc[4] = {};
+        uint4 b[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) b[nt] = wfrag[(nt * KS) * kWave + wl];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint4 bn[4];
+            if (s + 1 < KS) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) bn[nt] = wfrag[(nt * KS + s + 1) * kWave + wl];
+            }
+            const bf16x8 cur = a[s % KD];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, as_bf16x8(b[nt]), acc[nt], 0, 0, 0);
+            a[s % KD] = as_bf16x8(load16(s + KD < KS ? cp + 16 * (s + KD) : np + 16 * (s + KD - KS)));
+            if (s + 1 < KS) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) b[nt] = bn[nt];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep each k-step's refill where it is issued
+        }
+        cp = np;
+        if (PAGED && mine && lane < kPRows && !my_dst) flag_error(err, SA_DEVERR_BLOCK_TABLE);
+        if (!mine) my_dst = nullptr;
+        // register i of lane l: token r0 + 8 (i / 4) + 4 (l / 32) + i % 4, index dim 32 nt + l % 32.
+        // Lane j < 32 holds the destination of token r0 + j, shared through the wave.
+        const uint64_t my_bits = reinterpret_cast<uint64_t>(my_dst);
+        // Registers i and i + 1 hold consecutive tokens.  Neighbouring lanes swap one of them so that
+        // an even lane stores dims (d, d + 1) of the first token and an odd lane those of the second,
+        // as one 4-byte store each.
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const int tr = 8 * (i / 4) + 4 * (lane / 32) + i % 4 + (odd ? 1 : 0);
+            const uint64_t dst = ((uint64_t)__shfl((uint32_t)(my_bits >> 32), tr) << 32) | __shfl((uint32_t)my_bits, tr);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const float give = odd ? acc[nt][i] : acc[nt][i + 1];
+                const float got = __builtin_bit_cast(
+                    float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, give), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+                const float d0 = odd ? got : acc[nt][i], d1 = odd ? acc[nt][i + 1] : got;
+                const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)d0) |
+                                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)d1) << 16);
+                if (dst) *(global_u32 *)(dst + 2 * (32 * nt + (lane % 32 & ~1))) = v;
+            }
+        }
+    }
 }
 
 struct BltState {
@@ -171,12 +243,32 @@ hipError_t launch_project_k(sa_handle_s &h, const void *k, int64_t L, const void
                             const int32_t *row_seq, const int32_t *row_pos, int64_t pos0, hipStream_t st)
 {
     const int K = h.cfg.n_kv_heads * h.cfg.d_qk;
-    KernelTimer timer(h, SA_KERNEL_PROJECT, st);
-    hipLaunchKernelGGL(project_k_kernel, dim3((unsigned)((L + kPRows - 1) / kPRows)), dim3(kPThreads), 0, st,
-                       reinterpret_cast<const uint16_t *>(k), L, K, reinterpret_cast<const uint16_t *>(W_ik),
-                       reinterpret_cast<uint16_t *>(k_idx), block_table, n_seqs, max_blocks, h.cfg.page_size, n_pages,
-                       row_seq, row_pos, pos0, h.d_err);
-    return hipGetLastError();
+    const int64_t n_tiles = (L + kPRows - 1) / kPRows;
+    const int64_t want = (n_tiles + kPWaves - 1) / kPWaves;
+    const unsigned grid = (unsigned)(want < h.n_cu ? want : h.n_cu);
+    // one instantiation per supported key-row width (k-steps of 16 elements)
+    auto run = [&](auto ks_c) -> hipError_t {
+        constexpr int KS = decltype(ks_c)::value;
+        const size_t lds = (size_t)4 * KS * kWave * 16;  // W_ik as B fragments
+        const void *fn = block_table ? reinterpret_cast<const void *>(project_k_kernel<KS, true>)
+                                     : reinterpret_cast<const void *>(project_k_kernel<KS, false>);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        KernelTimer timer(h, SA_KERNEL_PROJECT, st);
+        hipLaunchKernelGGL((block_table ? project_k_kernel<KS, true> : project_k_kernel<KS, false>), dim3(grid),
+                           dim3(kPThreads), lds, st,
+                           reinterpret_cast<const uint16_t *>(k), L, reinterpret_cast<const uint16_t *>(W_ik),
+                           reinterpret_cast<uint16_t *>(k_idx), block_table, n_seqs, max_blocks, h.cfg.page_size,
+                           n_pages, row_seq, row_pos, pos0, h.d_err);
+        return hipGetLastError();
+    };
+    switch (K) {
+    case 576: return run(std::integral_constant<int, 36>{});  // the latent row
+    case 512: return run(std::integral_constant<int, 32>{});
+    case 256: return run(std::integral_constant<int, 16>{});
+    case 128: return run(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+    }
 }
 
 void destroy_projection_state(sa_handle_s &h)
