@@ -13,6 +13,9 @@ Stable Reinforcement Learning, and Verifiable Synthetic Data"):
   causal mask of the [P1] section 2.5 pseudocode (s <= t visible, else -inf).
 * ``topk`` -- per query the min(k, visible) keys of largest score, ties to the lower
   index, [P1] section 2.3 / 2.5; padded with -1.
+* ``block_topk`` -- the two-tier selection of [P2] "A Guide to Sparse Attention and
+  Efficient Reinforcement Learning in LLM Long-Context Inference", section 1.1: a few
+  fixed-size blocks kept by their best indexer score, then token-level top-k inside them.
 * ``attention_rows`` -- softmax(scale q k_sel^T) v_sel over the selected rows, [P1] section 2.5
   and [P3] section 2.4.
 * ``prefill`` -- the three steps above for chosen query rows of one sequence.
@@ -54,6 +57,8 @@ def _load():
     lib.orc_indexer_scores.restype = None
     lib.orc_topk.argtypes = [P, i64, P, P, i64, i32, P]
     lib.orc_topk.restype = None
+    lib.orc_block_topk.argtypes = [P, i64, P, P, i64, i32, i64, i64, P, P]
+    lib.orc_block_topk.restype = None
     lib.orc_attention.argtypes = [P, P, P, P, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_double, P, P]
     lib.orc_attention.restype = None
@@ -128,6 +133,39 @@ def topk(scores, visible, k_max: int, k_per_row=None) -> np.ndarray:
     return idx
 
 
+def block_topk(scores, visible, k_max: int, block_size: int, n_blocks: int, k_per_row=None,
+               with_blocks: bool = False):
+    """Two-tier (block -> token) selection, [P2] section 1.1.  Block j is the visible tokens
+    s with s // block_size == j; its score is their largest score; the first
+    min(n_blocks, visible blocks) blocks by (block score desc, block index asc) are kept;
+    the first min(k, candidates) of their tokens by (score desc, index asc) are selected.
+    Returns int32 [n_q, k_max] in rank order, -1 padded (and with ``with_blocks`` the kept
+    block indices [n_q, n_blocks] in rank order, -1 padded)."""
+    assert block_size >= 1 and n_blocks >= 1
+    sc = np.ascontiguousarray(np.asarray(scores, dtype=np.float64))
+    if sc.ndim == 1:
+        sc = sc[None, :]
+    n_q, ld = sc.shape
+    vis = np.ascontiguousarray(np.asarray(visible, dtype=np.int64).reshape(n_q))
+    assert np.all(vis <= ld)
+    kpr = None
+    if k_per_row is not None:
+        kpr = np.ascontiguousarray(np.asarray(k_per_row, dtype=np.int32).reshape(n_q))
+        assert np.all(kpr <= k_max)
+    idx = np.empty((n_q, k_max), dtype=np.int32)
+    blocks = np.empty((n_q, n_blocks), dtype=np.int32)
+    _load().orc_block_topk(_ptr(sc), ld, _ptr(vis), _ptr(kpr) if kpr is not None else None,
+                           n_q, int(k_max), int(block_size), int(n_blocks), _ptr(idx), _ptr(blocks))
+    return (idx, blocks) if with_blocks else idx
+
+
+def _select(sc, vis, k_max, k_per_row, blocks):
+    """Flat top-k, or the two-tier selection when ``blocks`` = (block_size, n_blocks)."""
+    if blocks is None:
+        return topk(sc, vis, k_max, k_per_row=k_per_row)
+    return block_topk(sc, vis, k_max, blocks[0], blocks[1], k_per_row=k_per_row)
+
+
 def attention_rows(q, K, V, idx, scale: float, d_v: int | None = None):
     """Softmax attention over the selected rows, [P1] section 2.5 / [P3] section 2.4.
 
@@ -164,11 +202,12 @@ attention = attention_rows
 
 
 def prefill(q, K, V, q_idx, w, k_idx, top_k: int, rows=None, scale: float | None = None,
-            d_v: int | None = None, with_scores: bool = False):
+            d_v: int | None = None, with_scores: bool = False, blocks=None):
     """The whole pipeline of [P1] section 2.5 for query rows ``rows`` of one sequence.
 
     Shapes: q [L,H,d_qk], K [L,H_kv,d_qk], V [L,H_kv,d_v] or None (latent layout, give d_v),
     q_idx [L,H_I,d_I], w [L,H_I], k_idx [L,d_I].  Query row t sees keys s <= t.
+    ``blocks`` = (block_size, n_blocks) selects with the two-tier rule of ``block_topk``.
     Returns dict(rows, scores, abs_scores, idx, out, lse); ``scores`` only if asked."""
     q_idx = _f32(q_idx)
     L = q_idx.shape[0]
@@ -177,7 +216,7 @@ def prefill(q, K, V, q_idx, w, k_idx, top_k: int, rows=None, scale: float | None
     scale = default_scale(d_qk) if scale is None else scale
     vis = rows + 1
     sc, ab = indexer_scores(q_idx[rows], _f32(w)[rows], k_idx, vis, with_abs=True)
-    idx = topk(sc, vis, top_k)
+    idx = _select(sc, vis, top_k, None, blocks)
     out, lse = attention_rows(_f32(q)[rows], K, V, idx, scale, d_v=d_v)
     res = dict(rows=rows, idx=idx, out=out, lse=lse)
     if with_scores:
@@ -200,13 +239,14 @@ def depage(pages, block_table_row, n: int) -> np.ndarray:
 
 def decode(q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len, top_k,
            k_max: int | None = None, seqs=None, scale: float | None = None,
-           d_v: int | None = None, with_scores: bool = False):
+           d_v: int | None = None, with_scores: bool = False, blocks=None):
     """One decode step per sequence against paged caches ([P3] section 2.3).
 
     q [B,H,d_qk], q_idx [B,H_I,d_I], w [B,H_I]; kv_pages [n_pages,P,H_kv,d_qk];
     v_pages [n_pages,P,H_kv,d_v] or None (latent layout: give d_v); kidx_pages
     [n_pages,P,d_I]; block_table [B, max_blocks]; ctx_len [B] (the new token is the last
-    of its n_b visible tokens); top_k int or [B].  Returns dict(seqs, idx [nb,k_max],
+    of its n_b visible tokens); top_k int or [B]; ``blocks`` = (block_size, n_blocks) selects
+    with the two-tier rule of ``block_topk``.  Returns dict(seqs, idx [nb,k_max],
     out, lse) and, if asked, per-sequence score vectors."""
     q = _f32(q)
     B = q.shape[0]
@@ -225,7 +265,7 @@ def decode(q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len, top
         n = int(ctx_len[b])
         kI = _f32(depage(kidx_pages, block_table[b], n))
         sc, ab = indexer_scores(_f32(q_idx)[b:b + 1], _f32(w)[b:b + 1], kI, [n], with_abs=True)
-        idx = topk(sc, [n], k_max, k_per_row=[int(ks[b])])
+        idx = _select(sc, [n], k_max, [int(ks[b])], blocks)
         Kb = _f32(depage(kv_pages, block_table[b], n))
         Vb = None if v_pages is None else _f32(depage(v_pages, block_table[b], n))
         out, lse = attention_rows(q[b:b + 1], Kb, Vb, idx, scale, d_v=d_v)

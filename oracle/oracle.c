@@ -15,6 +15,9 @@
  *        Post-Training" -- section 2.2 (indexer score formula and its design points),
  *        section 2.3 (per-query top-k token selection), section 2.5 (pseudocode of the
  *        indexer -> causal mask -> top-k -> gather -> softmax attention pipeline).
+ *   [P2] "A Guide to Sparse Attention and Efficient Reinforcement Learning in LLM
+ *        Long-Context Inference" -- section 1 (the model keeps multi-head latent
+ *        attention), section 1.1 (two-tier block -> token selection).
  *   [P3] "Long-Context LLMs Explained: Sparse Attention, Stable Reinforcement Learning,
  *        and Verifiable Synthetic Data" -- section 2.2 (two-stage design), section 2.3
  *        (decode reads only the selected k KV entries; composes with paged KV
@@ -121,6 +124,70 @@ void orc_topk(const double *scores,     /* [n_q, ld]                        */
         qsort(c, (size_t)n, sizeof(orc_cand), orc_cand_rank_order);
         for (int64_t r = 0; r < k_max; ++r)
             idx[i * k_max + r] = r < m ? (int32_t)c[r].index : -1;
+        free(c);
+    }
+}
+
+/* ------------------------------------------------------------------------------------
+ * Two-tier (block -> token) selection, [P2] "A Guide to Sparse Attention and Efficient
+ * Reinforcement Learning in LLM Long-Context Inference", section 1.1 (fine-grained token
+ * selection): the history is cut into fixed-size blocks, a few high-value blocks are kept
+ * on the strength of the indexer scores, and token-level selection then runs inside the
+ * kept blocks only.  Readings (the page fixes none of these details):
+ *   - block j holds the tokens s with s / block_size == j (aligned to position 0), and
+ *     only its visible tokens s < visible[i] belong to it, so the last block may be short;
+ *   - a block's score is the largest indexer score among its visible tokens;
+ *   - blocks are ranked by (block score descending, block index ascending) and the first
+ *     min(n_blocks, number of visible blocks) are kept;
+ *   - the candidates are the visible tokens of the kept blocks; they are ranked by
+ *     (score descending, token index ascending) and the first min(k_i, candidates) are
+ *     selected; the remaining k_max slots are -1.
+ * The output row lists the selected indices in rank order.  blocks_out (optional,
+ * [n_q, n_blocks]) receives the kept block indices in rank order, -1 padded.
+ * ---------------------------------------------------------------------------------- */
+void orc_block_topk(const double *scores,     /* [n_q, ld]                       */
+                    int64_t ld,
+                    const int64_t *visible,   /* [n_q]                           */
+                    const int32_t *k_per_row, /* [n_q] or NULL (then k_max each) */
+                    int64_t n_q, int32_t k_max,
+                    int64_t block_size, int64_t n_blocks,
+                    int32_t *idx,             /* [n_q, k_max]                    */
+                    int32_t *blocks_out)      /* [n_q, n_blocks] or NULL         */
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_q; ++i) {
+        int64_t n = visible[i];
+        int64_t k = k_per_row ? k_per_row[i] : k_max;
+        int64_t n_blk = (n + block_size - 1) / block_size;
+        int64_t kept = n_blocks < n_blk ? n_blocks : n_blk;
+        orc_cand *blk = (orc_cand *)malloc((size_t)(n_blk > 0 ? n_blk : 1) * sizeof(orc_cand));
+        char *chosen = (char *)calloc((size_t)(n_blk > 0 ? n_blk : 1), 1);
+        orc_cand *c = (orc_cand *)malloc((size_t)(n > 0 ? n : 1) * sizeof(orc_cand));
+        for (int64_t j = 0; j < n_blk; ++j) {
+            double best = -INFINITY;
+            for (int64_t s = j * block_size; s < (j + 1) * block_size && s < n; ++s)
+                if (scores[i * ld + s] > best) best = scores[i * ld + s];
+            blk[j].score = best;
+            blk[j].index = j;
+        }
+        qsort(blk, (size_t)n_blk, sizeof(orc_cand), orc_cand_rank_order);
+        for (int64_t r = 0; r < kept; ++r) chosen[blk[r].index] = 1;
+        if (blocks_out)
+            for (int64_t r = 0; r < n_blocks; ++r)
+                blocks_out[i * n_blocks + r] = r < kept ? (int32_t)blk[r].index : -1;
+        int64_t n_c = 0;
+        for (int64_t s = 0; s < n; ++s) {
+            if (!chosen[s / block_size]) continue;
+            c[n_c].score = scores[i * ld + s];
+            c[n_c].index = s;
+            ++n_c;
+        }
+        qsort(c, (size_t)n_c, sizeof(orc_cand), orc_cand_rank_order);
+        int64_t m = k < n_c ? k : n_c;
+        for (int64_t r = 0; r < k_max; ++r)
+            idx[i * k_max + r] = r < m ? (int32_t)c[r].index : -1;
+        free(blk);
+        free(chosen);
         free(c);
     }
 }

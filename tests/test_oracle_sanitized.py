@@ -1,6 +1,6 @@
 """The oracle's C code under AddressSanitizer and UndefinedBehaviorSanitizer (host only).
 
-A small C driver calls orc_indexer_scores, orc_topk and orc_attention on edge cases (a single
+A small C driver calls orc_indexer_scores, orc_topk, orc_block_topk and orc_attention on edge cases (a single
 visible key, k larger than the visible count, -1 padding in the index rows, a shared latent row
 as well as a separate V, grouped kv heads) and checks a few facts the definitions fix; the whole
 program is built with gcc -fsanitize=address,undefined, so any out-of-bounds access, leak or
@@ -24,6 +24,9 @@ void orc_indexer_scores(const float *q, const float *w, const float *k, const in
                         int64_t n_q, int64_t n_k, int H_I, int d_I, double *out, double *abs_out);
 void orc_topk(const double *scores, int64_t ld, const int64_t *visible, const int32_t *k_per_row,
               int64_t n_q, int32_t k_max, int32_t *idx);
+void orc_block_topk(const double *scores, int64_t ld, const int64_t *visible, const int32_t *k_per_row,
+                    int64_t n_q, int32_t k_max, int64_t block_size, int64_t n_blocks, int32_t *idx,
+                    int32_t *blocks_out);
 void orc_attention(const float *q, const float *K, const float *V, const int32_t *idx, int64_t idx_ld,
                    int64_t n_q, int64_t n_k, int H, int H_kv, int d_qk, int d_v, double scale,
                    double *out, double *lse);
@@ -59,6 +62,29 @@ static int run_case(int64_t n_q, int64_t n_k, int H_I, int d_I, int k_max, int H
             }
         }
     }
+    /* two-tier selection: blocks of 3 tokens (a short last block on most rows), more blocks
+       asked for than some rows have */
+    int32_t *blk = malloc((size_t)(n_q * 4) * sizeof(int32_t));
+    for (int per_row = 0; per_row < 2; ++per_row) {
+        orc_block_topk(s, n_k, vis, per_row ? kr : NULL, n_q, k_max, 3, 4, idx, blk);
+        for (int64_t i = 0; i < n_q; ++i) {
+            int64_t n_blk = (vis[i] + 2) / 3, kept = n_blk < 4 ? n_blk : 4;
+            for (int r = 0; r < 4; ++r) {
+                int32_t b = blk[i * 4 + r];
+                if (r < kept) CHECK(b >= 0 && b < n_blk); else CHECK(b == -1);
+            }
+            int nsel = 0;
+            for (int r = 0; r < k_max; ++r) {
+                int32_t v = idx[i * k_max + r];
+                if (v < 0) { CHECK(v == -1); continue; }
+                CHECK(v < vis[i]);
+                ++nsel;
+            }
+            CHECK(nsel >= 1);
+        }
+    }
+    free(blk);
+    orc_topk(s, n_k, vis, NULL, n_q, k_max, idx);
     float *q = randv((size_t)(n_q * H * d_qk)), *K = randv((size_t)(n_k * H_kv * d_qk));
     float *V = sep_v ? randv((size_t)(n_k * H_kv * d_v)) : NULL;
     double *o = malloc((size_t)(n_q * H * d_v) * sizeof(double)), *lse = malloc((size_t)(n_q * H) * sizeof(double));
