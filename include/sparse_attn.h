@@ -87,6 +87,8 @@ typedef struct {
 #define SA_OP_DECODE  2  /* n = B (batch), max_ctx = upper bound of every ctx_len[b]     */
 #define SA_OP_TOPK    3  /* n = rows, max_ctx = cols                                      */
 #define SA_OP_PROJECT 4  /* n = L rows of indexer_project_q, max_ctx ignored              */
+#define SA_OP_PREFILL_BLOCKS 5  /* sparse_attn_prefill_blocks: n = L, max_ctx ignored     */
+#define SA_OP_DECODE_BLOCKS  6  /* sparse_attn_decode_blocks: as SA_OP_DECODE             */
 
 /* Create a handle for one configuration.  Validates the config, allocates the 4-byte
  * device error word on the current device (the only device allocation the library makes)
@@ -136,6 +138,26 @@ sa_status_t topk_select(sa_handle_t h, const float *scores, int64_t rows, int64_
                         const int32_t *valid_len, const int32_t *k_per_row, int32_t k,
                         int32_t *idx, void *stream);
 
+/* Two-tier (block -> token) selection of a score matrix -- "A Guide to Sparse Attention and
+ * Efficient Reinforcement Learning in LLM Long-Context Inference", section 1.1 (fine-grained
+ * token selection: the history is cut into fixed-size blocks, a few high-value blocks are kept
+ * by their indexer scores, and token-level selection runs inside the kept blocks only).  Row r
+ * (candidates scores[r, 0 .. valid(r)), valid and k(r) as in topk_select):
+ *   1. block j is the tokens s < valid(r) with s / block_size == j (the last may be short);
+ *      its score is the largest score among them;
+ *   2. the first min(n_blocks, blocks) blocks by (block score desc, block index asc) are kept;
+ *   3. idx row r gets the min(k(r), tokens in the kept blocks) tokens of the kept blocks with
+ *      the largest scores (ties -> lower index), ascending, then -1 padding to width k.
+ * With n_blocks >= k the result equals topk_select's.
+ *   block_size  a power of two in [1, 1024]
+ *   n_blocks    1 <= n_blocks <= 2048, n_blocks * block_size <= 16384
+ * Scores must not be NaN.  Needs no workspace.
+ * Errors: those of topk_select; SA_ERR_INVALID_ARG for block_size / n_blocks out of range;
+ * SA_ERR_UNSUPPORTED if n_blocks * block_size > 16384 or cols / block_size > 16384. */
+sa_status_t topk_select_blocks(sa_handle_t h, const float *scores, int64_t rows, int64_t cols, int64_t ld,
+                               const int32_t *valid_len, const int32_t *k_per_row, int32_t k,
+                               int32_t block_size, int32_t n_blocks, int32_t *idx, void *stream);
+
 /* Causal prefill of one sequence: indexer -> per-query top-k -> attention over the
  * selected rows -- the whole pipeline of "Sparse Attention and RL Optimization...",
  * section 2.5 and "Long-Context LLMs Explained...", section 2.4.  Scores are produced
@@ -154,6 +176,18 @@ sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, con
                                 const void *q_idx, const float *w, const void *k_idx, int64_t L,
                                 int32_t topk, float *out, float *lse, int32_t *idx_out,
                                 void *ws, size_t ws_bytes, void *stream);
+
+/* sparse_attn_prefill with the two-tier selection of topk_select_blocks in place of the
+ * per-query top-k ("A Guide to Sparse Attention and Efficient Reinforcement Learning in LLM
+ * Long-Context Inference", section 1.1); every other argument as in sparse_attn_prefill.  The
+ * scores of each block of query rows are materialised in the workspace, which must hold at
+ * least sparse_attn_workspace_size(SA_OP_PREFILL_BLOCKS, L) bytes.  A row attends to fewer than
+ * min(topk, t + 1) tokens when the kept blocks hold fewer; its idx_out row is -1 padded.
+ * Errors: those of sparse_attn_prefill and topk_select_blocks (with cols = L). */
+sa_status_t sparse_attn_prefill_blocks(sa_handle_t h, const void *q, const void *k, const void *v,
+                                       const void *q_idx, const float *w, const void *k_idx, int64_t L,
+                                       int32_t topk, int32_t block_size, int32_t n_blocks, float *out,
+                                       float *lse, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
 /* One decode step for B sequences against paged caches -- "Long-Context LLMs
  * Explained...", section 2.3: the indexer scores the whole cached context, and attention
@@ -180,6 +214,20 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
                                const int32_t *ctx_len, const int32_t *topk, int32_t B,
                                int32_t max_ctx, float *out, float *lse, int32_t *idx_out,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* sparse_attn_decode with the two-tier selection of topk_select_blocks in place of the
+ * per-sequence top-k ("A Guide to Sparse Attention and Efficient Reinforcement Learning in LLM
+ * Long-Context Inference", section 1.1): blocks are aligned to logical token 0, so with
+ * block_size = page_size a block is one page of the sequence.  Every other argument as in
+ * sparse_attn_decode; the workspace is sparse_attn_workspace_size(SA_OP_DECODE_BLOCKS, B,
+ * max_ctx) bytes.  Errors: those of sparse_attn_decode and topk_select_blocks (with
+ * cols = max_ctx). */
+sa_status_t sparse_attn_decode_blocks(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                      const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                      const int32_t *ctx_len, const int32_t *topk, int32_t B,
+                                      int32_t max_ctx, int32_t block_size, int32_t n_blocks, float *out,
+                                      float *lse, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Index-space projections -- the first lines of the "Sparse Attention and RL Optimization...",
  * section 2.5 pseudocode: the index query and key are linear maps of the attention query and

@@ -12,7 +12,9 @@ ReLU(q(t,j).k(s)) ("Sparse Attention and RL Optimization: Three Technical Breakt
 LLM Post-Training", section 2.2); each query keeps the top-k tokens (section 2.3) and runs
 softmax attention over only those KV rows (section 2.5; for decode over a paged cache,
 "Long-Context LLMs Explained: Sparse Attention, Stable Reinforcement Learning, and
-Verifiable Synthetic Data", section 2.3).
+Verifiable Synthetic Data", section 2.3).  The ``*_blocks`` variants select with the two-tier
+block -> token rule of "A Guide to Sparse Attention and Efficient Reinforcement Learning in
+LLM Long-Context Inference", section 1.1.
 """
 from __future__ import annotations
 
@@ -25,13 +27,14 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_DEVICE_CHECK = range(6)
 SA_F32, SA_BF16 = 0, 1
-SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK, SA_OP_PROJECT = 1, 2, 3, 4
+SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK, SA_OP_PROJECT, SA_OP_PREFILL_BLOCKS, SA_OP_DECODE_BLOCKS = 1, 2, 3, 4, 5, 6
 SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK = 1, 2, 4, 8
 
 # Every symbol include/sparse_attn.h declares.
 EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error",
             "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
-            "sparse_attn_prefill", "sparse_attn_decode", "indexer_project_q", "indexer_project_k",
+            "topk_select_blocks", "sparse_attn_prefill", "sparse_attn_prefill_blocks", "sparse_attn_decode",
+            "sparse_attn_decode_blocks", "indexer_project_q", "indexer_project_k",
             "sparse_attn_profile", "sparse_attn_profile_read")
 KERNEL_KINDS = ("indexer", "topk", "attention", "merge", "project")
 
@@ -92,8 +95,12 @@ def load_library() -> ctypes.CDLL:
         "sparse_attn_check": ([P, P, ctypes.POINTER(ctypes.c_uint32)], st),
         "indexer_scores": ([P, P, P, P, i64, P, P], st),
         "topk_select": ([P, P, i64, i64, i64, P, P, i32, P, P], st),
+        "topk_select_blocks": ([P, P, i64, i64, i64, P, P, i32, i32, i32, P, P], st),
         "sparse_attn_prefill": ([P, P, P, P, P, P, P, i64, i32, P, P, P, P, sz, P], st),
+        "sparse_attn_prefill_blocks": ([P, P, P, P, P, P, P, i64, i32, i32, i32, P, P, P, P, sz, P], st),
         "sparse_attn_decode": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, P, P, P, P, sz, P], st),
+        "sparse_attn_decode_blocks": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, sz,
+                                       P], st),
         "indexer_project_q": ([P, P, i64, P, P, P, P, P, sz, P], st),
         "indexer_project_k": ([P, P, i64, P, P, P, i32, i32, i64, P, P, i64, P], st),
         "sparse_attn_profile": ([P, ctypes.c_int], st),
@@ -202,6 +209,17 @@ def topk_select(h: Handle, scores, k: int, idx, valid_len=None, k_per_row=None, 
                                              _ptr(k_per_row), int(k), _ptr(idx), _stream(stream)))
 
 
+def topk_select_blocks(h: Handle, scores, k: int, block_size: int, n_blocks: int, idx, valid_len=None,
+                       k_per_row=None, cols=None, stream=None) -> None:
+    """Two-tier selection: n_blocks blocks of block_size tokens kept by their best score, then the
+    top-k tokens inside them."""
+    rows, ld = scores.shape
+    cols = ld if cols is None else cols
+    _check(h.ptr, load_library().topk_select_blocks(h.ptr, _ptr(scores), rows, cols, ld, _ptr(valid_len),
+                                                    _ptr(k_per_row), int(k), int(block_size), int(n_blocks),
+                                                    _ptr(idx), _stream(stream)))
+
+
 def sparse_attn_prefill(h: Handle, q, k, v, q_idx, w, k_idx, topk: int, out, lse=None,
                         idx_out=None, ws=None, stream=None) -> None:
     L = q.shape[0]
@@ -209,6 +227,28 @@ def sparse_attn_prefill(h: Handle, q, k, v, q_idx, w, k_idx, topk: int, out, lse
     _check(h.ptr, load_library().sparse_attn_prefill(
         h.ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(w), _ptr(k_idx), L, int(topk), _ptr(out),
         _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_prefill_blocks(h: Handle, q, k, v, q_idx, w, k_idx, topk: int, block_size: int, n_blocks: int,
+                               out, lse=None, idx_out=None, ws=None, stream=None) -> None:
+    L = q.shape[0]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(h.ptr, load_library().sparse_attn_prefill_blocks(
+        h.ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(w), _ptr(k_idx), L, int(topk), int(block_size),
+        int(n_blocks), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_decode_blocks(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len,
+                              topk, max_ctx: int, block_size: int, n_blocks: int, out, lse=None, idx_out=None,
+                              ws=None, stream=None) -> None:
+    B = q.shape[0]
+    n_pages = kv_pages.shape[0]
+    max_blocks = block_table.shape[1]
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(h.ptr, load_library().sparse_attn_decode_blocks(
+        h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
+        _ptr(block_table), max_blocks, _ptr(ctx_len), _ptr(topk), B, int(max_ctx), int(block_size),
+        int(n_blocks), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def sparse_attn_decode(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len,

@@ -72,11 +72,11 @@ struct PrefillLayout {
 };
 
 // Fast path (bf16, 64 x 128 indexer): [idx | fused indexer/top-k workspace].
-// Generic path: [scores of one block of query rows | idx].
-PrefillLayout prefill_layout(const sa_handle_s &h, int64_t L)
+// Generic path, and every two-tier selection: [scores of one block of query rows | idx].
+PrefillLayout prefill_layout(const sa_handle_s &h, int64_t L, bool chunked = false)
 {
     PrefillLayout p;
-    if (h.fast_indexer) {
+    if (h.fast_indexer && !chunked) {
         p.idx = 0;
         p.scores = align_up((size_t)L * (size_t)h.cfg.max_topk * sizeof(int32_t));
         p.total = p.scores + align_up(sa::prefill_topk_workspace(h, L));
@@ -104,6 +104,37 @@ DecodeLayout decode_layout(const sa_handle_s &h, int64_t B, int64_t max_ctx)
     d.total = d.attn + align_up(sa::attention_workspace(h, B, true));
     return d;
 }
+
+// Two-tier (block -> token) selection parameters; nullptr selects plain per-query top-k.
+struct BlockSelect {
+    int32_t block_size, n_blocks;
+};
+
+sa_status_t check_block_select(sa_handle_t h, const BlockSelect &b, int64_t cols)
+{
+    const int32_t bs = b.block_size;
+    if (bs < 1 || bs > 1024 || (bs & (bs - 1)) != 0)
+        return fail(h, SA_ERR_INVALID_ARG, "block_size (%d) must be a power of two in [1, 1024]", bs);
+    if (b.n_blocks < 1 || b.n_blocks > sa::kBlockSelectMaxKept)
+        return fail(h, SA_ERR_INVALID_ARG, "n_blocks (%d) must be in [1, %d]", b.n_blocks, sa::kBlockSelectMaxKept);
+    if ((int64_t)b.n_blocks * bs > sa::kBlockSelectMaxItems)
+        return fail(h, SA_ERR_UNSUPPORTED, "n_blocks * block_size (%lld) exceeds %d candidate tokens",
+                    (long long)b.n_blocks * bs, sa::kBlockSelectMaxItems);
+    if ((cols + bs - 1) / bs > sa::kBlockSelectMaxItems)
+        return fail(h, SA_ERR_UNSUPPORTED, "%lld tokens make more than %d blocks of %d", (long long)cols,
+                    sa::kBlockSelectMaxItems, bs);
+    return SA_OK;
+}
+
+sa_status_t prefill_impl(sa_handle_t h, const void *q, const void *k, const void *v, const void *q_idx,
+                         const float *w, const void *k_idx, int64_t L, int32_t topk, const BlockSelect *blocks,
+                         float *out, float *lse, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const float *w, const void *kv_pages,
+                        const void *v_pages, const void *kidx_pages, int64_t n_pages, const int32_t *block_table,
+                        int32_t max_blocks, const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                        const BlockSelect *blocks, float *out, float *lse, int32_t *idx_out, void *ws,
+                        size_t ws_bytes, void *stream);
 
 }  // namespace
 
@@ -274,10 +305,12 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
     if (n < 1) return fail(h, SA_ERR_INVALID_ARG, "n must be >= 1");
     switch (op) {
     case SA_OP_PREFILL:
+    case SA_OP_PREFILL_BLOCKS:
         if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "L exceeds int32 token indices");
-        *bytes = prefill_layout(*h, n).total;
+        *bytes = prefill_layout(*h, n, op == SA_OP_PREFILL_BLOCKS).total;
         return SA_OK;
     case SA_OP_DECODE:
+    case SA_OP_DECODE_BLOCKS:
         if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
         *bytes = decode_layout(*h, n, max_ctx).total;
         return SA_OK;
@@ -349,10 +382,75 @@ sa_status_t topk_select(sa_handle_t h, const float *scores, int64_t rows, int64_
                       "top-k launch");
 }
 
+sa_status_t topk_select_blocks(sa_handle_t h, const float *scores, int64_t rows, int64_t cols, int64_t ld,
+                               const int32_t *valid_len, const int32_t *k_per_row, int32_t k, int32_t block_size,
+                               int32_t n_blocks, int32_t *idx, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!scores || !idx) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (rows < 1 || cols < 1) return fail(h, SA_ERR_INVALID_ARG, "rows and cols must be >= 1");
+    if (cols > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "cols exceeds int32 indices");
+    if (rows > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "rows exceeds the launch limit");
+    if (ld < cols) return fail(h, SA_ERR_INVALID_ARG, "ld (%lld) < cols (%lld)", (long long)ld, (long long)cols);
+    if (k < 1 || k > h->cfg.max_topk)
+        return fail(h, SA_ERR_INVALID_ARG, "k (%d) must be in [1, max_topk=%d]", k, h->cfg.max_topk);
+    sa_status_t s = check_block_select(h, BlockSelect{block_size, n_blocks}, cols);
+    if (s != SA_OK) return s;
+    s = check_device(h);
+    if (s != SA_OK) return s;
+    return hip_status(h, sa::launch_block_topk(*h, scores, ld, rows, cols, valid_len, 0, k_per_row, k, block_size,
+                                               n_blocks, idx, k, h->d_err, reinterpret_cast<hipStream_t>(stream)),
+                      "block top-k launch");
+}
+
 sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, const void *v,
                                 const void *q_idx, const float *w, const void *k_idx, int64_t L,
                                 int32_t topk, float *out, float *lse, int32_t *idx_out, void *ws,
                                 size_t ws_bytes, void *stream)
+{
+    return prefill_impl(h, q, k, v, q_idx, w, k_idx, L, topk, nullptr, out, lse, idx_out, ws, ws_bytes, stream);
+}
+
+sa_status_t sparse_attn_prefill_blocks(sa_handle_t h, const void *q, const void *k, const void *v,
+                                       const void *q_idx, const float *w, const void *k_idx, int64_t L,
+                                       int32_t topk, int32_t block_size, int32_t n_blocks, float *out, float *lse,
+                                       int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    const BlockSelect b{block_size, n_blocks};
+    return prefill_impl(h, q, k, v, q_idx, w, k_idx, L, topk, &b, out, lse, idx_out, ws, ws_bytes, stream);
+}
+
+sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                               const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                               const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                               float *out, float *lse, int32_t *idx_out, void *ws, size_t ws_bytes,
+                               void *stream)
+{
+    return decode_impl(h, q, q_idx, w, kv_pages, v_pages, kidx_pages, n_pages, block_table, max_blocks, ctx_len,
+                       topk, B, max_ctx, nullptr, out, lse, idx_out, ws, ws_bytes, stream);
+}
+
+sa_status_t sparse_attn_decode_blocks(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                      const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                      const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                                      int32_t block_size, int32_t n_blocks, float *out, float *lse,
+                                      int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    const BlockSelect b{block_size, n_blocks};
+    return decode_impl(h, q, q_idx, w, kv_pages, v_pages, kidx_pages, n_pages, block_table, max_blocks, ctx_len,
+                       topk, B, max_ctx, &b, out, lse, idx_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+sa_status_t prefill_impl(sa_handle_t h, const void *q, const void *k, const void *v, const void *q_idx,
+                         const float *w, const void *k_idx, int64_t L, int32_t topk, const BlockSelect *blocks,
+                         float *out, float *lse, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
 {
     if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
     h->last_error.clear();
@@ -366,7 +464,11 @@ sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, con
         return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
     if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(q_idx) || !aligned16(k_idx))
         return fail(h, SA_ERR_INVALID_ARG, "q, k, v, q_idx and k_idx must be 16-byte aligned");
-    const PrefillLayout lay = prefill_layout(*h, L);
+    if (blocks) {
+        const sa_status_t sb = check_block_select(h, *blocks, L);
+        if (sb != SA_OK) return sb;
+    }
+    const PrefillLayout lay = prefill_layout(*h, L, blocks != nullptr);
     if (!ws || ws_bytes < lay.total)
         return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
     sa_status_t s = check_device(h);
@@ -377,7 +479,7 @@ sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, con
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
     const size_t es = elem_size(*h);
 
-    if (h->fast_indexer) {
+    if (h->fast_indexer && !blocks) {
         // fused indexer + streaming top-k: no score matrix at all
         s = hip_status(h, sa::launch_prefill_topk(*h, q_idx, w, k_idx, L, topk, idx, base + lay.scores, st),
                        "indexer/top-k launch");
@@ -394,9 +496,15 @@ sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, con
                                                  w + r0 * c.n_idx_heads, rows, keys, vis, scores, cols, cols, st),
                            "indexer launch");
             if (s != SA_OK) return s;
-            s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
-                                              idx + r0 * topk, topk, h->d_err, st),
-                           "top-k launch");
+            if (blocks)
+                s = hip_status(h, sa::launch_block_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
+                                                        blocks->block_size, blocks->n_blocks, idx + r0 * topk,
+                                                        topk, h->d_err, st),
+                               "block top-k launch");
+            else
+                s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
+                                                  idx + r0 * topk, topk, h->d_err, st),
+                               "top-k launch");
             if (s != SA_OK) return s;
         }
     }
@@ -408,12 +516,11 @@ sa_status_t sparse_attn_prefill(sa_handle_t h, const void *q, const void *k, con
                       "attention launch");
 }
 
-sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, const float *w,
-                               const void *kv_pages, const void *v_pages, const void *kidx_pages,
-                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
-                               const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
-                               float *out, float *lse, int32_t *idx_out, void *ws, size_t ws_bytes,
-                               void *stream)
+sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const float *w, const void *kv_pages,
+                        const void *v_pages, const void *kidx_pages, int64_t n_pages, const int32_t *block_table,
+                        int32_t max_blocks, const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                        const BlockSelect *blocks, float *out, float *lse, int32_t *idx_out, void *ws,
+                        size_t ws_bytes, void *stream)
 {
     if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
     h->last_error.clear();
@@ -432,6 +539,10 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
     if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
         (v_pages && !aligned16(v_pages)))
         return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+    if (blocks) {
+        const sa_status_t sb = check_block_select(h, *blocks, max_ctx);
+        if (sb != SA_OK) return sb;
+    }
     const DecodeLayout lay = decode_layout(*h, B, max_ctx);
     if (!ws || ws_bytes < lay.total)
         return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
@@ -443,7 +554,27 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
 
     sa::Visibility vis{0, ctx_len, max_ctx};
-    if (h->fast_decode) {
+    if (blocks) {
+        // scores of every cached token, then the two-tier selection per sequence
+        int64_t ld = max_ctx;
+        if (h->fast_decode) {
+            const sa::DecodeTopkLayout dl = sa::decode_topk_layout(B, max_ctx);
+            s = hip_status(h, sa::launch_decode_indexer(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks,
+                                                        ctx_len, B, max_ctx, base + lay.scores, st),
+                           "decode indexer launch");
+            scores = reinterpret_cast<float *>(base + lay.scores + dl.scores);
+            ld = dl.ld;
+        } else {
+            sa::RowSource keys{kidx_pages, c.d_idx, block_table, max_blocks, c.page_size, n_pages};
+            s = hip_status(h, sa::launch_indexer(*h, q_idx, w, B, keys, vis, scores, max_ctx, max_ctx, st),
+                           "indexer launch");
+        }
+        if (s != SA_OK) return s;
+        s = hip_status(h, sa::launch_block_topk(*h, scores, ld, B, max_ctx, ctx_len, 0, topk, c.max_topk,
+                                                blocks->block_size, blocks->n_blocks, idx, c.max_topk, h->d_err, st),
+                       "block top-k launch");
+        if (s != SA_OK) return s;
+    } else if (h->fast_decode) {
         s = hip_status(h, sa::launch_decode_indexer_topk(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks,
                                                          ctx_len, topk, B, max_ctx, idx, base + lay.scores, st),
                        "decode indexer/top-k launch");
@@ -464,6 +595,10 @@ sa_status_t sparse_attn_decode(sa_handle_t h, const void *q, const void *q_idx, 
     return hip_status(h, sa::launch_attention(*h, q, B, kv, vv, vis, sel, out, lse, base + lay.attn, st),
                       "attention launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const void *W_iq, const void *W_w,
                               void *q_idx, float *w, void *ws, size_t ws_bytes, void *stream)

@@ -356,16 +356,14 @@ DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
     return l;
 }
 
-hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
-                                      int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
-                                      const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
-                                      int32_t *idx, void *ws, hipStream_t st)
+hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                 int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, void *ws, hipStream_t st)
 {
     const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
     char *base = reinterpret_cast<char *>(ws);
     float *scores = reinterpret_cast<float *>(base + l.scores);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base + l.hist);
-    const int32_t max_topk = h.cfg.max_topk;
     {
         const int64_t nz = (int64_t)B * kBins;
         hipLaunchKernelGGL(decode_reset_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist,
@@ -383,6 +381,22 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                      const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
+                                      int32_t *idx, void *ws, hipStream_t st)
+{
+    hipError_t e = launch_decode_indexer(h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks, ctx_len, B,
+                                         max_ctx, ws, st);
+    if (e != hipSuccess) return e;
+    const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
+    char *base = reinterpret_cast<char *>(ws);
+    const float *scores = reinterpret_cast<const float *>(base + l.scores);
+    const uint32_t *hist = reinterpret_cast<const uint32_t *>(base + l.hist);
+    const int32_t max_topk = h.cfg.max_topk;
     KernelTimer timer(h, SA_KERNEL_TOPK, st);
     hipLaunchKernelGGL(decode_topk_kernel, dim3((unsigned)B), dim3(kTopkThreads), 0, st, scores, l.ld, ctx_len,
                        max_ctx, topk_b, max_topk, hist, idx, h.d_err);

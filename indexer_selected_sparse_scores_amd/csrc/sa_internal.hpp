@@ -81,6 +81,19 @@ hipError_t launch_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t 
                        const int32_t *valid_len, int64_t causal_row0, const int32_t *k_per_row,
                        int32_t k, int32_t *idx, int64_t idx_ld, uint32_t *err, hipStream_t st);
 
+// ---- two-tier (block -> token) selection over materialised scores ------------------------
+// Rows as in launch_topk.  Blocks of block_size tokens (a power of two, <= 1024) are ranked by
+// their best score, the first min(n_blocks, blocks) are kept, and the min(k(r), candidates)
+// best tokens inside them are written ascending, -1 padded to idx_ld.  The host guarantees
+// ceil(cols / block_size) <= kBlockSelectMaxItems, n_blocks <= kBlockSelectMaxKept and
+// n_blocks * block_size <= kBlockSelectMaxItems (everything is held in LDS).
+constexpr int kBlockSelectMaxItems = 16384;
+constexpr int kBlockSelectMaxKept = 2048;
+hipError_t launch_block_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t rows, int64_t cols,
+                             const int32_t *valid_len, int64_t causal_row0, const int32_t *k_per_row, int32_t k,
+                             int32_t block_size, int32_t n_blocks, int32_t *idx, int64_t idx_ld, uint32_t *err,
+                             hipStream_t st);
+
 // ---- attention over selected rows --------------------------------------------------------
 // Query row r attends to the first m(r) = min(k(r), visible(r)) entries of idx row r.
 struct Selection {
@@ -111,6 +124,12 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
                                       int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
                                       const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
                                       int32_t *idx, void *ws, hipStream_t st);
+
+// The paged decode indexer alone: sequence b's scores land at ws + layout.scores, row stride
+// layout.ld (floats), for tokens s < ctx_len[b].
+hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                 int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, void *ws, hipStream_t st);
 
 // ---- index-space projections (bf16) ---------------------------------------------------
 size_t projection_workspace();

@@ -8,6 +8,11 @@ Tolerances (bf16 inputs, fp32 accumulation):
     within 1e-3 relative of the oracle's m-th score.
   * attention outputs: within 2e-3 absolute of the oracle evaluated on the GPU's own
     selection (after the top-k check passed); LSE within 2e-3 absolute as well.
+  * two-tier (block -> token) sets: bit-exact, except where the oracle's kept-block boundary
+    (its last kept and first dropped block scores) or its token boundary (m-th and (m+1)-th
+    candidate scores) is a near-tie at 1e-3 relative; then every index in the symmetric
+    difference must be a near-tie of the token boundary or lie in a block whose score is a
+    near-tie of the block boundary.
 """
 from __future__ import annotations
 
@@ -66,6 +71,48 @@ def check_topk_row(gpu_row, ref_scores: np.ndarray, m: int, visible: int, what="
     for s in G ^ O:
         assert abs(sc[s] - tau) <= TIE_REL * max(abs(tau), abs(sc[s])) or sc[s] == tau, \
             f"{what}: index {s} (score {sc[s]}) is not a near-tie of {tau}"
+    return len(G ^ O)
+
+
+def _near(a, b):
+    return a == b or abs(a - b) <= TIE_REL * max(abs(a), abs(b))
+
+
+def check_block_topk_row(gpu_row, ref_scores: np.ndarray, visible: int, k: int, block_size: int,
+                         n_blocks: int, what=""):
+    """Two-tier selection of one row against the oracle's block_topk on the oracle's scores.
+    Returns the size of the (near-tie) symmetric difference."""
+    g = np.asarray(gpu_row)
+    sel = g[g >= 0]
+    sc = np.asarray(ref_scores[:visible], dtype=np.float64)
+    ref, kept = oracle.block_topk(sc, [visible], len(g), block_size, n_blocks, k_per_row=[k],
+                                  with_blocks=True)
+    O = set(int(x) for x in ref[0] if x >= 0)
+    assert len(np.unique(sel)) == len(sel), f"{what}: duplicate indices"
+    assert len(sel) == 0 or (sel.min() >= 0 and sel.max() < visible), f"{what}: index out of range"
+    G = set(sel.tolist())
+    assert np.all(g[len(sel):] == -1), f"{what}: padding is not -1"
+    if G == O:
+        return 0
+    n_blk = -(-visible // block_size)
+    bmax = np.array([sc[j * block_size:(j + 1) * block_size].max() for j in range(n_blk)])
+    kept = [int(b) for b in kept[0] if b >= 0]
+    tau_b = bmax[kept[-1]]
+    dropped = np.setdiff1d(np.arange(n_blk), kept)
+    tau_b2 = bmax[dropped].max() if len(dropped) else -np.inf
+    cands = np.array([s for s in range(visible) if s // block_size in set(kept)])
+    order = cands[np.lexsort((cands, -sc[cands]))]
+    m = len(O)
+    tau = sc[order[m - 1]]
+    tau2 = sc[order[m]] if m < len(order) else -np.inf
+    block_tie, token_tie = _near(tau_b, tau_b2), _near(tau, tau2)
+    assert block_tie or token_tie, (f"{what}: sets differ without a near-tie (blocks {tau_b} / {tau_b2}, "
+                                    f"tokens {tau} / {tau2})")
+    if not block_tie:
+        assert len(G) == len(O), f"{what}: {len(G)} selected, expected {len(O)}"
+    for s in G ^ O:
+        ok = (token_tie and _near(sc[s], tau)) or (block_tie and _near(bmax[s // block_size], tau_b))
+        assert ok, f"{what}: index {s} (score {sc[s]}) is not a near-tie of a selection boundary"
     return len(G ^ O)
 
 

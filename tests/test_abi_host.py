@@ -67,6 +67,11 @@ def test_create_null_arguments():
     assert lib.indexer_scores(None, None, None, None, 1, None, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_prefill(None, *([None] * 6), 1, 1, None, None, None, None, 0, None) \
         == sa.SA_ERR_INVALID_ARG
+    assert lib.topk_select_blocks(None, None, 1, 1, 1, None, None, 1, 64, 1, None, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_prefill_blocks(None, *([None] * 6), 1, 1, 64, 1, None, None, None, None, 0, None) \
+        == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_decode_blocks(None, *([None] * 6), 1, None, 1, None, None, 1, 1, 64, 1, None, None,
+                                         None, None, 0, None) == sa.SA_ERR_INVALID_ARG
     size = ctypes.c_size_t()
     assert lib.sparse_attn_workspace_size(None, 1, 1, 1, ctypes.byref(size)) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_last_error(None)

@@ -162,3 +162,31 @@ def test_pipeline_with_blocks_equals_attention_on_its_selection():
     full = oracle.prefill(q, K, V, q_idx, w, k_idx, 6, blocks=(4, 10))
     flat = oracle.prefill(q, K, V, q_idx, w, k_idx, 6)
     np.testing.assert_array_equal(full["idx"], flat["idx"])
+
+
+def test_parity_checker_accepts_the_oracle_and_rejects_planted_mistakes():
+    """The GPU tests' two-tier checker (tests/parity.py) passes the oracle's own selection and
+    fails a selection with a planted mistake: a token swapped for an unselected candidate, a
+    kept block swapped for a dropped one, a duplicate."""
+    import pytest
+
+    from tests.parity import check_block_topk_row
+    r = np.random.default_rng(27)
+    row = r.standard_normal(500)
+    idx = oracle.block_topk(row, [500], 40, 16, 4)[0]
+    assert check_block_topk_row(np.sort(idx), row, 500, 40, 16, 4) == 0
+    sel = set(int(x) for x in idx)
+    _, kept = oracle.block_topk(row, [500], 40, 16, 4, with_blocks=True)
+    kept = set(int(b) for b in kept[0])
+    cands = [s for s in range(500) if s // 16 in kept and s not in sel]
+    swapped = np.sort(np.array(sorted(sel - {int(idx[-1])}) + [cands[0]]))
+    with pytest.raises(AssertionError):
+        check_block_topk_row(swapped, row, 500, 40, 16, 4)
+    outside = [s for s in range(500) if s // 16 not in kept]
+    moved = np.sort(np.array(sorted(sel - {int(idx[0])}) + [outside[0]]))
+    with pytest.raises(AssertionError):
+        check_block_topk_row(moved, row, 500, 40, 16, 4)
+    dup = np.sort(idx.copy())
+    dup[1] = dup[0]
+    with pytest.raises(AssertionError):
+        check_block_topk_row(dup, row, 500, 40, 16, 4)
