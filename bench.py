@@ -10,7 +10,8 @@ resident in HBM before timing starts.
 Prints one JSON line: `value` is prefill tokens/s at 128K context; decode tokens/s, the
 per-kernel times (HIP events the library records around each launch on the launch stream),
 the roofline of the dominant kernel (the fused prefill indexer / top-k) and of the decode
-kernels, and the CPU oracle's throughput on a bounded sample ride along.
+kernels, the index projections, the two-tier (block -> token) selection variant of both
+steps, and the CPU oracle's throughput on a bounded sample ride along.
 
 HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
 calibrated on the 1 GiB copy it performs after the warm-up, and stored in
@@ -52,6 +53,9 @@ def parse():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--no-projections", action="store_true", help="skip the index-projection measurement")
+    ap.add_argument("--no-two-tier", action="store_true", help="skip the two-tier (block -> token) measurement")
+    ap.add_argument("--block-size", type=int, default=64, help="two-tier selection: tokens per block")
+    ap.add_argument("--n-blocks", type=int, default=64, help="two-tier selection: blocks kept per query")
     return ap.parse_args()
 
 
@@ -234,6 +238,7 @@ def main():
                 rf["measured_peak"] = key
 
     projections = None if args.no_projections else measure_projections(h_pre, P, L, args.steps, torch)
+    two_tier = None if args.no_two_tier else measure_two_tier(cfg, P, D, L, K, args, torch)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -266,6 +271,7 @@ def main():
         "kernels": kernels,
         "peaks_measured": peaks,
         "projections": projections,
+        "two_tier": two_tier,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -320,6 +326,76 @@ def measure_projections(h, P, L, steps, torch):
                 "algorithmic_per_launch": f"{k_bytes} B = {L} rows x ({2 * kk} B latent row read + "
                                           f"{2 * s.d_idx} B index key written) + W_ik"},
     }
+
+
+def measure_two_tier(cfg, P, D, L, K, args, torch):
+    """The two-tier (block -> token) selection on the same inputs (not part of `value`): blocks of
+    --block-size tokens, --n-blocks kept per query, top-K inside them.  Decode: the paged indexer,
+    then one selection workgroup per sequence over its scores (4 B per cached token read back), then
+    the same attention.  Prefill: scores materialised per block of query rows, then the selection
+    per row, then the same attention."""
+    import numpy as np
+
+    import indexer_selected_sparse_scores_amd as sa
+    dev = "cuda"
+    bs, nb = args.block_size, args.n_blocks
+    s = cfg
+    B = D["q"].shape[0]
+    res = {"block_size": bs, "n_blocks": nb, "topk": K}
+
+    def timed(h, fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        sa.sparse_attn_profile(h, True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        kern = sa.sparse_attn_profile_read(h)
+        sa.sparse_attn_profile(h, False)
+        sa.sparse_attn_check(h)
+        per = {k: round(ms / reps, 4) for k, (ms, n) in kern.items() if n}
+        return e0.elapsed_time(e1) / reps, per
+
+    with sa.Handle(cfg) as h:
+        out = torch.empty((B, s.n_heads, s.d_v), device=dev)
+        idx = torch.empty((B, K), device=dev, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_DECODE_BLOCKS, B, D["max_ctx"])
+        log(f"[bench] two-tier decode B={B} block={bs} n_blocks={nb}")
+        ms, per = timed(h, lambda: sa.sparse_attn_decode_blocks(
+            h, D["q"], D["q_idx"], D["w"], D["kv_pages"], None, D["kidx_pages"], D["block_table"], D["ctx_len"],
+            D["topk"], D["max_ctx"], bs, nb, out, None, idx, ws), args.steps)
+        ctx = D["ctx_np"].astype(np.int64)
+        # per sequence: one page-maximum key per 64 tokens (bs >= 64; else every score), the scores of
+        # the kept blocks' tokens, and the k index slots written
+        span = 64 if bs >= 64 else 1
+        cand = np.minimum(ctx, nb * bs)
+        sel_bytes = int((-(-ctx // span) * 4 + cand * 4 + K * 4).sum())
+        sel_ms = per.get("topk")
+        res["decode"] = {"ms": round(ms, 4), "tokens_per_s": round(B / (ms * 1e-3), 1), "kernels_ms": per}
+        if sel_ms:
+            gbs = sel_bytes / (sel_ms * 1e-3) / 1e9
+            res["decode"]["selection_roofline"] = {
+                "kernel": "block_topk_rows_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "algorithmic_per_launch": f"{sel_bytes} B = per sequence ceil(n/{span}) block-maximum keys + "
+                                          f"min(n, {nb * bs}) candidate scores read + {K} indices written"}
+        del out, idx, ws
+    with sa.Handle(cfg) as h:
+        out = torch.empty((L, s.n_heads, s.d_v), device=dev)
+        idx = torch.empty((L, K), device=dev, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL_BLOCKS, L)
+        log(f"[bench] two-tier prefill L={L} block={bs} n_blocks={nb}")
+        ms, per = timed(h, lambda: sa.sparse_attn_prefill_blocks(
+            h, P["q"], P["k"], None, P["q_idx"], P["w"], P["k_idx"], K, bs, nb, out, None, idx, ws),
+            max(1, min(args.steps, 2)))
+        res["prefill"] = {"ms": round(ms, 4), "tokens_per_s": round(L / (ms * 1e-3), 1), "kernels_ms": per}
+        del out, idx, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def measured_peaks(torch):

@@ -400,7 +400,8 @@ sa_status_t topk_select_blocks(sa_handle_t h, const float *scores, int64_t rows,
     s = check_device(h);
     if (s != SA_OK) return s;
     return hip_status(h, sa::launch_block_topk(*h, scores, ld, rows, cols, valid_len, 0, k_per_row, k, block_size,
-                                               n_blocks, idx, k, h->d_err, reinterpret_cast<hipStream_t>(stream)),
+                                               n_blocks, nullptr, 0, idx, k, h->d_err,
+                                               reinterpret_cast<hipStream_t>(stream)),
                       "block top-k launch");
 }
 
@@ -498,8 +499,8 @@ sa_status_t prefill_impl(sa_handle_t h, const void *q, const void *k, const void
             if (s != SA_OK) return s;
             if (blocks)
                 s = hip_status(h, sa::launch_block_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
-                                                        blocks->block_size, blocks->n_blocks, idx + r0 * topk,
-                                                        topk, h->d_err, st),
+                                                        blocks->block_size, blocks->n_blocks, nullptr, 0,
+                                                        idx + r0 * topk, topk, h->d_err, st),
                                "block top-k launch");
             else
                 s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, r0, nullptr, topk,
@@ -556,14 +557,20 @@ sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const f
     sa::Visibility vis{0, ctx_len, max_ctx};
     if (blocks) {
         // scores of every cached token, then the two-tier selection per sequence
-        int64_t ld = max_ctx;
+        int64_t ld = max_ctx, pmax_ld = 0;
+        const uint32_t *pmax = nullptr;
         if (h->fast_decode) {
             const sa::DecodeTopkLayout dl = sa::decode_topk_layout(B, max_ctx);
+            const bool use_pmax = blocks->block_size >= 64;
             s = hip_status(h, sa::launch_decode_indexer(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks,
-                                                        ctx_len, B, max_ctx, base + lay.scores, st),
+                                                        ctx_len, B, max_ctx, use_pmax, base + lay.scores, st),
                            "decode indexer launch");
             scores = reinterpret_cast<float *>(base + lay.scores + dl.scores);
             ld = dl.ld;
+            if (use_pmax) {
+                pmax = reinterpret_cast<const uint32_t *>(base + lay.scores + dl.pmax);
+                pmax_ld = dl.pmax_ld;
+            }
         } else {
             sa::RowSource keys{kidx_pages, c.d_idx, block_table, max_blocks, c.page_size, n_pages};
             s = hip_status(h, sa::launch_indexer(*h, q_idx, w, B, keys, vis, scores, max_ctx, max_ctx, st),
@@ -571,7 +578,8 @@ sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const f
         }
         if (s != SA_OK) return s;
         s = hip_status(h, sa::launch_block_topk(*h, scores, ld, B, max_ctx, ctx_len, 0, topk, c.max_topk,
-                                                blocks->block_size, blocks->n_blocks, idx, c.max_topk, h->d_err, st),
+                                                blocks->block_size, blocks->n_blocks, pmax, pmax_ld, idx, c.max_topk,
+                                                h->d_err, st),
                        "block top-k launch");
         if (s != SA_OK) return s;
     } else if (h->fast_decode) {

@@ -11,7 +11,9 @@
 // One 1024-thread workgroup per row, everything in LDS (about 80 KB):
 //  1. block maxima: coalesced loads of the row's scores as order-preserving keys, a max over
 //     each block's lanes (blocks of up to 64 tokens live inside one wave; longer ones are
-//     combined with LDS atomics), and a 2048-bin histogram of the block keys;
+//     combined with LDS atomics) -- or, when the producer of the scores also wrote the maxima of
+//     each 64-token span (the paged decode indexer does, one per page), a combination of those --
+//     and a 2048-bin histogram of the block keys;
 //  2. the kept blocks: the threshold bin of the n_blocks-th block key, an MSD radix select and
 //     an ordered emit of the kept block ids in ascending order (the shared top-k helpers);
 //  3. the candidates: the visible tokens of the kept blocks, in ascending token order (only the
@@ -70,7 +72,8 @@ __device__ __forceinline__ uint32_t group_max(uint32_t x, int g)
 __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
     const float *__restrict__ scores, int64_t ld, int64_t cols, const int32_t *__restrict__ valid_len,
     int64_t causal_row0, const int32_t *__restrict__ k_per_row, int32_t k, int32_t bs_shift,
-    int32_t n_blocks, int32_t *__restrict__ idx, int64_t idx_ld, uint32_t *err)
+    int32_t n_blocks, const uint32_t *__restrict__ pmax, int64_t pmax_ld, int32_t *__restrict__ idx,
+    int64_t idx_ld, uint32_t *err)
 {
     __shared__ BlockTopkShared sh;
     const int64_t r = blockIdx.x;
@@ -100,15 +103,38 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
         for (int j = tid; j < n_blk; j += kThreads) sh.key[j] = 0;
     __syncthreads();
 
-    // 1. block maxima.  A block of <= 64 tokens is a group of lanes of one wave, led by the lane
-    // holding its first token (s % bs == 0, since each round starts at a multiple of 1024).
-    const int g = bs < kWave ? bs : kWave;
-    for (int64_t base = 0; base < n; base += kThreads) {
-        const int64_t s = base + tid;
-        const uint32_t x = group_max(s < n ? order_key(row[s]) : 0u, g);
-        if ((tid & (g - 1)) == 0 && s < n) {
-            if (bs <= kWave) sh.key[s >> bs_shift] = x;
-            else atomicMax(&sh.key[s >> bs_shift], x);
+    // 1. block maxima
+    if (pmax) {
+        // from the maxima of the 64-token spans (block_size >= 64): block j covers spans
+        // j * bs / 64 .. (j + 1) * bs / 64 - 1
+        const int n64 = (int)((n + kWave - 1) / kWave), sh64 = bs_shift - 6;
+        const uint32_t *prow = pmax + r * pmax_ld;
+        for (int j = tid; j < n64; j += kThreads) {
+            const uint32_t x = prow[j];
+            if (sh64 == 0) sh.key[j] = x;
+            else atomicMax(&sh.key[j >> sh64], x);
+        }
+    } else {
+        // from the scores, four rounds of loads in flight.  A block of <= 64 tokens is a group of
+        // lanes of one wave, led by the lane holding its first token (s % bs == 0, since each round
+        // starts at a multiple of 1024); longer blocks combine their waves' maxima with atomics.
+        const int g = bs < kWave ? bs : kWave;
+        for (int64_t base = 0; base < n; base += 4 * kThreads) {
+            uint32_t x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t s = base + u * kThreads + tid;
+                x[u] = s < n ? order_key(row[s]) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t s = base + u * kThreads + tid;
+                const uint32_t m = group_max(x[u], g);
+                if ((tid & (g - 1)) == 0 && s < n) {
+                    if (bs <= kWave) sh.key[s >> bs_shift] = m;
+                    else atomicMax(&sh.key[s >> bs_shift], m);
+                }
+            }
         }
     }
     __syncthreads();
@@ -166,15 +192,16 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
 
 hipError_t launch_block_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t rows, int64_t cols,
                              const int32_t *valid_len, int64_t causal_row0, const int32_t *k_per_row, int32_t k,
-                             int32_t block_size, int32_t n_blocks, int32_t *idx, int64_t idx_ld, uint32_t *err,
-                             hipStream_t st)
+                             int32_t block_size, int32_t n_blocks, const uint32_t *pmax, int64_t pmax_ld,
+                             int32_t *idx, int64_t idx_ld, uint32_t *err, hipStream_t st)
 {
     if (rows <= 0) return hipSuccess;
     int shift = 0;
     while ((1 << shift) < block_size) ++shift;
+    if (block_size < kWave) pmax = nullptr;
     KernelTimer timer(h, SA_KERNEL_TOPK, st);
     hipLaunchKernelGGL(block_topk_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, scores, ld, cols,
-                       valid_len, causal_row0, k_per_row, k, shift, n_blocks, idx, idx_ld, err);
+                       valid_len, causal_row0, k_per_row, k, shift, n_blocks, pmax, pmax_ld, idx, idx_ld, err);
     return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ kidx_pages,
     int64_t n_pages, const int32_t *__restrict__ block_table, int32_t max_blocks,
     const int32_t *__restrict__ ctx_len, int32_t max_ctx, float *__restrict__ scores, int64_t ld,
-    uint32_t *__restrict__ hist_g, uint32_t *err)
+    uint32_t *__restrict__ hist_g, uint32_t *__restrict__ pmax_g, int64_t pmax_ld, uint32_t *err)
 {
     __shared__ DecodeIdxShared sh;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
@@ -178,6 +178,20 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
             if (s0 < n) dst[0] = v.x;
             if (s0 + 1 < n) dst[1] = v.y;
             if (s0 + 2 < n) dst[2] = v.z;
+        }
+        if (pmax_g) {
+            // the largest score of each of the wave's pages as an order key (a page is the 16 lanes
+            // of one DPP row; tokens past the context count as key 0, below every score's key)
+            uint32_t x = s0 < n ? order_key(v.x) : 0u;
+            x = max(x, s0 + 1 < n ? order_key(v.y) : 0u);
+            x = max(x, s0 + 2 < n ? order_key(v.z) : 0u);
+            x = max(x, s0 + 3 < n ? order_key(v.w) : 0u);
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true));  // row_shr:1
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true));  // row_shr:2
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true));  // row_shr:4
+            x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true));  // row_shr:8
+            const int64_t lp = lp0 + lane / 16;
+            if ((lane & 15) == 15 && lp * kPage < n) pmax_g[b * pmax_ld + lp] = x;
         }
     }
     __syncthreads();
@@ -352,18 +366,22 @@ DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
     };
     l.scores = take((size_t)B * l.ld * sizeof(float));
     l.hist = take((size_t)B * kBins * sizeof(uint32_t));
+    l.pmax_ld = l.ld / kPage;
+    l.pmax = take((size_t)B * l.pmax_ld * sizeof(uint32_t));
     l.total = at;
     return l;
 }
 
 hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
                                  int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
-                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, void *ws, hipStream_t st)
+                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, bool page_maxima, void *ws,
+                                 hipStream_t st)
 {
     const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
     char *base = reinterpret_cast<char *>(ws);
     float *scores = reinterpret_cast<float *>(base + l.scores);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base + l.hist);
+    uint32_t *pmax = page_maxima ? reinterpret_cast<uint32_t *>(base + l.pmax) : nullptr;
     {
         const int64_t nz = (int64_t)B * kBins;
         hipLaunchKernelGGL(decode_reset_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist,
@@ -377,7 +395,7 @@ hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float 
         hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(kIdxThreads), 0, st,
                            reinterpret_cast<const uint16_t *>(q_idx), w,
                            reinterpret_cast<const uint16_t *>(kidx_pages), n_pages, block_table, max_blocks,
-                           ctx_len, max_ctx, scores, l.ld, hist, h.d_err);
+                           ctx_len, max_ctx, scores, l.ld, hist, pmax, l.pmax_ld, h.d_err);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -390,7 +408,7 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
                                       int32_t *idx, void *ws, hipStream_t st)
 {
     hipError_t e = launch_decode_indexer(h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks, ctx_len, B,
-                                         max_ctx, ws, st);
+                                         max_ctx, false, ws, st);
     if (e != hipSuccess) return e;
     const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
     char *base = reinterpret_cast<char *>(ws);

@@ -86,13 +86,15 @@ hipError_t launch_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t 
 // their best score, the first min(n_blocks, blocks) are kept, and the min(k(r), candidates)
 // best tokens inside them are written ascending, -1 padded to idx_ld.  The host guarantees
 // ceil(cols / block_size) <= kBlockSelectMaxItems, n_blocks <= kBlockSelectMaxKept and
-// n_blocks * block_size <= kBlockSelectMaxItems (everything is held in LDS).
+// n_blocks * block_size <= kBlockSelectMaxItems (everything is held in LDS).  pmax (optional, only
+// with block_size >= 64): row r's order keys of the largest score of each 64-token span of its
+// valid tokens, stride pmax_ld; block maxima are then combined from it instead of the scores.
 constexpr int kBlockSelectMaxItems = 16384;
 constexpr int kBlockSelectMaxKept = 2048;
 hipError_t launch_block_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t rows, int64_t cols,
                              const int32_t *valid_len, int64_t causal_row0, const int32_t *k_per_row, int32_t k,
-                             int32_t block_size, int32_t n_blocks, int32_t *idx, int64_t idx_ld, uint32_t *err,
-                             hipStream_t st);
+                             int32_t block_size, int32_t n_blocks, const uint32_t *pmax, int64_t pmax_ld,
+                             int32_t *idx, int64_t idx_ld, uint32_t *err, hipStream_t st);
 
 // ---- attention over selected rows --------------------------------------------------------
 // Query row r attends to the first m(r) = min(k(r), visible(r)) entries of idx row r.
@@ -116,7 +118,8 @@ hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w
 // ---- paged decode indexer + per-sequence top-k (bf16, H_I = 64, d_I = 128, 64-token pages) --
 struct DecodeTopkLayout {
     int64_t ld;          // score row stride (floats)
-    size_t scores, hist, total;  // byte offsets in the workspace
+    int64_t pmax_ld;     // page-maxima row stride (uint32 order keys, one per 64-token page)
+    size_t scores, hist, pmax, total;  // byte offsets in the workspace
 };
 DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx);
 // idx [B, max_topk] gets each sequence's selection; ws holds decode_topk_layout(B, max_ctx).total
@@ -126,10 +129,12 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
                                       int32_t *idx, void *ws, hipStream_t st);
 
 // The paged decode indexer alone: sequence b's scores land at ws + layout.scores, row stride
-// layout.ld (floats), for tokens s < ctx_len[b].
+// layout.ld (floats), for tokens s < ctx_len[b]; with page_maxima, the order key of the largest
+// score of each visible 64-token logical page lands at ws + layout.pmax, row stride layout.pmax_ld.
 hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
                                  int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
-                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, void *ws, hipStream_t st);
+                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, bool page_maxima, void *ws,
+                                 hipStream_t st);
 
 // ---- index-space projections (bf16) ---------------------------------------------------
 size_t projection_workspace();

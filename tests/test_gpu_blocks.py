@@ -240,14 +240,17 @@ def _check_decode_blocks(d, out, lse, idx, bs, nb, seqs, d_v, what, latent=True)
     say(f"{what}: seqs={len(seqs)} near-tie set diffs={diffs} max|dO|={err:.2e}")
 
 
-def test_decode_blocks_small_paged():
+@pytest.mark.parametrize("bs,nb", [(64, 6), (256, 2), (128, 3), (32, 12), (1024, 1)])
+def test_decode_blocks_small_paged(bs, nb):
+    """Blocks of one page take the indexer's page maxima as they are, wider blocks combine them,
+    narrower ones are scored from the scores themselves."""
     wl = inputs.WORKLOADS["decode_b64"]
-    ctx = [1, 63, 64, 65, 300, 1000, 2500, 129]
-    say(f"decode_blocks latent small ctx={ctx} topk=256 block=64 n_blocks=6")
+    ctx = [1, 63, 64, 65, 300, 1000, 2500, 129, 1100, 4097]
+    say(f"decode_blocks latent small ctx={ctx} topk=256 block={bs} n_blocks={nb}")
     d = inputs.decode_inputs(inputs.small(wl, topk=256), DEV, ctx=ctx, seed=3)
     with sa.Handle(inputs.library_config(wl, max_topk=256)) as h:
-        out, lse, idx = _decode_blocks(h, d, 64, 6)
-    _check_decode_blocks(d, out, lse, idx, 64, 6, np.arange(len(ctx)), 512, "decode_blocks small")
+        out, lse, idx = _decode_blocks(h, d, bs, nb)
+    _check_decode_blocks(d, out, lse, idx, bs, nb, np.arange(len(ctx)), 512, f"decode_blocks small b{bs}")
 
 
 def test_decode_blocks_generic_paged():
