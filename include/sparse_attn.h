@@ -63,6 +63,7 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype_t;
 #define SA_DEVERR_BLOCK_TABLE   2u  /* a visible token's page was -1 or >= n_pages       */
 #define SA_DEVERR_CTX_LEN       4u  /* ctx_len[b] outside [1, max_ctx]                   */
 #define SA_DEVERR_TOPK          8u  /* topk[b] outside [1, max_topk]                     */
+#define SA_DEVERR_ROW          16u  /* row_seq[t] / row_pos[t] out of range (row skipped) */
 
 typedef struct {
     int32_t n_idx_heads;   /* H_I: index heads (e.g. 64)                                  */
@@ -89,6 +90,7 @@ typedef struct {
 #define SA_OP_PROJECT 4  /* n = L rows of indexer_project_q, max_ctx ignored              */
 #define SA_OP_PREFILL_BLOCKS 5  /* sparse_attn_prefill_blocks: n = L, max_ctx ignored     */
 #define SA_OP_DECODE_BLOCKS  6  /* sparse_attn_decode_blocks: as SA_OP_DECODE             */
+#define SA_OP_PREFILL_PAGED  7  /* sparse_attn_prefill_paged: n = T query rows, max_ctx   */
 
 /* Create a handle for one configuration.  Validates the config, allocates the 4-byte
  * device error word on the current device (the only device allocation the library makes)
@@ -228,6 +230,33 @@ sa_status_t sparse_attn_decode_blocks(sa_handle_t h, const void *q, const void *
                                       const int32_t *ctx_len, const int32_t *topk, int32_t B,
                                       int32_t max_ctx, int32_t block_size, int32_t n_blocks, float *out,
                                       float *lse, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Query rows against paged caches: chunked prefill (new tokens of a sequence whose earlier tokens
+ * are already cached), varlen batches of several sequences, and several new tokens per sequence in
+ * one decode step.  Query row t is the token at position p = row_pos[t] of sequence
+ * b = row_seq[t]; it scores the tokens s <= p of that sequence in the paged index-key cache, keeps
+ * its top-k, and attends to the selected rows of the paged KV cache -- "Long-Context LLMs
+ * Explained...", section 2.3 (selection over a paged cache) with the causal look-back of "Sparse
+ * Attention and RL Optimization...", section 2.5.  The caches must already hold every token
+ * s <= p (write the new tokens' rows first, e.g. with indexer_project_k).
+ *   q [T, H, d_qk], q_idx [T, H_I, d_I], w [T, H_I] fp32: the T query rows, in any order
+ *   kv_pages, v_pages, kidx_pages, n_pages: the page pools of sparse_attn_decode
+ *   block_table [n_seqs, max_blocks] int32 (host-known n_seqs, max_blocks)
+ *   row_seq, row_pos [T] int32 (device): sequence in [0, n_seqs), position in [0, max_ctx)
+ *   max_ctx    host-side bound of every row_pos + 1, <= max_blocks * page_size
+ *   topk       k, 1 <= k <= max_topk; row t attends to min(k, p + 1) tokens
+ *   out [T, H, d_v] fp32; lse [T, H] fp32 or NULL; idx_out [T, topk] int32 or NULL (positions,
+ *   ascending, -1 padded)
+ *   ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_PREFILL_PAGED, T, max_ctx)
+ * A row whose (row_seq, row_pos) is out of range sets SA_DEVERR_ROW and is skipped (its outputs
+ * are unspecified).  Errors: SA_ERR_INVALID_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP; device-side bits as
+ * in sparse_attn_decode. */
+sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                      const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t n_seqs,
+                                      int32_t max_blocks, const int32_t *row_seq, const int32_t *row_pos,
+                                      int64_t T, int32_t max_ctx, int32_t topk, float *out, float *lse,
+                                      int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Index-space projections -- the first lines of the "Sparse Attention and RL Optimization...",
  * section 2.5 pseudocode: the index query and key are linear maps of the attention query and

@@ -105,6 +105,42 @@ DecodeLayout decode_layout(const sa_handle_s &h, int64_t B, int64_t max_ctx)
     return d;
 }
 
+// Query rows against paged caches: [row_seq copy | ctx | budget | scores (and histograms) of one
+// block of rows | idx | split-attention partials (few rows only)].
+struct PagedLayout {
+    size_t seq, ctx, budget, scores, idx, attn, total;
+    int64_t chunk;   // query rows scored at once
+    bool split;      // attention splits each row's selection over workgroups
+};
+
+PagedLayout paged_layout(const sa_handle_s &h, int64_t T, int64_t max_ctx)
+{
+    PagedLayout p;
+    const int64_t ld = h.fast_decode ? (max_ctx + 63) / 64 * 64 : max_ctx;
+    int64_t chunk = (int64_t)(kPrefillChunkBytes / (sizeof(float) * (size_t)ld));
+    if (chunk < 1) chunk = 1;
+    if (chunk > 65535) chunk = 65535;  // grid y of the indexer kernels
+    if (chunk > T) chunk = T;
+    p.chunk = chunk;
+    p.split = h.fast_attn && T < h.n_cu;
+    size_t at = 0;
+    p.seq = at;
+    at += align_up((size_t)T * sizeof(int32_t));
+    p.ctx = at;
+    at += align_up((size_t)T * sizeof(int32_t));
+    p.budget = at;
+    at += align_up((size_t)T * sizeof(int32_t));
+    p.scores = at;
+    at += align_up(h.fast_decode ? sa::decode_topk_layout(chunk, max_ctx).total
+                                 : (size_t)chunk * (size_t)max_ctx * sizeof(float));
+    p.idx = at;
+    at += align_up((size_t)T * (size_t)h.cfg.max_topk * sizeof(int32_t));
+    p.attn = at;
+    at += align_up(p.split ? sa::attention_workspace(h, T, true) : 0);
+    p.total = at;
+    return p;
+}
+
 // Two-tier (block -> token) selection parameters; nullptr selects plain per-query top-k.
 struct BlockSelect {
     int32_t block_size, n_blocks;
@@ -313,6 +349,11 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
     case SA_OP_DECODE_BLOCKS:
         if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
         *bytes = decode_layout(*h, n, max_ctx).total;
+        return SA_OK;
+    case SA_OP_PREFILL_PAGED:
+        if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T exceeds the launch limit");
+        if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
+        *bytes = paged_layout(*h, n, max_ctx).total;
         return SA_OK;
     case SA_OP_TOPK:
         *bytes = 0;
@@ -563,7 +604,8 @@ sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const f
             const sa::DecodeTopkLayout dl = sa::decode_topk_layout(B, max_ctx);
             const bool use_pmax = blocks->block_size >= 64;
             s = hip_status(h, sa::launch_decode_indexer(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks,
-                                                        ctx_len, B, max_ctx, use_pmax, base + lay.scores, st),
+                                                        ctx_len, nullptr, B, max_ctx, use_pmax, base + lay.scores,
+                                                        st),
                            "decode indexer launch");
             scores = reinterpret_cast<float *>(base + lay.scores + dl.scores);
             ld = dl.ld;
@@ -607,6 +649,83 @@ sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const f
 }  // namespace
 
 extern "C" {
+
+sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                      const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table, int32_t n_seqs,
+                                      int32_t max_blocks, const int32_t *row_seq, const int32_t *row_pos,
+                                      int64_t T, int32_t max_ctx, int32_t topk, float *out, float *lse,
+                                      int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    const sa_config_t &c = h->cfg;
+    if (!q || !q_idx || !w || !kv_pages || !kidx_pages || !block_table || !row_seq || !row_pos || !out)
+        return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (c.v_from_k ? v_pages != nullptr : v_pages == nullptr)
+        return fail(h, SA_ERR_INVALID_ARG, c.v_from_k ? "v_pages must be NULL when v_from_k = 1"
+                                                      : "v_pages must not be NULL when v_from_k = 0");
+    if (T < 1 || T > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T must be in [1, 2^31)");
+    if (n_seqs < 1) return fail(h, SA_ERR_INVALID_ARG, "n_seqs must be >= 1");
+    if (n_pages < 1) return fail(h, SA_ERR_INVALID_ARG, "n_pages must be >= 1");
+    if (max_blocks < 1) return fail(h, SA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+    if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)max_blocks * c.page_size)
+        return fail(h, SA_ERR_INVALID_ARG, "max_ctx (%d) must be in [1, max_blocks * page_size = %lld]",
+                    max_ctx, (long long)max_blocks * c.page_size);
+    if (topk < 1 || topk > c.max_topk)
+        return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
+    if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
+        (v_pages && !aligned16(v_pages)))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+    const PagedLayout lay = paged_layout(*h, T, max_ctx);
+    if (!ws || ws_bytes < lay.total)
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *base = reinterpret_cast<char *>(ws);
+    int32_t *seq = reinterpret_cast<int32_t *>(base + lay.seq);
+    int32_t *ctx = reinterpret_cast<int32_t *>(base + lay.ctx);
+    int32_t *budget = reinterpret_cast<int32_t *>(base + lay.budget);
+    float *scores = reinterpret_cast<float *>(base + lay.scores);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
+    const size_t es = elem_size(*h);
+
+    s = hip_status(h, sa::launch_paged_rows(*h, row_seq, row_pos, T, n_seqs, max_ctx, topk, seq, ctx, budget, st),
+                   "row check launch");
+    if (s != SA_OK) return s;
+    // indexer -> top-k per block of query rows, each row over its own sequence's pages
+    for (int64_t r0 = 0; r0 < T; r0 += lay.chunk) {
+        const int32_t rows = (int32_t)(r0 + lay.chunk < T ? lay.chunk : T - r0);
+        const void *qi = reinterpret_cast<const char *>(q_idx) + r0 * c.n_idx_heads * c.d_idx * es;
+        const float *wr = w + r0 * c.n_idx_heads;
+        if (h->fast_decode) {
+            s = hip_status(h, sa::launch_decode_indexer(*h, qi, wr, kidx_pages, n_pages, block_table, max_blocks,
+                                                        ctx + r0, seq + r0, rows, max_ctx, false, scores, st),
+                           "decode indexer launch");
+            if (s != SA_OK) return s;
+            s = hip_status(h, sa::launch_decode_topk(*h, ctx + r0, budget + r0, topk, rows, max_ctx, idx + r0 * topk,
+                                                     scores, st),
+                           "top-k launch");
+        } else {
+            sa::RowSource keys{kidx_pages, c.d_idx, block_table, max_blocks, c.page_size, n_pages, seq + r0};
+            sa::Visibility vis{0, ctx + r0, max_ctx};
+            s = hip_status(h, sa::launch_indexer(*h, qi, wr, rows, keys, vis, scores, max_ctx, max_ctx, st),
+                           "indexer launch");
+            if (s != SA_OK) return s;
+            s = hip_status(h, sa::launch_topk(*h, scores, max_ctx, rows, max_ctx, ctx + r0, 0, nullptr, topk,
+                                              idx + r0 * topk, topk, h->d_err, st),
+                           "top-k launch");
+        }
+        if (s != SA_OK) return s;
+    }
+    sa::RowSource kv{kv_pages, (int64_t)c.n_kv_heads * c.d_qk, block_table, max_blocks, c.page_size, n_pages, seq};
+    sa::RowSource vv{v_pages, (int64_t)c.n_kv_heads * c.d_v, block_table, max_blocks, c.page_size, n_pages, seq};
+    sa::Visibility vis{0, ctx, max_ctx};
+    sa::Selection sel{idx, topk, topk, nullptr};
+    return hip_status(h, sa::launch_attention(*h, q, T, kv, vv, vis, sel, out, lse, base + lay.attn, st, lay.split),
+                      "attention launch");
+}
 
 sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const void *W_iq, const void *W_w,
                               void *q_idx, float *w, void *ws, size_t ws_bytes, void *stream)

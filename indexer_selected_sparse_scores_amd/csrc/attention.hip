@@ -52,7 +52,8 @@ __device__ __forceinline__ int64_t budget(const Selection &sel, int64_t r, uint3
     return k;
 }
 
-// Element offset of token s of the sequence of query row b, or -1 if its page is invalid.
+// Element offset of token s of sequence b (the sequence of the query row, RowSource::seq_of), or
+// -1 if its page is invalid.
 __device__ __forceinline__ int64_t token_offset(const RowSource &src, int64_t b, int64_t s)
 {
     if (!src.block_table) return s * src.row_elems;
@@ -89,15 +90,16 @@ struct AttnShared {
     int64_t row_off[2][kChunk];             // element offsets of a chunk's rows (-1: none)
 };
 
-// Element offset of selected slot j of query row r, -1 if the slot is unused or invalid.
-__device__ __forceinline__ int64_t slot_offset(const RowSource &kv, const int32_t *idx_row, int64_t r,
+// Element offset of selected slot j of a query row of sequence tb, -1 if the slot is unused or
+// invalid.
+__device__ __forceinline__ int64_t slot_offset(const RowSource &kv, const int32_t *idx_row, int64_t tb,
                                                int64_t j, int64_t j_end, int64_t visible, uint32_t *err)
 {
     if (j >= j_end) return -1;
     const int64_t s = idx_row[j];
     if (s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
     if (s < 0 || s >= visible) return -1;
-    const int64_t off = token_offset(kv, r, s);
+    const int64_t off = token_offset(kv, tb, s);
     if (off < 0) flag_error(err, SA_DEVERR_BLOCK_TABLE);
     return off;
 }
@@ -166,6 +168,7 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     const int64_t kr = budget(sel, r, err0);
     const int64_t m = kr < visible ? kr : visible;
     const int64_t j_begin = 0, j_end = m;
+    const int64_t tb = kv.block_table ? kv.seq_of(r) : r;  // block-table row of the sequence
     const int32_t *idx_row = sel.idx + r * sel.idx_ld;
     const uint16_t *kv_base = reinterpret_cast<const uint16_t *>(kv.base);
     const int n_chunks = (int)((j_end - j_begin + kChunk - 1) / kChunk);
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     // would make the wave wait for the load right there)
     int32_t pend_s = -1;
     if (tid < kChunk) {
-        sh.row_off[0][tid] = slot_offset(kv, idx_row, r, j_begin + tid, j_end, visible, err);
-        sh.row_off[1][tid] = slot_offset(kv, idx_row, r, j_begin + kChunk + tid, j_end, visible, err);
+        sh.row_off[0][tid] = slot_offset(kv, idx_row, tb, j_begin + tid, j_end, visible, err);
+        sh.row_off[1][tid] = slot_offset(kv, idx_row, tb, j_begin + kChunk + tid, j_end, visible, err);
         if (pend_j < j_end) pend_s = idx_row[pend_j];
     }
     __syncthreads();
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
             if (ps >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
             if (ps >= 0 && ps < visible) {
                 if (kv.block_table) {
-                    page = kv.block_table[r * kv.max_blocks + ps / kv.page_size];
+                    page = kv.block_table[tb * kv.max_blocks + ps / kv.page_size];
                     page_pending = true;
                 } else {
                     off_next = ps * kv.row_elems;
@@ -431,6 +434,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
     const int64_t m = kr < visible ? kr : visible;
     const int64_t j_begin = (int64_t)split * kDSplitRows;
     if (j_begin >= m) return;  // the merge kernel ignores unused splits
+    const int64_t tb = kv.block_table ? kv.seq_of(r) : r;  // block-table row of the sequence
     const int n_here = (int)(m - j_begin < kDSplitRows ? m - j_begin : kDSplitRows);
     const int n_chunks = (n_here + kChunk - 1) / kChunk;
     const int32_t *idx_row = sel.idx + r * sel.idx_ld + j_begin;
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
                 if (s >= visible) flag_error(err, SA_DEVERR_INDEX_RANGE);
                 if (s >= 0 && s < visible) {
                     if (kv.block_table) {
-                        const int32_t page = kv.block_table[r * kv.max_blocks + s / kv.page_size];
+                        const int32_t page = kv.block_table[tb * kv.max_blocks + s / kv.page_size];
                         if (page >= 0 && page < kv.n_pages)
                             row = (int64_t)page * kv.page_size + s % kv.page_size;
                         else
@@ -712,6 +716,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
     const int32_t *idx_row = sel.idx + r * sel.idx_ld;
     const T *kbase = reinterpret_cast<const T *>(kv.base);
     const T *vbase = reinterpret_cast<const T *>(vsrc.base);
+    const int64_t tb = kv.block_table ? kv.seq_of(r) : r;  // block-table row of the sequence
     for (int c = threadIdx.x; c < d_qk; c += blockDim.x) qh[c] = load_elem(q + (r * H + h) * (int64_t)d_qk + c);
     __syncthreads();
 
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
         float l = neg_inf;
         if (s >= visible && h == 0) flag_error(err, SA_DEVERR_INDEX_RANGE);
         if (s >= 0 && s < visible) {
-            const int64_t off = token_offset(kv, r, s);
+            const int64_t off = token_offset(kv, tb, s);
             if (off >= 0) {
                 const T *kr_ = kbase + off + (int64_t)g * d_qk;
                 float dot = 0.f;
@@ -749,7 +754,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
             const float p = pw[j];
             if (p == 0.f) continue;
             const int64_t s = idx_row[j];
-            const int64_t off = token_offset(vbase ? vsrc : kv, r, s);
+            const int64_t off = token_offset(vbase ? vsrc : kv, tb, s);
             const T *vr = vbase ? vbase + off + (int64_t)g * d_v : kbase + off + (int64_t)g * d_qk;
             a = fmaf(p, load_elem(vr + d), a);
         }
@@ -769,11 +774,11 @@ size_t attention_workspace(const sa_handle_s &h, int64_t n_rows, bool decode)
 
 hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSource kv,
                             RowSource v, Visibility vis, Selection sel, float *out, float *lse,
-                            void *ws, hipStream_t st)
+                            void *ws, hipStream_t st, bool allow_split)
 {
     if (n_rows <= 0) return hipSuccess;
     const float scale_log2 = h.scale * kLog2e;
-    const bool decode = vis.ctx_len != nullptr;
+    const bool decode = vis.ctx_len != nullptr && allow_split;
     if (h.fast_attn) {
         const uint16_t *qq = reinterpret_cast<const uint16_t *>(q);
         if (!decode) {

@@ -75,12 +75,13 @@ struct DecodeIdxShared {
 __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ kidx_pages,
     int64_t n_pages, const int32_t *__restrict__ block_table, int32_t max_blocks,
-    const int32_t *__restrict__ ctx_len, int32_t max_ctx, float *__restrict__ scores, int64_t ld,
-    uint32_t *__restrict__ hist_g, uint32_t *__restrict__ pmax_g, int64_t pmax_ld, uint32_t *err)
+    const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ row_seq, int32_t max_ctx,
+    float *__restrict__ scores, int64_t ld, uint32_t *__restrict__ hist_g, uint32_t *__restrict__ pmax_g,
+    int64_t pmax_ld, uint32_t *err)
 {
     __shared__ DecodeIdxShared sh;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-    const int64_t b = blockIdx.y;
+    const int64_t b = blockIdx.y;  // query row: its q, weights, context length and outputs
     const int64_t n = ctx_len[b];
     if (n < 1 || n > max_ctx) {
         if (tid == 0 && blockIdx.x == 0) flag_error(err, SA_DEVERR_CTX_LEN);
@@ -89,14 +90,15 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
     const int64_t key0 = (int64_t)blockIdx.x * kKeysPerBlock;
     if (key0 >= n) return;
 
-    // this wave's pages: logical pages lp0 .. lp0 + 3
+    // this wave's pages: logical pages lp0 .. lp0 + 3 of the row's sequence
     const int64_t lp0 = key0 / kPage + (int64_t)kPagesPerWave * wave;
+    const int64_t tb = row_seq ? (int64_t)row_seq[b] : b;
     int64_t page[kPagesPerWave];
     bool page_ok[kPagesPerWave];
 #pragma unroll
     for (int i = 0; i < kPagesPerWave; ++i) {
         const bool used = (lp0 + i) * kPage < n;
-        const int32_t p = used ? block_table[b * max_blocks + lp0 + i] : 0;
+        const int32_t p = used ? block_table[tb * max_blocks + lp0 + i] : 0;
         page_ok[i] = p >= 0 && p < n_pages;
         if (used && !page_ok[i] && lane == 0) flag_error(err, SA_DEVERR_BLOCK_TABLE);
         page[i] = page_ok[i] ? p : 0;  // an unused or bad page is read from page 0 and ignored
@@ -374,8 +376,8 @@ DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
 
 hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
                                  int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
-                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, bool page_maxima, void *ws,
-                                 hipStream_t st)
+                                 const int32_t *ctx_len, const int32_t *row_seq, int32_t B, int32_t max_ctx,
+                                 bool page_maxima, void *ws, hipStream_t st)
 {
     const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
     char *base = reinterpret_cast<char *>(ws);
@@ -395,7 +397,7 @@ hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float 
         hipLaunchKernelGGL(indexer_decode_kernel, grid, dim3(kIdxThreads), 0, st,
                            reinterpret_cast<const uint16_t *>(q_idx), w,
                            reinterpret_cast<const uint16_t *>(kidx_pages), n_pages, block_table, max_blocks,
-                           ctx_len, max_ctx, scores, l.ld, hist, pmax, l.pmax_ld, h.d_err);
+                           ctx_len, row_seq, max_ctx, scores, l.ld, hist, pmax, l.pmax_ld, h.d_err);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -407,14 +409,19 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
                                       const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
                                       int32_t *idx, void *ws, hipStream_t st)
 {
-    hipError_t e = launch_decode_indexer(h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks, ctx_len, B,
-                                         max_ctx, false, ws, st);
+    hipError_t e = launch_decode_indexer(h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks, ctx_len,
+                                         nullptr, B, max_ctx, false, ws, st);
     if (e != hipSuccess) return e;
+    return launch_decode_topk(h, ctx_len, topk_b, h.cfg.max_topk, B, max_ctx, idx, ws, st);
+}
+
+hipError_t launch_decode_topk(sa_handle_s &h, const int32_t *ctx_len, const int32_t *topk_b, int32_t max_topk,
+                              int32_t B, int32_t max_ctx, int32_t *idx, void *ws, hipStream_t st)
+{
     const DecodeTopkLayout l = decode_topk_layout(B, max_ctx);
     char *base = reinterpret_cast<char *>(ws);
     const float *scores = reinterpret_cast<const float *>(base + l.scores);
     const uint32_t *hist = reinterpret_cast<const uint32_t *>(base + l.hist);
-    const int32_t max_topk = h.cfg.max_topk;
     KernelTimer timer(h, SA_KERNEL_TOPK, st);
     hipLaunchKernelGGL(decode_topk_kernel, dim3((unsigned)B), dim3(kTopkThreads), 0, st, scores, l.ld, ctx_len,
                        max_ctx, topk_b, max_topk, hist, idx, h.d_err);

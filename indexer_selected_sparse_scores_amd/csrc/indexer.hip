@@ -39,7 +39,7 @@ __device__ __forceinline__ const T *token_row(const RowSource &src, int64_t b, i
         ok = true;
         return reinterpret_cast<const T *>(src.base) + s * src.row_elems;
     }
-    int32_t page = src.block_table[b * src.max_blocks + s / src.page_size];
+    int32_t page = src.block_table[src.seq_of(b) * src.max_blocks + s / src.page_size];
     ok = page >= 0 && page < src.n_pages;
     if (!ok) page = 0;
     return reinterpret_cast<const T *>(src.base) +

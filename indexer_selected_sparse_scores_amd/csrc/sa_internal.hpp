@@ -51,7 +51,9 @@ hipError_t drain_profile(sa_handle_s &h);
 // Where the index keys / KV rows of a query row live.
 //  contiguous: row s of sequence = base + s * row_elems
 //  paged:      token s of sequence b = pool page block_table[b * max_blocks + s / page_size],
-//              slot s % page_size; pages hold page_size rows of row_elems elements.
+//              slot s % page_size; pages hold page_size rows of row_elems elements.  Query row r
+//              belongs to sequence b = row_seq[r] (row_seq != nullptr, entries already checked),
+//              else b = r.
 struct RowSource {
     const void *base;
     int64_t row_elems;              // elements per token row
@@ -59,6 +61,8 @@ struct RowSource {
     int32_t max_blocks;
     int32_t page_size;
     int64_t n_pages;
+    const int32_t *row_seq = nullptr;
+    __device__ int64_t seq_of(int64_t r) const { return row_seq ? (int64_t)row_seq[r] : r; }
 };
 
 // Which keys a query row sees: keys s < visible(r), where visible(r) = causal_row0 + r + 1
@@ -105,9 +109,12 @@ struct Selection {
     const int32_t *k_per_row;
 };
 
+// Rows with a context-length array (decode) may split each row's selection over workgroups
+// (allow_split; ws then holds attention_workspace(h, n_rows, true) bytes); otherwise one
+// workgroup attends to each row.
 hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows,
                             RowSource kv, RowSource v, Visibility vis, Selection sel,
-                            float *out, float *lse, void *ws, hipStream_t st);
+                            float *out, float *lse, void *ws, hipStream_t st, bool allow_split = true);
 
 // ---- fused prefill indexer + streaming top-k (bf16, H_I = 64, d_I = 128) ---------------
 // idx [L, topk] gets every row's selection; ws holds prefill_topk_workspace(h, L) bytes.
@@ -131,10 +138,23 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
 // The paged decode indexer alone: sequence b's scores land at ws + layout.scores, row stride
 // layout.ld (floats), for tokens s < ctx_len[b]; with page_maxima, the order key of the largest
 // score of each visible 64-token logical page lands at ws + layout.pmax, row stride layout.pmax_ld.
+// Row b reads the block-table row row_seq[b] (row_seq != nullptr, entries already checked) or b.
 hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
                                  int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
-                                 const int32_t *ctx_len, int32_t B, int32_t max_ctx, bool page_maxima, void *ws,
-                                 hipStream_t st);
+                                 const int32_t *ctx_len, const int32_t *row_seq, int32_t B, int32_t max_ctx,
+                                 bool page_maxima, void *ws, hipStream_t st);
+// The per-row top-k over the scores and histograms launch_decode_indexer left in ws: row b keeps
+// min(topk_b[b], ctx_len[b]) tokens (topk_b[b] <= max_topk), written to idx [B, max_topk].
+hipError_t launch_decode_topk(sa_handle_s &h, const int32_t *ctx_len, const int32_t *topk_b, int32_t max_topk,
+                              int32_t B, int32_t max_ctx, int32_t *idx, void *ws, hipStream_t st);
+
+// ---- query rows against paged caches --------------------------------------------------
+// Checks (row_seq[t], row_pos[t]) (sequence in [0, n_seqs), position in [0, max_ctx); a bad row
+// sets SA_DEVERR_ROW) and writes seq[t] (0 for a bad row), ctx[t] = row_pos[t] + 1 (0 for a bad
+// row, which every later kernel skips) and budget[t] = topk.
+hipError_t launch_paged_rows(sa_handle_s &h, const int32_t *row_seq, const int32_t *row_pos, int64_t T,
+                             int32_t n_seqs, int32_t max_ctx, int32_t topk, int32_t *seq, int32_t *ctx,
+                             int32_t *budget, hipStream_t st);
 
 // ---- index-space projections (bf16) ---------------------------------------------------
 size_t projection_workspace();

@@ -197,6 +197,28 @@ def decode_inputs(wl: Workload, device="cuda", seed: int | None = None, ctx=None
     return out
 
 
+def paged_rows_inputs(wl: Workload, ctx, row_seq, row_pos, device="cuda", seed: int | None = None):
+    """Paged caches of len(ctx) sequences (as decode_inputs) and T = len(row_seq) query rows drawn
+    like the workload's queries: row t is the token at position row_pos[t] of sequence row_seq[t].
+    Adds q [T,H,d_qk], q_idx [T,H_I,d_I], w [T,H_I] (replacing the decode rows), row_seq and
+    row_pos [T] int32 on the device and as numpy (rs_np, rp_np)."""
+    s = wl.shapes
+    seed = BASE_SEED + wl.seed_offset if seed is None else seed
+    d = decode_inputs(wl, device, seed=seed, ctx=ctx)
+    rs = np.asarray(row_seq, dtype=np.int64)
+    rp = np.asarray(row_pos, dtype=np.int64)
+    T = len(rs)
+    g = _gen(seed + 101, device)
+    dt = torch_dtype(s)
+    d["q_idx"] = _normal((T, s.H_I, s.d_I), s.idx_std, g, device, dt)
+    d["w"] = _weights(s, T, g, device)
+    d["q"] = _normal((T, s.H, s.d_qk), 1.0, g, device, dt)
+    d["row_seq"] = torch.from_numpy(rs.astype(np.int32)).to(device)
+    d["row_pos"] = torch.from_numpy(rp.astype(np.int32)).to(device)
+    d["rs_np"], d["rp_np"] = rs, rp
+    return d
+
+
 def library_config(wl: Workload, max_topk: int | None = None):
     """The library configuration matching a workload's shapes."""
     from indexer_selected_sparse_scores_amd import Config

@@ -22,6 +22,8 @@ Stable Reinforcement Learning, and Verifiable Synthetic Data"):
 * ``decode`` -- one new token per sequence against a paged cache: the pages are first
   laid out contiguously through the block table ([P3] section 2.3: only the selected k
   entries are read, and this composes with paged KV management), then the same steps.
+* ``prefill_paged`` -- query rows that each name their sequence and position in paged caches
+  (chunked prefill, varlen batches): every row is one decode step of its sequence.
 * ``project`` / ``round_bf16`` / ``paged_slot`` -- the index projections of the [P1] section
   2.5 pseudocode (i_q = W_iq(q), i_k = W_ik(k)) as plain linear maps in double, the rounding
   of their bf16 outputs, and where a projected key lands in the paged index cache.
@@ -277,6 +279,23 @@ def decode(q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len, top
     res = dict(seqs=seqs, idx=idx_all, out=out_all, lse=lse_all)
     if with_scores:
         res["scores"] = scores
+    return res
+
+
+def prefill_paged(q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, row_seq, row_pos, top_k: int,
+                  rows=None, scale: float | None = None, d_v: int | None = None, with_scores: bool = False):
+    """Query rows against paged caches ([P3] section 2.3 with the causal look-back of [P1] section
+    2.5): query row t is the token at position p = row_pos[t] of sequence b = row_seq[t] and sees
+    the tokens s <= p of b.  Each row is exactly a one-token decode step of sequence b with context
+    p + 1, so this is ``decode`` over the rows, each given its sequence's block-table row.
+    Returns the dict of ``decode`` for the chosen rows (all by default)."""
+    rs = np.asarray(row_seq, dtype=np.int64)
+    rp = np.asarray(row_pos, dtype=np.int64)
+    rows = np.arange(len(rs)) if rows is None else np.asarray(rows, dtype=np.int64)
+    table = np.asarray(block_table)[rs[rows]]
+    res = decode(_f32(q)[rows], _f32(q_idx)[rows], _f32(w)[rows], kv_pages, v_pages, kidx_pages, table,
+                 rp[rows] + 1, top_k, k_max=top_k, scale=scale, d_v=d_v, with_scores=with_scores)
+    res["rows"] = rows
     return res
 
 

@@ -1,0 +1,188 @@
+"""GPU parity of query rows against paged caches (sparse_attn_prefill_paged): chunked prefill,
+varlen batches and several new tokens per sequence, against the CPU oracle.
+
+Pages: "Long-Context LLMs Explained: Sparse Attention, Stable Reinforcement Learning, and
+Verifiable Synthetic Data", section 2.3 (selection over a paged cache), with the causal look-back
+of "Sparse Attention and RL Optimization: Three Technical Breakthroughs in LLM Post-Training",
+section 2.5.  Tolerances are those of tests/parity.py."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_sparse_scores_amd as sa
+import oracle
+from indexer_selected_sparse_scores_amd import inputs
+from tests.parity import check_attention, check_topk_row, compact_pages, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(h, d, topk, max_ctx=None, check=True):
+    T = d["q"].shape[0]
+    s = h.cfg
+    max_ctx = int(d["rp_np"].max()) + 1 if max_ctx is None else max_ctx
+    out = torch.empty((T, s.n_heads, s.d_v), device=DEV, dtype=torch.float32)
+    lse = torch.empty((T, s.n_heads), device=DEV, dtype=torch.float32)
+    idx = torch.empty((T, topk), device=DEV, dtype=torch.int32)
+    ws = sa.workspace(h, sa.SA_OP_PREFILL_PAGED, T, max_ctx)
+    sa.sparse_attn_prefill_paged(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], d["v_pages"], d["kidx_pages"],
+                                 d["block_table"], d["row_seq"], d["row_pos"], max_ctx, topk, out, lse, idx, ws)
+    if check:
+        assert sa.sparse_attn_check(h) == 0
+    return out, lse, idx
+
+
+def _check(d, out, lse, idx, rows, topk, d_v, what, latent=True):
+    """Sampled rows against the oracle: selection with the near-tie rule, attention on the GPU's
+    own selection.  Pages leave the device once per sequence."""
+    rows = np.asarray(sorted(set(int(r) for r in rows)))
+    rs, rp = d["rs_np"], d["rp_np"]
+    table = to_np(d["block_table"])
+    gi = to_np(idx)
+    q, qi, w = to_np(d["q"]), to_np(d["q_idx"]), to_np(d["w"])
+    diffs = 0
+    ref_out = np.empty((len(rows), q.shape[1], d_v))
+    ref_lse = np.empty((len(rows), q.shape[1]))
+    for b in np.unique(rs[rows]):
+        mine = [i for i, t in enumerate(rows) if rs[t] == b]
+        n_max = int(rp[rows[mine]].max()) + 1
+        kv_pool, tab = compact_pages(d["kv_pages"], table[b:b + 1], np.array([n_max]))
+        ki_pool, _ = compact_pages(d["kidx_pages"], table[b:b + 1], np.array([n_max]))
+        v_pool = None if latent else compact_pages(d["v_pages"], table[b:b + 1], np.array([n_max]))[0]
+        for i in mine:
+            t = rows[i]
+            n = int(rp[t]) + 1
+            kI = oracle.depage(ki_pool, tab[0], n)
+            sc = oracle.indexer_scores(qi[t:t + 1], w[t:t + 1], kI, [n])[0]
+            diffs += check_topk_row(gi[t], sc, min(topk, n), n, what=f"{what} row {t} (seq {b}, pos {n - 1})")
+            Kb = oracle.depage(kv_pool, tab[0], n)
+            Vb = None if latent else oracle.depage(v_pool, tab[0], n)
+            o, l = oracle.attention_rows(q[t:t + 1], Kb, Vb, gi[t:t + 1], oracle.default_scale(q.shape[-1]), d_v=d_v)
+            ref_out[i], ref_lse[i] = o[0], l[0]
+    err = check_attention(to_np(out)[rows], to_np(lse)[rows], ref_out, ref_lse, what=what)
+    say(f"{what}: rows={len(rows)} near-tie set diffs={diffs} max|dO|={err:.2e}")
+
+
+def test_chunked_prefill_of_one_sequence():
+    """The last 1000 tokens of a 3000-token paged sequence as one chunk, rows shuffled (one
+    attention workgroup per row)."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    n = 3000
+    pos = np.random.default_rng(1).permutation(np.arange(2000, n))
+    say(f"prefill_paged chunk: positions 2000..2999 of a {n}-token sequence, topk=256")
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=256), [n], np.zeros(len(pos), np.int64), pos, DEV, seed=21)
+    with sa.Handle(inputs.library_config(wl, max_topk=256)) as h:
+        out, lse, idx = _run(h, d, 256)
+    rows = np.concatenate([np.arange(8), np.argsort(pos)[[0, 1, -2, -1]],
+                           np.random.default_rng(2).integers(0, len(pos), 20)])
+    _check(d, out, lse, idx, rows, 256, 512, "prefill_paged chunk")
+
+
+def test_varlen_batch_every_position():
+    """Four sequences (700, 64, 1500 and 1 tokens), every position of each as a query row, rows
+    interleaved; k = 512 exceeds the short sequences, which fall back to dense attention."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [700, 64, 1500, 1]
+    rs = np.concatenate([np.full(n, b) for b, n in enumerate(ctx)])
+    rp = np.concatenate([np.arange(n) for n in ctx])
+    order = np.random.default_rng(3).permutation(len(rs))
+    rs, rp = rs[order], rp[order]
+    say(f"prefill_paged varlen ctx={ctx} T={len(rs)} topk=512")
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=512), ctx, rs, rp, DEV, seed=22)
+    with sa.Handle(inputs.library_config(wl, max_topk=512)) as h:
+        out, lse, idx = _run(h, d, 512)
+    where = {(int(b), int(p)): t for t, (b, p) in enumerate(zip(rs, rp))}
+    picks = [(0, 0), (0, 511), (0, 512), (0, 699), (1, 0), (1, 63), (2, 0), (2, 513), (2, 1024), (2, 1499), (3, 0)]
+    rows = [where[k] for k in picks] + list(np.random.default_rng(4).integers(0, len(rs), 16))
+    _check(d, out, lse, idx, rows, 512, 512, "prefill_paged varlen")
+
+
+def test_one_row_per_sequence_equals_decode():
+    """Rows at the last position of each sequence are decode steps: bit-identical to
+    sparse_attn_decode on the same rows (few rows: the split attention path)."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [5000, 129, 20000, 64, 777, 4097, 3, 16384]
+    B = len(ctx)
+    say(f"prefill_paged one row per sequence vs sparse_attn_decode, ctx={ctx}")
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=2048), ctx, np.arange(B), np.array(ctx) - 1, DEV, seed=23)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _run(h, d, 2048)
+        out2 = torch.empty_like(out)
+        lse2 = torch.empty_like(lse)
+        idx2 = torch.empty_like(idx)
+        ws = sa.workspace(h, sa.SA_OP_DECODE, B, d["max_ctx"])
+        sa.sparse_attn_decode(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], None, d["kidx_pages"], d["block_table"],
+                              d["ctx_len"], d["topk"], d["max_ctx"], out2, lse2, idx2, ws)
+        assert sa.sparse_attn_check(h) == 0
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+    assert torch.equal(lse, lse2)
+    _check(d, out, lse, idx, np.arange(B), 2048, 512, "prefill_paged = decode")
+
+
+def test_generic_kernels_fp32():
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], shapes=inputs.TINY, topk=16)
+    ctx = [100, 333]
+    rs = np.concatenate([np.full(n, b) for b, n in enumerate(ctx)])
+    rp = np.concatenate([np.arange(n) for n in ctx])
+    say(f"prefill_paged tiny (fp32, generic kernels) ctx={ctx} T={len(rs)} topk=16")
+    d = inputs.paged_rows_inputs(wl, ctx, rs, rp, DEV, seed=24)
+    with sa.Handle(inputs.library_config(wl, max_topk=16)) as h:
+        out, lse, idx = _run(h, d, 16)
+    _check(d, out, lse, idx, np.arange(len(rs)), 16, 64, "prefill_paged tiny", latent=False)
+
+
+def test_bad_rows_are_flagged_and_skipped():
+    """A row naming a sequence or position out of range sets SA_DEVERR_ROW; the other rows are
+    unaffected."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [300, 200]
+    rs = np.array([0, 1, 0, 1, 0])
+    rp = np.array([10, 199, 299, 5, 150])
+    say("prefill_paged with a bad sequence id and a bad position")
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=64), ctx, rs, rp, DEV, seed=25)
+    bad_seq = d["row_seq"].clone()
+    bad_seq[1] = 7          # only 2 sequences
+    bad_pos = d["row_pos"].clone()
+    bad_pos[3] = 400        # beyond max_ctx = 300
+    d2 = dict(d, row_seq=bad_seq, row_pos=bad_pos)
+    with sa.Handle(inputs.library_config(wl, max_topk=64)) as h:
+        out, lse, idx = _run(h, d2, 64, max_ctx=300, check=False)
+        bits = ctypes.c_uint32()
+        st = sa.load_library().sparse_attn_check(h.ptr, torch.cuda.current_stream().cuda_stream, ctypes.byref(bits))
+        assert st == sa.SA_ERR_DEVICE_CHECK
+        assert bits.value & sa.SA_DEVERR_ROW
+        assert sa.sparse_attn_check(h) == 0  # cleared
+    _check(d, out, lse, idx, [0, 2, 4], 64, 512, "prefill_paged good rows beside bad ones")
+
+
+def test_chunk_at_128k():
+    """The chunk the benchmark times: the last 2048 positions of a 131072-token paged sequence."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    n, T = 131072, 2048
+    say(f"prefill_paged chunk of {T} at the end of a {n}-token sequence, topk=2048 (5 rows checked)")
+    d = inputs.paged_rows_inputs(wl, [n], np.zeros(T, np.int64), np.arange(n - T, n), DEV, seed=26)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _run(h, d, 2048)
+    _check(d, out, lse, idx, [0, 1, 1000, T - 2, T - 1], 2048, 512, "prefill_paged 128k chunk")
+    del d, out, lse, idx
+    torch.cuda.empty_cache()

@@ -70,3 +70,36 @@ def test_budget_closed_form():
     assert oracle.decode_budget(100, 0.1) == 100       # never more than the context
     assert oracle.decode_budget(20480, 0.2) == 4096
     assert oracle.decode_budget(3000, 0.0999) == 299   # floor, not round
+
+
+def test_paged_rows_equal_the_contiguous_prefill_of_each_sequence():
+    """prefill_paged over every position of two paged sequences, rows shuffled and interleaved,
+    equals the plain causal prefill of each sequence laid out contiguously, row for row."""
+    page, d_v, k = 4, 16, 6
+    seqs = [_seq(41, 23), _seq(42, 14)]
+    n_pages = sum((s["q"].shape[0] + page - 1) // page for s in seqs) + 2
+    perm = np.random.default_rng(43).permutation(n_pages)
+    tables = np.full((2, 8), -1, np.int32)
+    used = 0
+    for b, s in enumerate(seqs):
+        nb = (s["q"].shape[0] + page - 1) // page
+        tables[b, :nb] = perm[used:used + nb]
+        used += nb
+    kv_pool = np.zeros((n_pages, page, 1, 24), np.float32)
+    ki_pool = np.zeros((n_pages, page, 8), np.float32)
+    for b, s in enumerate(seqs):
+        kv_pool += _page(s["K"], page, tables[b], n_pages)
+        ki_pool += _page(s["k_idx"], page, tables[b], n_pages)
+    row_seq = np.concatenate([np.full(s["q"].shape[0], b) for b, s in enumerate(seqs)])
+    row_pos = np.concatenate([np.arange(s["q"].shape[0]) for s in seqs])
+    order = np.random.default_rng(44).permutation(len(row_seq))
+    row_seq, row_pos = row_seq[order], row_pos[order]
+    q = np.stack([seqs[b]["q"][p] for b, p in zip(row_seq, row_pos)])
+    qi = np.stack([seqs[b]["q_idx"][p] for b, p in zip(row_seq, row_pos)])
+    w = np.stack([seqs[b]["w"][p] for b, p in zip(row_seq, row_pos)])
+    res = oracle.prefill_paged(q, qi, w, kv_pool, None, ki_pool, tables, row_seq, row_pos, k, d_v=d_v)
+    pre = [oracle.prefill(s["q"], s["K"], None, s["q_idx"], s["w"], s["k_idx"], top_k=k, d_v=d_v) for s in seqs]
+    for t, (b, p) in enumerate(zip(row_seq, row_pos)):
+        np.testing.assert_array_equal(res["idx"][t], pre[b]["idx"][p])
+        np.testing.assert_array_equal(res["out"][t], pre[b]["out"][p])
+        np.testing.assert_array_equal(res["lse"][t], pre[b]["lse"][p])
