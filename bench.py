@@ -11,7 +11,8 @@ Prints one JSON line: `value` is prefill tokens/s at 128K context; decode tokens
 per-kernel times (HIP events the library records around each launch on the launch stream),
 the roofline of the dominant kernel (the fused prefill indexer / top-k) and of the decode
 kernels, the index projections, the two-tier (block -> token) selection variant of both
-steps, and the CPU oracle's throughput on a bounded sample ride along.
+steps, a chunked prefill against the paged caches, and the CPU oracle's throughput on a bounded
+sample ride along.
 
 HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
 calibrated on the 1 GiB copy it performs after the warm-up, and stored in
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--no-projections", action="store_true", help="skip the index-projection measurement")
     ap.add_argument("--no-two-tier", action="store_true", help="skip the two-tier (block -> token) measurement")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill (paged query rows) measurement")
+    ap.add_argument("--chunk", type=int, default=4096, help="chunked prefill: new tokens at the end of the context")
     ap.add_argument("--block-size", type=int, default=64, help="two-tier selection: tokens per block")
     ap.add_argument("--n-blocks", type=int, default=64, help="two-tier selection: blocks kept per query")
     return ap.parse_args()
@@ -239,6 +242,7 @@ def main():
 
     projections = None if args.no_projections else measure_projections(h_pre, P, L, args.steps, torch)
     two_tier = None if args.no_two_tier else measure_two_tier(cfg, P, D, L, K, args, torch)
+    chunk = None if args.no_chunk else measure_chunk(cfg, P, D, K, args, torch)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -272,6 +276,7 @@ def main():
         "peaks_measured": peaks,
         "projections": projections,
         "two_tier": two_tier,
+        "chunked_prefill": chunk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -395,6 +400,62 @@ def measure_two_tier(cfg, P, D, L, K, args, torch):
         res["prefill"] = {"ms": round(ms, 4), "tokens_per_s": round(L / (ms * 1e-3), 1), "kernels_ms": per}
         del out, idx, ws
     torch.cuda.empty_cache()
+    return res
+
+
+def measure_chunk(cfg, P, D, K, args, torch):
+    """Chunked prefill (not part of `value`): the last --chunk positions of sequence 0 of the decode
+    caches as query rows of sparse_attn_prefill_paged, each over its own causal prefix of the paged
+    caches; the query rows are the first rows of the prefill inputs (synthetic, same distribution)."""
+    import numpy as np
+
+    import indexer_selected_sparse_scores_amd as sa
+    dev = "cuda"
+    s = cfg
+    n = int(D["ctx_np"][0])
+    C = min(args.chunk, n, P["q"].shape[0])
+    pos = np.arange(n - C, n)
+    row_seq = torch.zeros(C, dtype=torch.int32, device=dev)
+    row_pos = torch.from_numpy(pos.astype(np.int32)).to(dev)
+    with sa.Handle(cfg) as h:
+        out = torch.empty((C, s.n_heads, s.d_v), device=dev)
+        idx = torch.empty((C, K), device=dev, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL_PAGED, C, n)
+
+        def run():
+            sa.sparse_attn_prefill_paged(h, P["q"][:C], P["q_idx"][:C], P["w"][:C], D["kv_pages"], None,
+                                         D["kidx_pages"], D["block_table"][:1], row_seq, row_pos, n, K, out, None,
+                                         idx, ws)
+
+        log(f"[bench] chunked prefill: {C} new tokens at positions {n - C}..{n - 1}")
+        run()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        sa.sparse_attn_profile(h, True)
+        reps = max(1, min(args.steps, 3))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        kern = sa.sparse_attn_profile_read(h)
+        sa.sparse_attn_check(h)
+        ms = e0.elapsed_time(e1) / reps
+        per = {k: round(v / reps, 4) for k, (v, c) in kern.items() if c}
+        del out, idx, ws
+    torch.cuda.empty_cache()
+    pairs = int((pos + 1).sum())
+    flops = pairs * 2 * s.n_idx_heads * s.d_idx
+    res = {"workload": f"{C} new tokens of one sequence at positions {n - C}..{n - 1} over its paged caches",
+           "ms": round(ms, 4), "tokens_per_s": round(C / (ms * 1e-3), 1), "kernels_ms": per}
+    if per.get("indexer"):
+        tf = flops / (per["indexer"] * 1e-3) / 1e12
+        res["indexer_roofline"] = {"kernel": "indexer_decode_kernel (one query row per workgroup column)",
+                                   "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                   "algorithmic_per_launch": f"{flops:.4g} flop = {pairs} causal pairs x "
+                                                             f"{2 * s.n_idx_heads * s.d_idx} flop, over all launches"}
     return res
 
 
