@@ -24,6 +24,9 @@ Stable Reinforcement Learning, and Verifiable Synthetic Data"):
   entries are read, and this composes with paged KV management), then the same steps.
 * ``prefill_paged`` -- query rows that each name their sequence and position in paged caches
   (chunked prefill, varlen batches): every row is one decode step of its sequence.
+* ``acceptance_rate`` / ``bin_percentiles`` -- the per-token acceptance rate between a dense and a
+  sparse next-token distribution and its lower-tail statistic per bin of positions, [P5] "Sparrow:
+  Sparse Rollout for Stable and Efficient Long-context RL of Large Language Models", section 3.1.
 * ``project`` / ``round_bf16`` / ``paged_slot`` -- the index projections of the [P1] section
   2.5 pseudocode (i_q = W_iq(q), i_k = W_ik(k)) as plain linear maps in double, the rounding
   of their bf16 outputs, and where a projected key lands in the paged index cache.
@@ -297,6 +300,50 @@ def prefill_paged(q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, row_s
                  rp[rows] + 1, top_k, k_max=top_k, scale=scale, d_v=d_v, with_scores=with_scores)
     res["rows"] = rows
     return res
+
+
+# ---------------------------------------------------------------------------------------
+# Acceptance rate between dense and sparse next-token distributions
+# ---------------------------------------------------------------------------------------
+def softmax(logits) -> np.ndarray:
+    """Row-wise softmax in float64 (max subtracted first)."""
+    x = np.asarray(logits, dtype=np.float64)
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def acceptance_rate(logits_p, logits_q) -> np.ndarray:
+    """Per-token acceptance rate, [P5] section 3.1: with p and q the softmax distributions of the
+    two logit rows over the vocabulary, alpha = E_{x~q}[min(p(x)/q(x), 1)] = sum_x min(p(x), q(x))
+    (the page prints the right-hand side as an expectation over the vocabulary; the sum is what the
+    left-hand side equals).  logits [T, V] -> alpha [T] float64."""
+    return np.minimum(softmax(logits_p), softmax(logits_q)).sum(axis=-1)
+
+
+def bin_percentiles(alpha, pos, bin_size: int, n_bins: int, percentile: float):
+    """Lower-tail statistic per bin of positions, [P5] section 3.1 (the 5-percentile of the
+    per-token acceptance rate in bins of 2K positions): token t falls in bin pos[t] // bin_size
+    (tokens outside [0, n_bins) are ignored).  Per bin: the count, the mean and the percentile of
+    its values, the percentile taken between order statistics as
+    h = (n - 1) percentile / 100, x[floor h] + (h - floor h) (x[floor h + 1] - x[floor h]) on the
+    ascending values x (NaN for an empty bin).  Returns (count int64, mean, pct) float64 arrays."""
+    a = np.asarray(alpha, dtype=np.float64)
+    b = np.asarray(pos, dtype=np.int64) // int(bin_size)
+    count = np.zeros(n_bins, dtype=np.int64)
+    mean = np.full(n_bins, np.nan)
+    pct = np.full(n_bins, np.nan)
+    for j in range(n_bins):
+        x = np.sort(a[b == j])
+        n = len(x)
+        count[j] = n
+        if n == 0:
+            continue
+        mean[j] = x.sum() / n
+        h = (n - 1) * percentile / 100.0
+        lo = int(math.floor(h))
+        hi = min(lo + 1, n - 1)
+        pct[j] = x[lo] + (h - lo) * (x[hi] - x[lo])
+    return count, mean, pct
 
 
 # ---------------------------------------------------------------------------------------
