@@ -11,8 +11,8 @@ Prints one JSON line: `value` is prefill tokens/s at 128K context; decode tokens
 per-kernel times (HIP events the library records around each launch on the launch stream),
 the roofline of the dominant kernel (the fused prefill indexer / top-k) and of the decode
 kernels, the index projections, the two-tier (block -> token) selection variant of both
-steps, a chunked prefill against the paged caches, and the CPU oracle's throughput on a bounded
-sample ride along.
+steps, a chunked prefill against the paged caches, the acceptance-rate statistic, and the CPU
+oracle's throughput on a bounded sample ride along.
 
 HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
 calibrated on the 1 GiB copy it performs after the warm-up, and stored in
@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--no-projections", action="store_true", help="skip the index-projection measurement")
     ap.add_argument("--no-two-tier", action="store_true", help="skip the two-tier (block -> token) measurement")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill (paged query rows) measurement")
+    ap.add_argument("--no-acceptance", action="store_true", help="skip the acceptance-rate measurement")
     ap.add_argument("--chunk", type=int, default=4096, help="chunked prefill: new tokens at the end of the context")
     ap.add_argument("--block-size", type=int, default=64, help="two-tier selection: tokens per block")
     ap.add_argument("--n-blocks", type=int, default=64, help="two-tier selection: blocks kept per query")
@@ -243,6 +244,7 @@ def main():
     projections = None if args.no_projections else measure_projections(h_pre, P, L, args.steps, torch)
     two_tier = None if args.no_two_tier else measure_two_tier(cfg, P, D, L, K, args, torch)
     chunk = None if args.no_chunk else measure_chunk(cfg, P, D, K, args, torch)
+    acceptance = None if args.no_acceptance else measure_acceptance(cfg, args, torch)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -277,6 +279,7 @@ def main():
         "projections": projections,
         "two_tier": two_tier,
         "chunked_prefill": chunk,
+        "acceptance": acceptance,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -456,6 +459,56 @@ def measure_chunk(cfg, P, D, K, args, torch):
                                    "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                                    "algorithmic_per_launch": f"{flops:.4g} flop = {pairs} causal pairs x "
                                                              f"{2 * s.n_idx_heads * s.d_idx} flop, over all launches"}
+    return res
+
+
+def measure_acceptance(cfg, args, torch, T=4096, V=151936):
+    """The per-token acceptance rate between dense and sparse next-token logits and its 5-percentile
+    per bin of 2048 positions (not part of `value`): T tokens over a vocabulary of V, fp32 logits
+    (synthetic, inputs.acceptance_inputs)."""
+    import indexer_selected_sparse_scores_amd as sa
+    from indexer_selected_sparse_scores_amd import inputs
+    dev = "cuda"
+    d = inputs.acceptance_inputs(T, V, dev)
+    n_bins = (T + 2047) // 2048
+    alpha = torch.empty(T, dtype=torch.float32, device=dev)
+    count = torch.empty(n_bins, dtype=torch.int32, device=dev)
+    mean = torch.empty(n_bins, dtype=torch.float32, device=dev)
+    pct = torch.empty(n_bins, dtype=torch.float32, device=dev)
+    log(f"[bench] acceptance rate T={T} V={V}")
+    with sa.Handle(cfg) as h:
+        def run():
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha)
+            sa.acceptance_bin_stats(h, alpha, d["pos"], 2048, n_bins, 5.0, count, mean, pct)
+
+        run()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        reps = max(1, args.steps)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for _ in range(reps):
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha)
+        ev[1].record()
+        for _ in range(reps):
+            sa.acceptance_bin_stats(h, alpha, d["pos"], 2048, n_bins, 5.0, count, mean, pct)
+        ev[2].record()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        a_ms = ev[0].elapsed_time(ev[1]) / reps
+        b_ms = ev[1].elapsed_time(ev[2]) / reps
+    nbytes = 2 * T * V * 4
+    gbs = nbytes / (a_ms * 1e-3) / 1e9
+    res = {"workload": f"{T} tokens x {V} vocabulary, fp32 logits, 5-percentile per 2048 positions",
+           "alpha_ms": round(a_ms, 4), "bin_stats_ms": round(b_ms, 4),
+           "tokens_per_s": round(T / ((a_ms + b_ms) * 1e-3), 1),
+           "roofline": {"kernel": "acceptance_rate_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "algorithmic_per_launch": f"{nbytes} B = {T} tokens x 2 rows x {V} x 4 B (each logit "
+                                                  f"read once)"},
+           "pct_5": [round(float(x), 5) for x in pct.cpu()], "mean": [round(float(x), 5) for x in mean.cpu()]}
+    del d
+    torch.cuda.empty_cache()
     return res
 
 

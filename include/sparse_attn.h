@@ -296,6 +296,30 @@ sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const voi
                               const int32_t *block_table, int32_t n_seqs, int32_t max_blocks, int64_t n_pages,
                               const int32_t *row_seq, const int32_t *row_pos, int64_t pos0, void *stream);
 
+/* Per-token acceptance rate between a dense and a sparse next-token distribution -- "Sparrow:
+ * Sparse Rollout for Stable and Efficient Long-context RL of Large Language Models", section 3.1:
+ * alpha(t) = E_{x~q}[min(p(x)/q(x), 1)] = sum_x min(p(x), q(x)), where p and q are the softmax of
+ * logit rows t of logits_p and logits_q over the vocabulary.
+ *   logits_p, logits_q [T, ld] fp32 (row t: entries 0 .. V-1); each row needs a finite entry
+ *   alpha [T] fp32 out, in [0, 1]
+ * Streams both rows twice (max and sum of exp, then the sum of minima); fp32 arithmetic.
+ * Needs no workspace.  Errors: SA_ERR_INVALID_ARG (NULL pointer, T < 1, V < 1, ld < V). */
+sa_status_t acceptance_rate(sa_handle_t h, const float *logits_p, const float *logits_q, int64_t T, int64_t V,
+                            int64_t ld, float *alpha, void *stream);
+
+/* The lower-tail statistic of the acceptance rate per bin of positions -- the same page and
+ * section (the 5-percentile of the per-token values in bins of 2K positions).  Token t falls in
+ * bin pos[t] / bin_size; tokens with a negative position or a bin >= n_bins are ignored.  Per
+ * bin j: count[j] tokens, mean[j] (NaN if empty) and pct[j] = x[lo] + (h - lo) (x[lo + 1] - x[lo])
+ * with x the bin's values ascending, h = (count - 1) percentile / 100 and lo = floor(h) (the value
+ * itself at the top rank; NaN if empty).
+ *   alpha [T] fp32, pos [T] int32; count [n_bins] int32 out, mean, pct [n_bins] fp32 out
+ * Needs no workspace.  Errors: SA_ERR_INVALID_ARG (NULL pointer, T < 1, bin_size < 1,
+ * n_bins < 1, percentile outside [0, 100]). */
+sa_status_t acceptance_bin_stats(sa_handle_t h, const float *alpha, const int32_t *pos, int64_t T,
+                                 int32_t bin_size, int32_t n_bins, float percentile, int32_t *count,
+                                 float *mean, float *pct, void *stream);
+
 /* Kernel timing, a tracing aid for benchmarks.  While enabled, every kernel the handle
  * launches is bracketed by a pair of hipEvents recorded on the launch stream, and the
  * elapsed times are summed per kernel kind.  Enabling resets the sums; it creates events
@@ -308,7 +332,8 @@ sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const voi
 #define SA_KERNEL_ATTENTION 2  /* attention over the selected rows                        */
 #define SA_KERNEL_MERGE     3  /* merge of split decode attention states                  */
 #define SA_KERNEL_PROJECT   4  /* index-space projections (indexer_project_q / _k)         */
-#define SA_KERNEL_COUNT     5
+#define SA_KERNEL_ACCEPT    5  /* acceptance rate and its per-bin statistics               */
+#define SA_KERNEL_COUNT     6
 sa_status_t sparse_attn_profile(sa_handle_t h, int enable);
 sa_status_t sparse_attn_profile_read(sa_handle_t h, double *total_ms, int64_t *launches);
 

@@ -36,8 +36,9 @@ EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error
             "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
             "topk_select_blocks", "sparse_attn_prefill", "sparse_attn_prefill_blocks", "sparse_attn_decode",
             "sparse_attn_decode_blocks", "sparse_attn_prefill_paged", "indexer_project_q", "indexer_project_k",
+            "acceptance_rate", "acceptance_bin_stats",
             "sparse_attn_profile", "sparse_attn_profile_read")
-KERNEL_KINDS = ("indexer", "topk", "attention", "merge", "project")
+KERNEL_KINDS = ("indexer", "topk", "attention", "merge", "project", "accept")
 
 
 class SparseAttnError(RuntimeError):
@@ -105,6 +106,8 @@ def load_library() -> ctypes.CDLL:
         "sparse_attn_prefill_paged": ([P, P, P, P, P, P, P, i64, P, i32, i32, P, P, i64, i32, i32, P, P, P, P, sz,
                                        P], st),
         "indexer_project_q": ([P, P, i64, P, P, P, P, P, sz, P], st),
+        "acceptance_rate": ([P, P, P, i64, i64, i64, P, P], st),
+        "acceptance_bin_stats": ([P, P, P, i64, i32, i32, ctypes.c_float, P, P, P, P], st),
         "indexer_project_k": ([P, P, i64, P, P, P, i32, i32, i64, P, P, i64, P], st),
         "sparse_attn_profile": ([P, ctypes.c_int], st),
         "sparse_attn_profile_read": ([P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
@@ -296,6 +299,25 @@ def indexer_project_k(h: Handle, k, W_ik, k_idx, block_table=None, n_pages: int 
     _check(h.ptr, load_library().indexer_project_k(h.ptr, _ptr(k), L, _ptr(W_ik), _ptr(k_idx), _ptr(block_table),
                                                    n_seqs, max_blocks, int(n_pages), _ptr(row_seq), _ptr(row_pos),
                                                    int(pos0), _stream(stream)))
+
+
+def acceptance_rate(h: Handle, logits_p, logits_q, alpha, V: int | None = None, stream=None) -> None:
+    """alpha[t] = sum_x min(softmax(logits_p[t])(x), softmax(logits_q[t])(x)) over the first V entries."""
+    T, ld = logits_p.shape
+    V = ld if V is None else V
+    if logits_q.shape != logits_p.shape:
+        raise ValueError("logits_p and logits_q must have the same shape")
+    _check(h.ptr, load_library().acceptance_rate(h.ptr, _ptr(logits_p), _ptr(logits_q), T, int(V), ld, _ptr(alpha),
+                                                 _stream(stream)))
+
+
+def acceptance_bin_stats(h: Handle, alpha, pos, bin_size: int, n_bins: int, percentile: float, count, mean, pct,
+                         stream=None) -> None:
+    """Per bin of positions (pos // bin_size): count, mean and the interpolated percentile of alpha."""
+    T = alpha.shape[0]
+    _check(h.ptr, load_library().acceptance_bin_stats(h.ptr, _ptr(alpha), _ptr(pos), T, int(bin_size), int(n_bins),
+                                                      float(percentile), _ptr(count), _ptr(mean), _ptr(pct),
+                                                      _stream(stream)))
 
 
 def sparse_attn_profile(h: Handle, enable: bool) -> None:

@@ -727,6 +727,40 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
                       "attention launch");
 }
 
+sa_status_t acceptance_rate(sa_handle_t h, const float *logits_p, const float *logits_q, int64_t T, int64_t V,
+                            int64_t ld, float *alpha, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!logits_p || !logits_q || !alpha) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (T < 1 || T > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T must be in [1, 2^31)");
+    if (V < 1 || ld < V) return fail(h, SA_ERR_INVALID_ARG, "need 1 <= V <= ld (V %lld, ld %lld)", (long long)V,
+                                     (long long)ld);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    return hip_status(h, sa::launch_acceptance_rate(*h, logits_p, logits_q, T, V, ld, alpha,
+                                                    reinterpret_cast<hipStream_t>(stream)),
+                      "acceptance-rate launch");
+}
+
+sa_status_t acceptance_bin_stats(sa_handle_t h, const float *alpha, const int32_t *pos, int64_t T, int32_t bin_size,
+                                 int32_t n_bins, float percentile, int32_t *count, float *mean, float *pct,
+                                 void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (!alpha || !pos || !count || !mean || !pct) return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (T < 1) return fail(h, SA_ERR_INVALID_ARG, "T must be >= 1");
+    if (bin_size < 1 || n_bins < 1) return fail(h, SA_ERR_INVALID_ARG, "bin_size and n_bins must be >= 1");
+    if (!(percentile >= 0.f && percentile <= 100.f))
+        return fail(h, SA_ERR_INVALID_ARG, "percentile must be in [0, 100]");
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    return hip_status(h, sa::launch_bin_stats(*h, alpha, pos, T, bin_size, n_bins, percentile, count, mean, pct,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      "bin statistics launch");
+}
+
 sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const void *W_iq, const void *W_w,
                               void *q_idx, float *w, void *ws, size_t ws_bytes, void *stream)
 {

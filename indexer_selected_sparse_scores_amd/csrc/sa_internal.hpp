@@ -156,6 +156,12 @@ hipError_t launch_paged_rows(sa_handle_s &h, const int32_t *row_seq, const int32
                              int32_t n_seqs, int32_t max_ctx, int32_t topk, int32_t *seq, int32_t *ctx,
                              int32_t *budget, hipStream_t st);
 
+// ---- acceptance rate between two next-token distributions ---------------------------------
+hipError_t launch_acceptance_rate(sa_handle_s &h, const float *lp, const float *lq, int64_t T, int64_t V, int64_t ld,
+                                  float *alpha, hipStream_t st);
+hipError_t launch_bin_stats(sa_handle_s &h, const float *alpha, const int32_t *pos, int64_t T, int32_t bin_size,
+                            int32_t n_bins, float percentile, int32_t *count, float *mean, float *pct, hipStream_t st);
+
 // ---- index-space projections (bf16) ---------------------------------------------------
 size_t projection_workspace();
 sa_status_t launch_project_q(sa_handle_s &h, const void *q, int64_t L, const void *W_iq, const void *W_w,

@@ -219,6 +219,20 @@ def paged_rows_inputs(wl: Workload, ctx, row_seq, row_pos, device="cuda", seed: 
     return d
 
 
+def acceptance_inputs(T: int, V: int, device="cuda", seed: int | None = None):
+    """Dense and sparse next-token logits for T tokens over a vocabulary of V (fp32, [T, V]):
+    dense z ~ N(0, 4) per entry; sparse z + d_t e with e ~ N(0, 1) per entry and one perturbation
+    scale per token d_t = 1.5 u_t^4, u_t ~ U(0, 1), so that most tokens stay nearly aligned and a
+    few diverge (a long tail of low acceptance rates).  Also positions pos [T] int32 = 0..T-1."""
+    seed = BASE_SEED + 50 if seed is None else seed
+    g = _gen(seed, device)
+    dense = torch.randn((T, V), generator=g, device=device, dtype=torch.float32) * 2.0
+    u = torch.rand((T, 1), generator=g, device=device, dtype=torch.float32)
+    sparse = dense + torch.randn((T, V), generator=g, device=device, dtype=torch.float32) * (1.5 * u ** 4)
+    pos = torch.arange(T, dtype=torch.int32, device=device)
+    return {"logits_p": dense, "logits_q": sparse, "pos": pos}
+
+
 def library_config(wl: Workload, max_topk: int | None = None):
     """The library configuration matching a workload's shapes."""
     from indexer_selected_sparse_scores_amd import Config
