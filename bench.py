@@ -57,6 +57,11 @@ def parse():
     ap.add_argument("--no-two-tier", action="store_true", help="skip the two-tier (block -> token) measurement")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill (paged query rows) measurement")
     ap.add_argument("--no-acceptance", action="store_true", help="skip the acceptance-rate measurement")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time the step alone (no projections, two-tier, chunked-prefill or acceptance legs)")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 FETCH_SIZE and WRITE_SIZE counter files of a "
+                         "--main-only run (no GPU needed)")
     ap.add_argument("--chunk", type=int, default=4096, help="chunked prefill: new tokens at the end of the context")
     ap.add_argument("--block-size", type=int, default=64, help="two-tier selection: tokens per block")
     ap.add_argument("--n-blocks", type=int, default=64, help="two-tier selection: blocks kept per query")
@@ -87,8 +92,66 @@ def stored_traffic(kernel: str):
     return rec["bytes_per_launch"]
 
 
+# Kernel -> the source files its code comes from (the stored traffic is valid while they are unchanged).
+KERNEL_SOURCES = {
+    "indexer_topk_prefill_kernel": ["prefill_topk.hip", "topk_device.hpp", "sa_device.hpp", "sa_internal.hpp"],
+    "attn_latent_mfma_kernel": ["attention.hip", "sa_device.hpp", "sa_internal.hpp"],
+    "indexer_decode_kernel": ["decode.hip", "topk_device.hpp", "sa_device.hpp", "sa_internal.hpp"],
+    "decode_topk_kernel": ["decode.hip", "topk_device.hpp", "sa_device.hpp", "sa_internal.hpp"],
+    "attn_decode_lds_kernel": ["attention.hip", "sa_device.hpp", "sa_internal.hpp"],
+    "attn_merge_kernel": ["attention.hip", "sa_device.hpp", "sa_internal.hpp"],
+}
+
+
+def ingest_traffic(fetch_csv: str, write_csv: str):
+    """profiles/traffic.json from the FETCH_SIZE and WRITE_SIZE counter files of two `--main-only`
+    runs: each counter (KiB per dispatch) is divided by what it reads for the 1 GiB calibration copy
+    (the dispatch right after the 1 GiB fill that creates its source), then averaged per kernel."""
+    import csv
+    import re
+
+    def load(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        cal = None
+        for i, r in enumerate(rows):
+            if "FillFunctor<unsigned char>" in r["Kernel_Name"] and int(r["Grid_Size"]) * 16 >= CALIBRATION_BYTES:
+                cal = float(rows[i + 1]["Counter_Value"]) * 1024 / CALIBRATION_BYTES
+        if cal is None:
+            raise SystemExit(f"{path}: no calibration copy found")
+        per = {}
+        for r in rows:
+            m = re.search(r"sa::\(anonymous namespace\)::(\w+)", r["Kernel_Name"])
+            if m and m.group(1) in KERNEL_SOURCES:
+                per.setdefault(m.group(1), []).append(float(r["Counter_Value"]))
+        return cal, {k: sum(v) / len(v) for k, v in per.items()}
+
+    f_cal, fetch = load(fetch_csv)
+    w_cal, write = load(write_csv)
+    out = {}
+    for k in KERNEL_SOURCES:
+        if k not in fetch or k not in write:
+            continue
+        rd = fetch[k] * 1024 / f_cal
+        wr = write[k] * 1024 / w_cal
+        out[k] = {"sources": KERNEL_SOURCES[k], "source_sha256": source_hash(KERNEL_SOURCES[k]),
+                  "fetch_size_kib": fetch[k], "write_size_kib": write[k], "read_bytes": int(rd),
+                  "write_bytes": int(wr), "bytes_per_launch": int(rd + wr),
+                  "calibration": {"copy_bytes": CALIBRATION_BYTES, "fetch_factor": f_cal, "write_factor": w_cal}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    for k, v in out.items():
+        print(f"{k}: read {v['read_bytes'] / 1e9:.4g} GB, write {v['write_bytes'] / 1e9:.4g} GB per launch")
+    print(f"wrote {path}")
+
+
 def main():
     args = parse()
+    if args.ingest_traffic:
+        ingest_traffic(*args.ingest_traffic)
+        return
+    if args.main_only:
+        args.no_projections = args.no_two_tier = args.no_chunk = args.no_acceptance = True
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
