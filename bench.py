@@ -471,8 +471,9 @@ def measure_two_tier(cfg, P, D, L, K, args, torch):
 
 def measure_chunk(cfg, P, D, K, args, torch):
     """Chunked prefill (not part of `value`): the last --chunk positions of sequence 0 of the decode
-    caches as query rows of sparse_attn_prefill_paged, each over its own causal prefix of the paged
-    caches; the query rows are the first rows of the prefill inputs (synthetic, same distribution)."""
+    caches as query rows, each over its own causal prefix of the paged caches, through
+    sparse_attn_prefill_chunk (fused row tiles) and through sparse_attn_prefill_paged (per-row path);
+    the query rows are the first rows of the prefill inputs (synthetic, same distribution)."""
     import numpy as np
 
     import indexer_selected_sparse_scores_amd as sa
@@ -488,40 +489,58 @@ def measure_chunk(cfg, P, D, K, args, torch):
         idx = torch.empty((C, K), device=dev, dtype=torch.int32)
         ws = sa.workspace(h, sa.SA_OP_PREFILL_PAGED, C, n)
 
-        def run():
+        ws_c = sa.workspace(h, sa.SA_OP_PREFILL_CHUNK, C, n)
+        table_row = D["block_table"][0].contiguous()
+
+        def run_rows():   # each row names its (sequence, position): the per-row path
             sa.sparse_attn_prefill_paged(h, P["q"][:C], P["q_idx"][:C], P["w"][:C], D["kv_pages"], None,
                                          D["kidx_pages"], D["block_table"][:1], row_seq, row_pos, n, K, out, None,
                                          idx, ws)
 
-        log(f"[bench] chunked prefill: {C} new tokens at positions {n - C}..{n - 1}")
-        run()
-        torch.cuda.synchronize()
-        sa.sparse_attn_check(h)
-        sa.sparse_attn_profile(h, True)
-        reps = max(1, min(args.steps, 3))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        def run_chunk():  # the chunk known on the host: fused row tiles over the pages
+            sa.sparse_attn_prefill_chunk(h, P["q"][:C], P["q_idx"][:C], P["w"][:C], D["kv_pages"], None,
+                                         D["kidx_pages"], table_row, n - C, K, out, None, idx, ws_c)
+
+        def timed(run):
             run()
-        e1.record()
-        torch.cuda.synchronize()
-        kern = sa.sparse_attn_profile_read(h)
-        sa.sparse_attn_check(h)
-        ms = e0.elapsed_time(e1) / reps
-        per = {k: round(v / reps, 4) for k, (v, c) in kern.items() if c}
-        del out, idx, ws
+            torch.cuda.synchronize()
+            sa.sparse_attn_check(h)
+            sa.sparse_attn_profile(h, True)
+            reps = max(1, min(args.steps, 3))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            kern = sa.sparse_attn_profile_read(h)
+            sa.sparse_attn_profile(h, False)
+            sa.sparse_attn_check(h)
+            return e0.elapsed_time(e1) / reps, {k: round(v / reps, 4) for k, (v, c) in kern.items() if c}
+
+        log(f"[bench] chunked prefill: {C} new tokens at positions {n - C}..{n - 1}")
+        ms_c, per_c = timed(run_chunk)
+        ms_r, per_r = timed(run_rows)
+        del out, idx, ws, ws_c
     torch.cuda.empty_cache()
     pairs = int((pos + 1).sum())
     flops = pairs * 2 * s.n_idx_heads * s.d_idx
+
+    def roof(kernel, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"kernel": kernel, "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_per_launch": f"{flops:.4g} flop = {pairs} causal pairs x "
+                                          f"{2 * s.n_idx_heads * s.d_idx} flop"}
+
     res = {"workload": f"{C} new tokens of one sequence at positions {n - C}..{n - 1} over its paged caches",
-           "ms": round(ms, 4), "tokens_per_s": round(C / (ms * 1e-3), 1), "kernels_ms": per}
-    if per.get("indexer"):
-        tf = flops / (per["indexer"] * 1e-3) / 1e12
-        res["indexer_roofline"] = {"kernel": "indexer_decode_kernel (one query row per workgroup column)",
-                                   "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                                   "algorithmic_per_launch": f"{flops:.4g} flop = {pairs} causal pairs x "
-                                                             f"{2 * s.n_idx_heads * s.d_idx} flop, over all launches"}
+           "ms": round(ms_c, 4), "tokens_per_s": round(C / (ms_c * 1e-3), 1), "kernels_ms": per_c,
+           "per_row_path": {"ms": round(ms_r, 4), "tokens_per_s": round(C / (ms_r * 1e-3), 1), "kernels_ms": per_r}}
+    if per_c.get("indexer"):
+        res["indexer_roofline"] = roof("indexer_topk_prefill_kernel (paged row tiles)", per_c["indexer"])
+    if per_r.get("indexer"):
+        res["per_row_path"]["indexer_roofline"] = roof("indexer_decode_kernel (one row per grid column, all launches)",
+                                                       per_r["indexer"])
     return res
 
 

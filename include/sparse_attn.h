@@ -91,6 +91,7 @@ typedef struct {
 #define SA_OP_PREFILL_BLOCKS 5  /* sparse_attn_prefill_blocks: n = L, max_ctx ignored     */
 #define SA_OP_DECODE_BLOCKS  6  /* sparse_attn_decode_blocks: as SA_OP_DECODE             */
 #define SA_OP_PREFILL_PAGED  7  /* sparse_attn_prefill_paged: n = T query rows, max_ctx   */
+#define SA_OP_PREFILL_CHUNK  8  /* sparse_attn_prefill_chunk: n = C rows, max_ctx = pos0 + C */
 
 /* Create a handle for one configuration.  Validates the config, allocates the 4-byte
  * device error word on the current device (the only device allocation the library makes)
@@ -256,6 +257,26 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
                                       int64_t n_pages, const int32_t *block_table, int32_t n_seqs,
                                       int32_t max_blocks, const int32_t *row_seq, const int32_t *row_pos,
                                       int64_t T, int32_t max_ctx, int32_t topk, float *out, float *lse,
+                                      int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Chunked prefill of one sequence against its paged caches: query row i is the token at position
+ * pos0 + i (i < C) of the sequence whose block-table row is block_table_row [max_blocks]; it sees the
+ * tokens 0 .. pos0 + i, which the caches must already hold.  The same computation as
+ * sparse_attn_prefill_paged with row_seq = 0, row_pos = pos0 + i, for the common case where the
+ * chunk is known on the host: with bf16, H_I = 64, d_I = 128 and 64-token pages (and pos0 + C <=
+ * 524288) the rows run as tiles of the fused prefill indexer / top-k, sharing every key tile (one
+ * page) between 8 rows -- "Sparse Attention and RL Optimization...", sections 2.2, 2.3 and 2.5;
+ * "Long-Context LLMs Explained...", section 2.3.
+ *   q [C, H, d_qk], q_idx [C, H_I, d_I], w [C, H_I] fp32; pools as in sparse_attn_decode
+ *   pos0 >= 0, C >= 1, pos0 + C <= max_blocks * page_size; topk in [1, max_topk]
+ *   out [C, H, d_v] fp32; lse [C, H] or NULL; idx_out [C, topk] or NULL (positions, ascending, -1 pad)
+ *   ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_PREFILL_CHUNK, C, pos0 + C)
+ * A block-table entry of a visible page outside [0, n_pages) sets SA_DEVERR_BLOCK_TABLE; its tokens are
+ * given no weight.  Errors: SA_ERR_INVALID_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP. */
+sa_status_t sparse_attn_prefill_chunk(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                      const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table_row, int32_t max_blocks,
+                                      int64_t pos0, int64_t C, int32_t topk, float *out, float *lse,
                                       int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Index-space projections -- the first lines of the "Sparse Attention and RL Optimization...",

@@ -141,6 +141,32 @@ PagedLayout paged_layout(const sa_handle_s &h, int64_t T, int64_t max_ctx)
     return p;
 }
 
+// Chunked prefill of one sequence (C rows at positions pos0 ..): fused path [idx | fused indexer/top-k
+// workspace]; generic path [scores of one block of rows | idx].
+bool chunk_fused(const sa_handle_s &h, int64_t pos0, int64_t C)
+{
+    return h.fast_decode && (pos0 + C + 63) / 64 <= sa::kPrefillMaxPages;
+}
+
+PrefillLayout chunk_layout(const sa_handle_s &h, int64_t pos0, int64_t C)
+{
+    PrefillLayout p;
+    const size_t idx_bytes = align_up((size_t)C * (size_t)h.cfg.max_topk * sizeof(int32_t));
+    if (chunk_fused(h, pos0, C)) {
+        p.idx = 0;
+        p.scores = idx_bytes;
+        p.total = p.scores + align_up(sa::prefill_topk_workspace(h, C, pos0));
+        return p;
+    }
+    const int64_t n = pos0 + C;
+    int64_t rows = (int64_t)(kPrefillChunkBytes / (sizeof(float) * (size_t)n));
+    rows = rows < 1 ? 1 : (rows > C ? C : rows);
+    p.scores = 0;
+    p.idx = align_up((size_t)rows * (size_t)n * sizeof(float));
+    p.total = p.idx + idx_bytes;
+    return p;
+}
+
 // Two-tier (block -> token) selection parameters; nullptr selects plain per-query top-k.
 struct BlockSelect {
     int32_t block_size, n_blocks;
@@ -349,6 +375,11 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
     case SA_OP_DECODE_BLOCKS:
         if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
         *bytes = decode_layout(*h, n, max_ctx).total;
+        return SA_OK;
+    case SA_OP_PREFILL_CHUNK:
+        if (n > INT32_MAX || max_ctx < n || max_ctx > INT32_MAX)
+            return fail(h, SA_ERR_INVALID_ARG, "need 1 <= C <= pos0 + C = max_ctx < 2^31");
+        *bytes = chunk_layout(*h, max_ctx - n, n).total;
         return SA_OK;
     case SA_OP_PREFILL_PAGED:
         if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T exceeds the launch limit");
@@ -725,6 +756,74 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
     sa::Selection sel{idx, topk, topk, nullptr};
     return hip_status(h, sa::launch_attention(*h, q, T, kv, vv, vis, sel, out, lse, base + lay.attn, st, lay.split),
                       "attention launch");
+}
+
+sa_status_t sparse_attn_prefill_chunk(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                      const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                      int64_t n_pages, const int32_t *block_table_row, int32_t max_blocks,
+                                      int64_t pos0, int64_t C, int32_t topk, float *out, float *lse,
+                                      int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    const sa_config_t &c = h->cfg;
+    if (!q || !q_idx || !w || !kv_pages || !kidx_pages || !block_table_row || !out)
+        return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (c.v_from_k ? v_pages != nullptr : v_pages == nullptr)
+        return fail(h, SA_ERR_INVALID_ARG, c.v_from_k ? "v_pages must be NULL when v_from_k = 1"
+                                                      : "v_pages must not be NULL when v_from_k = 0");
+    if (n_pages < 1) return fail(h, SA_ERR_INVALID_ARG, "n_pages must be >= 1");
+    if (max_blocks < 1) return fail(h, SA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+    if (pos0 < 0 || C < 1 || pos0 + C > (int64_t)max_blocks * c.page_size || pos0 + C > INT32_MAX)
+        return fail(h, SA_ERR_INVALID_ARG, "need pos0 >= 0, C >= 1, pos0 + C <= max_blocks * page_size = %lld",
+                    (long long)max_blocks * c.page_size);
+    if (topk < 1 || topk > c.max_topk)
+        return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
+    if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
+        (v_pages && !aligned16(v_pages)))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+    const PrefillLayout lay = chunk_layout(*h, pos0, C);
+    if (!ws || ws_bytes < lay.total)
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *base = reinterpret_cast<char *>(ws);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
+    const size_t es = elem_size(*h);
+    // every query row reads the one block-table row: a row stride of 0
+    sa::RowSource kv{kv_pages, (int64_t)c.n_kv_heads * c.d_qk, block_table_row, 0, c.page_size, n_pages};
+    sa::RowSource vv{v_pages, (int64_t)c.n_kv_heads * c.d_v, block_table_row, 0, c.page_size, n_pages};
+
+    if (chunk_fused(*h, pos0, C)) {
+        s = hip_status(h, sa::launch_prefill_topk(*h, q_idx, w, kidx_pages, C, topk, idx, base + lay.scores, st,
+                                                  block_table_row, n_pages, pos0),
+                       "indexer/top-k launch");
+        if (s != SA_OK) return s;
+    } else {
+        float *scores = reinterpret_cast<float *>(base + lay.scores);
+        sa::RowSource keys{kidx_pages, c.d_idx, block_table_row, 0, c.page_size, n_pages};
+        const int64_t n = pos0 + C;
+        int64_t chunk = (int64_t)(kPrefillChunkBytes / (sizeof(float) * (size_t)n));
+        chunk = chunk < 1 ? 1 : (chunk > C ? C : chunk);
+        if (chunk > 65535) chunk = 65535;
+        for (int64_t r0 = 0; r0 < C; r0 += chunk) {
+            const int64_t rows = r0 + chunk < C ? chunk : C - r0;
+            const int64_t cols = pos0 + r0 + rows;  // keys any row of the block can see
+            sa::Visibility vis{pos0 + r0, nullptr, 0};
+            s = hip_status(h, sa::launch_indexer(*h, reinterpret_cast<const char *>(q_idx) + r0 * c.n_idx_heads * c.d_idx * es,
+                                                 w + r0 * c.n_idx_heads, rows, keys, vis, scores, cols, cols, st),
+                           "indexer launch");
+            if (s != SA_OK) return s;
+            s = hip_status(h, sa::launch_topk(*h, scores, cols, rows, cols, nullptr, pos0 + r0, nullptr, topk,
+                                              idx + r0 * topk, topk, h->d_err, st),
+                           "top-k launch");
+            if (s != SA_OK) return s;
+        }
+    }
+    sa::Visibility vis{pos0, nullptr, 0};
+    sa::Selection sel{idx, topk, topk, nullptr};
+    return hip_status(h, sa::launch_attention(*h, q, C, kv, vv, vis, sel, out, lse, nullptr, st), "attention launch");
 }
 
 sa_status_t acceptance_rate(sa_handle_t h, const float *logits_p, const float *logits_q, int64_t T, int64_t V,

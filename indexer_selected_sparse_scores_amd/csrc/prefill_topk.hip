@@ -24,6 +24,9 @@
 //    scores lie in bins >= b, no score in a lower bin can be selected.  Only scores in bins
 //    >= the running threshold are appended (ballot-compacted, in key order) to the row's
 //    candidate list in the workspace -- about m (1 + ln(t/m)) of the t+1 scores.
+//  * Query rows may be a chunk of a longer sequence (positions pos0 ..), and the keys may come from
+//    the 64-token pages of the sequence's block-table row: a key tile is then one page, whose pool
+//    page is looked up once per row tile and kept in LDS (chunked prefill against a paged cache).
 //  * At the end of the tile the final histogram fixes the threshold bin b* exactly.  The
 //    candidates in bins >= b* are gathered into LDS (at most kCap; otherwise the list is
 //    scanned in global memory), an MSD radix select over the remaining 21 key bits finds the
@@ -59,6 +62,7 @@ using topk::kPerThread;
 
 static_assert(kRows * kBins * 4 == kCap * 8, "the histogram region holds the candidates");
 
+template <bool kPaged>
 struct Shared {
     uint4 keys[kBufs][kKT * kChunks];    // key tiles in fragment order
     uint32_t region[kRows * kBins];      // 64 KB: histograms, then candidate (key, index)
@@ -66,6 +70,16 @@ struct Shared {
     int info[kRows][4];                  // per row: b*, count in bins > b*, count in bins >= b*,
                                          // candidate list length
     int tile;
+    int32_t pages[kPaged ? kPrefillMaxPages : 1];  // pool page of each 64-key tile (-1: bad entry)
+};
+
+// Where the index keys come from: contiguous rows, or the 64-token pages of one sequence's block-table
+// row (a key tile is exactly one page).
+struct KeySource {
+    const uint16_t *base;
+    const int32_t *table;   // paged: the sequence's block-table row
+    int64_t n_pages;
+    uint32_t *err;
 };
 
 // Key tile layout: the 16-byte piece holding dims 8 j .. 8 j + 7 of key r sits at
@@ -92,12 +106,16 @@ __device__ __forceinline__ void step_pattern()
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
 }
 
+// Query rows i = 0 .. L-1 are the tokens at positions pos0 + i of one sequence; keys are its tokens
+// 0 .. pos0 + L - 1 (contiguous rows, or pages of its block-table row when kPaged).
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
-    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ k_idx,
-    int64_t L, int32_t topk, int32_t *__restrict__ idx, uint2 *__restrict__ cands, int64_t cand_ld,
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KeySource ks, int64_t L, int64_t pos0,
+    int32_t topk, int32_t *__restrict__ idx, uint2 *__restrict__ cands, int64_t cand_ld,
     int32_t *__restrict__ counter, int32_t n_tiles)
 {
-    __shared__ Shared sh;
+    __shared__ Shared<kPaged> sh;
+    const uint16_t *__restrict__ k_idx = ks.base;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     uint2 *my_cands = cands + ((int64_t)blockIdx.x * kRows + wave) * cand_ld;
 
@@ -108,20 +126,33 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
         const int it = sh.tile;
         if (it >= n_tiles) break;
         const int64_t q0 = (int64_t)(n_tiles - 1 - it) * kRows;  // latest rows first
-        const int64_t t_last = (q0 + kRows - 1 < L - 1) ? q0 + kRows - 1 : L - 1;
-        const int64_t row = q0 + wave;
-        const bool row_ok = row < L;
+        // position of the tile's last row (keys 0 .. t_last are streamed)
+        const int64_t t_last = pos0 + ((q0 + kRows - 1 < L - 1) ? q0 + kRows - 1 : L - 1);
+        const int64_t ri = q0 + wave;    // this wave's query row
+        const int64_t row = pos0 + ri;   // and its position: it sees keys 0 .. row
+        const bool row_ok = ri < L;
         const int m = row_ok ? (int)((int64_t)topk < row + 1 ? (int64_t)topk : row + 1) : 0;
         const bool selects = row_ok && row + 1 > topk;  // fewer than all visible keys
         int n_cand = 0;                                    // this row's candidate list length
 
         if (t_last + 1 > topk) {  // some row of the tile needs scores
             for (int i = tid; i < kRows * kBins; i += kThreads) sh.region[i] = 0;
+            if constexpr (kPaged) {
+                // the pool page of every key tile of the prefix, checked once (a bad entry is read as page 0
+                // and its keys score -inf)
+                for (int j = tid; j <= (int)(t_last / kKT); j += kThreads) {
+                    const int32_t pg = ks.table[j];
+                    const bool ok = pg >= 0 && pg < ks.n_pages;
+                    if (!ok) flag_error(ks.err, SA_DEVERR_BLOCK_TABLE);
+                    sh.pages[j] = ok ? pg : -1;
+                }
+                __syncthreads();
+            }
 
             // A operand and weights of this wave's query row
             bf16x8 a[2][kD / 16];
             float wv[2][16];
-            const int64_t qrow = row_ok ? row : L - 1;
+            const int64_t qrow = row_ok ? ri : L - 1;
             const uint16_t *qr = q_idx + qrow * (int64_t)kH * kD;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -137,12 +168,19 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             // key tile loader: thread i moves chunks i and i + 512 of the 1024 in a tile
             const int n_kt = (int)(t_last / kKT) + 1;
             auto load_tile = [&](int kt, uint4 (&v)[kTileLoads]) {
+                // paged: every key of tile kt (a clamped one too: t_last lies in the last tile) is in
+                // page pages[kt], one uniform value per tile
+                int64_t shift = 0;
+                if constexpr (kPaged) {
+                    const int32_t pg = __builtin_amdgcn_readfirstlane(sh.pages[kt]);
+                    shift = ((int64_t)(pg >= 0 ? pg : 0) - kt) * kKT;
+                }
 #pragma unroll
                 for (int u = 0; u < kTileLoads; ++u) {
                     const int c = tid + u * kThreads;
                     int64_t s = (int64_t)kt * kKT + chunk_key(c);
                     if (s > t_last) s = t_last;
-                    v[u] = load16(k_idx + s * kD + 8 * chunk_col(c));
+                    v[u] = load16(k_idx + (s + shift) * kD + 8 * chunk_col(c));
                 }
             };
             auto store_tile = [&](int buf, const uint4 (&v)[kTileLoads]) {
@@ -182,9 +220,16 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             auto finish_window = [&](float part_odd, float part_even, uint32_t sb) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part_odd),
                                                                  __float_as_uint(part_even), false, false);
-                const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                 const bool vis = sb >= 32u && sb <= vis_hi;
                 const uint32_t s = sb - 32u;
+                if constexpr (kPaged) {
+                    // lanes 0-31 hold keys of tile kw - 1, lanes 32-63 of tile kw; keys of a bad page score -inf
+                    const int kw = __builtin_amdgcn_readfirstlane((int)(sb / kKT));
+                    const bool bad_lo = kw >= 1 && sh.pages[kw - 1] < 0;
+                    const bool bad_hi = sh.pages[kw < kPrefillMaxPages ? kw : kPrefillMaxPages - 1] < 0;
+                    if (vis && (lane < 32 ? bad_lo : bad_hi)) score = -__builtin_inff();
+                }
                 const uint32_t key = order_key(score);
                 atomicAdd(&hist[key >> kBinShift], vis ? 1u : 0u);
                 const bool keep = vis && (int)(key >> kBinShift) >= run_bin;
@@ -286,8 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             const int64_t rr = q0 + r;
             if (rr >= L) break;
             int32_t *dst = idx + rr * topk;
-            if (rr + 1 <= topk) {  // every visible key is selected
-                for (int i = tid; i < topk; i += kThreads) dst[i] = i <= rr ? i : -1;
+            const int64_t pr = pos0 + rr;  // the row's position
+            if (pr + 1 <= topk) {  // every visible key is selected
+                for (int i = tid; i < topk; i += kThreads) dst[i] = i <= pr ? i : -1;
                 continue;
             }
             const int mr = topk;
@@ -336,29 +382,36 @@ __global__ void reset_counter_kernel(int32_t *counter) { *counter = 0; }
 
 }  // namespace
 
-size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L)
+size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L, int64_t pos0)
 {
     const int64_t n_tiles = (L + kRows - 1) / kRows;
     const int64_t slots = n_tiles < h.n_cu ? n_tiles : h.n_cu;
-    const int64_t ld = (L + 63) / 64 * 64;
+    const int64_t ld = (pos0 + L + 63) / 64 * 64;  // a candidate list holds at most every key
     return 256 + (size_t)slots * kRows * (size_t)ld * sizeof(uint2);
 }
 
 hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
-                               int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st)
+                               int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st,
+                               const int32_t *table, int64_t n_pages, int64_t pos0)
 {
     const int64_t n_tiles = (L + kRows - 1) / kRows;
     const int64_t slots = n_tiles < h.n_cu ? n_tiles : h.n_cu;
-    const int64_t ld = (L + 63) / 64 * 64;
+    const int64_t ld = (pos0 + L + 63) / 64 * 64;
     int32_t *counter = reinterpret_cast<int32_t *>(ws);
     uint2 *cands = reinterpret_cast<uint2 *>(reinterpret_cast<char *>(ws) + 256);
     hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(1), 0, st, counter);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const KeySource ks{reinterpret_cast<const uint16_t *>(k_idx), table, n_pages, h.d_err};
     KernelTimer timer(h, SA_KERNEL_INDEXER, st);
-    hipLaunchKernelGGL(indexer_topk_prefill_kernel, dim3((unsigned)slots), dim3(kThreads), 0, st,
-                       reinterpret_cast<const uint16_t *>(q_idx), w, reinterpret_cast<const uint16_t *>(k_idx),
-                       L, topk, idx, cands, ld, counter, (int32_t)n_tiles);
+    if (table)
+        hipLaunchKernelGGL(indexer_topk_prefill_kernel<true>, dim3((unsigned)slots), dim3(kThreads), 0, st,
+                           reinterpret_cast<const uint16_t *>(q_idx), w, ks, L, pos0, topk, idx, cands, ld, counter,
+                           (int32_t)n_tiles);
+    else
+        hipLaunchKernelGGL(indexer_topk_prefill_kernel<false>, dim3((unsigned)slots), dim3(kThreads), 0, st,
+                           reinterpret_cast<const uint16_t *>(q_idx), w, ks, L, pos0, topk, idx, cands, ld, counter,
+                           (int32_t)n_tiles);
     return hipGetLastError();
 }
 

@@ -117,10 +117,15 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows,
                             float *out, float *lse, void *ws, hipStream_t st, bool allow_split = true);
 
 // ---- fused prefill indexer + streaming top-k (bf16, H_I = 64, d_I = 128) ---------------
-// idx [L, topk] gets every row's selection; ws holds prefill_topk_workspace(h, L) bytes.
-size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L);
+// idx [L, topk] gets every row's selection; ws holds prefill_topk_workspace(h, L, pos0) bytes.
+// Row i is the token at position pos0 + i; keys are the tokens 0 .. pos0 + L - 1: rows of k_idx, or
+// (table != nullptr) 64-token pages of the pool k_idx [n_pages, 64, d_I], page j of the sequence
+// being table[j] (table holds at most kPrefillMaxPages entries for the keys).
+constexpr int64_t kPrefillMaxPages = 8192;
+size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L, int64_t pos0 = 0);
 hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
-                               int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st);
+                               int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st,
+                               const int32_t *table = nullptr, int64_t n_pages = 0, int64_t pos0 = 0);
 
 // ---- paged decode indexer + per-sequence top-k (bf16, H_I = 64, d_I = 128, 64-token pages) --
 struct DecodeTopkLayout {

@@ -186,3 +186,118 @@ def test_chunk_at_128k():
     _check(d, out, lse, idx, [0, 1, 1000, T - 2, T - 1], 2048, 512, "prefill_paged 128k chunk")
     del d, out, lse, idx
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------
+# sparse_attn_prefill_chunk: one sequence, rows at positions pos0 .. pos0 + C - 1
+# ---------------------------------------------------------------------------------------
+def _run_chunk(h, d, pos0, C, topk, table_row=0, rows=None, check=True):
+    s = h.cfg
+    sl = slice(None) if rows is None else rows
+    q, qi, w = d["q"][sl], d["q_idx"][sl], d["w"][sl]
+    out = torch.empty((C, s.n_heads, s.d_v), device=DEV, dtype=torch.float32)
+    lse = torch.empty((C, s.n_heads), device=DEV, dtype=torch.float32)
+    idx = torch.empty((C, topk), device=DEV, dtype=torch.int32)
+    ws = sa.workspace(h, sa.SA_OP_PREFILL_CHUNK, C, pos0 + C)
+    sa.sparse_attn_prefill_chunk(h, q.contiguous(), qi.contiguous(), w.contiguous(), d["kv_pages"], d["v_pages"],
+                                 d["kidx_pages"], d["block_table"][table_row].contiguous(), pos0, topk, out, lse, idx,
+                                 ws)
+    if check:
+        assert sa.sparse_attn_check(h) == 0
+    return out, lse, idx
+
+
+def test_chunk_of_one_sequence_matches_the_oracle():
+    """Positions 2000..2999 of a 3000-token paged sequence through the fused row tiles."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    n, pos0 = 3000, 2000
+    say(f"prefill_chunk: positions {pos0}..{n - 1} of a {n}-token sequence, topk=256")
+    pos = np.arange(pos0, n)
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=256), [n], np.zeros(len(pos), np.int64), pos, DEV, seed=31)
+    with sa.Handle(inputs.library_config(wl, max_topk=256)) as h:
+        out, lse, idx = _run_chunk(h, d, pos0, len(pos), 256)
+    rows = np.concatenate([np.arange(6), [len(pos) - 2, len(pos) - 1], np.random.default_rng(5).integers(0, len(pos), 20)])
+    _check(d, out, lse, idx, rows, 256, 512, "prefill_chunk")
+
+
+def test_chunks_equal_the_contiguous_prefill_bit_for_bit():
+    """Two chunks (0..1499, 1500..2999) over shuffled pages give exactly what sparse_attn_prefill gives on
+    the same sequence laid out contiguously: the same fused kernel, the same keys in the same order."""
+    wl = inputs.WORKLOADS["prefill_8k"]
+    L, split = 3000, 1500
+    say(f"prefill_chunk x2 vs sparse_attn_prefill, L={L}, topk=512")
+    P = inputs.prefill_inputs(wl, DEV, L=L)
+    page = 64
+    n_pages = (L + page - 1) // page
+    perm = torch.from_numpy(np.random.default_rng(6).permutation(n_pages).astype(np.int64)).to(DEV)
+    pad = n_pages * page - L
+    k_pad = torch.cat([P["k"].reshape(L, -1), torch.zeros((pad, P["k"].shape[-1] * P["k"].shape[1]), dtype=P["k"].dtype,
+                                                            device=DEV)])
+    ki_pad = torch.cat([P["k_idx"], torch.zeros((pad, P["k_idx"].shape[1]), dtype=P["k_idx"].dtype, device=DEV)])
+    kv_pages = torch.empty((n_pages, page, 1, k_pad.shape[1]), dtype=k_pad.dtype, device=DEV)
+    kidx_pages = torch.empty((n_pages, page, ki_pad.shape[1]), dtype=ki_pad.dtype, device=DEV)
+    kv_pages[perm] = k_pad.reshape(n_pages, page, 1, -1)
+    kidx_pages[perm] = ki_pad.reshape(n_pages, page, -1)
+    table = perm.to(torch.int32).reshape(1, -1)
+    d = {"q": P["q"], "q_idx": P["q_idx"], "w": P["w"], "kv_pages": kv_pages, "v_pages": None,
+         "kidx_pages": kidx_pages, "block_table": table}
+    with sa.Handle(inputs.library_config(wl, max_topk=512)) as h:
+        o1, l1, i1 = _run_chunk(h, d, 0, split, 512, rows=slice(0, split))
+        o2, l2, i2 = _run_chunk(h, d, split, L - split, 512, rows=slice(split, L))
+        out = torch.empty((L, 16, 512), device=DEV)
+        lse = torch.empty((L, 16), device=DEV)
+        idx = torch.empty((L, 512), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL, L)
+        sa.sparse_attn_prefill(h, P["q"], P["k"], None, P["q_idx"], P["w"], P["k_idx"], 512, out, lse, idx, ws)
+        assert sa.sparse_attn_check(h) == 0
+    assert torch.equal(torch.cat([i1, i2]), idx)
+    assert torch.equal(torch.cat([o1, o2]), out)
+    assert torch.equal(torch.cat([l1, l2]), lse)
+
+
+def test_chunk_generic_kernels_fp32():
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], shapes=inputs.TINY, topk=16)
+    n, pos0 = 333, 200
+    say(f"prefill_chunk tiny (fp32, generic kernels): positions {pos0}..{n - 1}, topk=16")
+    pos = np.arange(pos0, n)
+    d = inputs.paged_rows_inputs(wl, [n], np.zeros(len(pos), np.int64), pos, DEV, seed=32)
+    with sa.Handle(inputs.library_config(wl, max_topk=16)) as h:
+        out, lse, idx = _run_chunk(h, d, pos0, len(pos), 16)
+    _check(d, out, lse, idx, np.arange(len(pos)), 16, 64, "prefill_chunk tiny", latent=False)
+
+
+def test_chunk_with_a_bad_page_entry():
+    """A bad block-table entry among the visible pages is flagged; its tokens get no weight and every
+    other token is unaffected (rows before that page are exact)."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    n, pos0 = 1000, 600
+    say("prefill_chunk with a corrupted block-table entry (page 3)")
+    pos = np.arange(pos0, n)
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=64), [n], np.zeros(len(pos), np.int64), pos, DEV, seed=33)
+    bt = d["block_table"].clone()
+    bt[0, 3] = 10 ** 6
+    d2 = dict(d, block_table=bt)
+    with sa.Handle(inputs.library_config(wl, max_topk=64)) as h:
+        out, lse, idx = _run_chunk(h, d2, pos0, len(pos), 64, check=False)
+        bits = ctypes.c_uint32()
+        st = sa.load_library().sparse_attn_check(h.ptr, torch.cuda.current_stream().cuda_stream, ctypes.byref(bits))
+        assert st == sa.SA_ERR_DEVICE_CHECK and bits.value & sa.SA_DEVERR_BLOCK_TABLE
+    assert torch.isfinite(out).all()
+    gi = to_np(idx)
+    # a selected token of the bad page (192..255) can only be there as a -inf score, i.e. never while
+    # enough finite ones exist
+    assert not np.any((gi >= 192) & (gi < 256))
+
+
+def test_prefill_chunk_at_128k():
+    """The chunk the benchmark times through the fused row tiles: the last 4096 positions of a 131072-token
+    paged sequence."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    n, C = 131072, 4096
+    say(f"prefill_chunk of {C} at the end of a {n}-token sequence, topk=2048 (5 rows checked)")
+    d = inputs.paged_rows_inputs(wl, [n], np.zeros(C, np.int64), np.arange(n - C, n), DEV, seed=34)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _run_chunk(h, d, n - C, C, 2048)
+    _check(d, out, lse, idx, [0, 1, 2000, C - 2, C - 1], 2048, 512, "prefill_chunk 128k")
+    del d, out, lse, idx
+    torch.cuda.empty_cache()
