@@ -88,6 +88,23 @@ PrefillLayout prefill_layout(const sa_handle_s &h, int64_t L, bool chunked = fal
     return p;
 }
 
+// Two-tier prefill on the fused kernels: [idx | tile counter | block keys [L, ceil(L / 64)] uint32].
+struct BlocksFusedLayout {
+    size_t idx, counter, keys, total;
+};
+
+BlocksFusedLayout blocks_fused_layout(const sa_handle_s &h, int64_t L)
+{
+    BlocksFusedLayout b;
+    b.idx = 0;
+    b.counter = align_up((size_t)L * (size_t)h.cfg.max_topk * sizeof(int32_t));
+    b.keys = b.counter + kAlign;
+    b.total = b.keys + align_up((size_t)L * sa::prefill_block_keys_ld(L, 0) * sizeof(uint32_t));
+    return b;
+}
+
+bool blocks_fused(const sa_handle_s &h, int32_t block_size) { return h.fast_indexer && block_size >= 64; }
+
 struct DecodeLayout {
     size_t scores, idx, attn, total;
 };
@@ -370,6 +387,11 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
     case SA_OP_PREFILL_BLOCKS:
         if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "L exceeds int32 token indices");
         *bytes = prefill_layout(*h, n, op == SA_OP_PREFILL_BLOCKS).total;
+        if (op == SA_OP_PREFILL_BLOCKS && h->fast_indexer) {
+            // the block size is not known here: room for either two-tier path
+            const size_t fused = blocks_fused_layout(*h, n).total;
+            if (fused > *bytes) *bytes = fused;
+        }
         return SA_OK;
     case SA_OP_DECODE:
     case SA_OP_DECODE_BLOCKS:
@@ -541,13 +563,37 @@ sa_status_t prefill_impl(sa_handle_t h, const void *q, const void *k, const void
         const sa_status_t sb = check_block_select(h, *blocks, L);
         if (sb != SA_OK) return sb;
     }
+    const bool fused_blocks = blocks && blocks_fused(*h, blocks->block_size);
     const PrefillLayout lay = prefill_layout(*h, L, blocks != nullptr);
-    if (!ws || ws_bytes < lay.total)
-        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
+    const size_t need = fused_blocks ? blocks_fused_layout(*h, L).total : lay.total;
+    if (!ws || ws_bytes < need)
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
     sa_status_t s = check_device(h);
     if (s != SA_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     char *base = reinterpret_cast<char *>(ws);
+    if (fused_blocks) {
+        // the fused indexer writes each row's best score per 64-key tile; the kept blocks' tokens are then
+        // scored again (bit-identical scores) and selected per row
+        const BlocksFusedLayout bl = blocks_fused_layout(*h, L);
+        int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + bl.idx);
+        uint32_t *keys = reinterpret_cast<uint32_t *>(base + bl.keys);
+        s = hip_status(h, sa::launch_prefill_topk(*h, q_idx, w, k_idx, L, topk, idx, base + bl.counter, st, nullptr, 0,
+                                                  0, keys, (int64_t)blocks->n_blocks * blocks->block_size),
+                       "block-key launch");
+        if (s != SA_OK) return s;
+        s = hip_status(h, sa::launch_block_rescore_topk(*h, q_idx, w, k_idx, nullptr, 0, L, 0, topk, blocks->block_size,
+                                                        blocks->n_blocks, keys, (int64_t)sa::prefill_block_keys_ld(L, 0),
+                                                        idx, st),
+                       "block rescore launch");
+        if (s != SA_OK) return s;
+        sa::RowSource kv{k, (int64_t)c.n_kv_heads * c.d_qk, nullptr, 0, 0, 0};
+        sa::RowSource vv{v, (int64_t)c.n_kv_heads * c.d_v, nullptr, 0, 0, 0};
+        sa::Visibility vis{0, nullptr, 0};
+        sa::Selection sel{idx, topk, topk, nullptr};
+        return hip_status(h, sa::launch_attention(*h, q, L, kv, vv, vis, sel, out, lse, nullptr, st),
+                          "attention launch");
+    }
     float *scores = reinterpret_cast<float *>(base + lay.scores);
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
     const size_t es = elem_size(*h);

@@ -69,35 +69,15 @@ __device__ __forceinline__ uint32_t group_max(uint32_t x, int g)
     return x;
 }
 
-__global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
-    const float *__restrict__ scores, int64_t ld, int64_t cols, const int32_t *__restrict__ valid_len,
-    int64_t causal_row0, const int32_t *__restrict__ k_per_row, int32_t k, int32_t bs_shift,
-    int32_t n_blocks, const uint32_t *__restrict__ pmax, int64_t pmax_ld, int32_t *__restrict__ idx,
-    int64_t idx_ld, uint32_t *err)
+// Steps 1 and 2 for one row: the key of every block's best score (from the row's scores, or from the
+// maxima of its 64-token spans when pmax != nullptr) and the `kept` best blocks, written ascending to
+// sh.kept.  Every thread of the workgroup calls it; it ends with a barrier.
+template <class Sh>
+__device__ void select_kept_blocks(Sh &sh, const float *__restrict__ row, const uint32_t *__restrict__ pmax,
+                                   int64_t n, int bs_shift, int kept, int n_blk)
 {
-    __shared__ BlockTopkShared sh;
-    const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
-    const float *row = scores + r * ld;
-    int32_t *dst = idx + r * idx_ld;
-
-    int64_t n;
-    if (valid_len) {
-        n = valid_len[r];
-    } else {
-        n = causal_row0 + r + 1;
-        if (n > cols) n = cols;
-    }
-    const int64_t kr = k_per_row ? (int64_t)k_per_row[r] : (int64_t)k;
-    if (n < 1 || n > cols || kr < 1 || kr > k) {
-        if (tid == 0) flag_error(err, SA_DEVERR_TOPK);
-        for (int64_t i = tid; i < idx_ld; i += kThreads) dst[i] = -1;
-        return;
-    }
     const int bs = 1 << bs_shift;
-    const int n_blk = (int)((n + bs - 1) >> bs_shift);  // <= kBlockSelectMaxItems (host check)
-    const int kept = n_blocks < n_blk ? n_blocks : n_blk;
-
     for (int j = tid; j < kBins; j += kThreads) sh.hist[j] = 0;
     if (bs > kWave)
         for (int j = tid; j < n_blk; j += kThreads) sh.key[j] = 0;
@@ -108,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
         // from the maxima of the 64-token spans (block_size >= 64): block j covers spans
         // j * bs / 64 .. (j + 1) * bs / 64 - 1
         const int n64 = (int)((n + kWave - 1) / kWave), sh64 = bs_shift - 6;
-        const uint32_t *prow = pmax + r * pmax_ld;
+        const uint32_t *prow = pmax;
         for (int j = tid; j < n64; j += kThreads) {
             const uint32_t x = prow[j];
             if (sh64 == 0) sh.key[j] = x;
@@ -157,6 +137,38 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
         topk::select_and_emit<kWaves>(sh.sel, BlockKeys{sh.key}, n_blk, sh.bin, sh.above, kept, sh.kept);
     }
     __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
+    const float *__restrict__ scores, int64_t ld, int64_t cols, const int32_t *__restrict__ valid_len,
+    int64_t causal_row0, const int32_t *__restrict__ k_per_row, int32_t k, int32_t bs_shift,
+    int32_t n_blocks, const uint32_t *__restrict__ pmax, int64_t pmax_ld, int32_t *__restrict__ idx,
+    int64_t idx_ld, uint32_t *err)
+{
+    __shared__ BlockTopkShared sh;
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float *row = scores + r * ld;
+    int32_t *dst = idx + r * idx_ld;
+
+    int64_t n;
+    if (valid_len) {
+        n = valid_len[r];
+    } else {
+        n = causal_row0 + r + 1;
+        if (n > cols) n = cols;
+    }
+    const int64_t kr = k_per_row ? (int64_t)k_per_row[r] : (int64_t)k;
+    if (n < 1 || n > cols || kr < 1 || kr > k) {
+        if (tid == 0) flag_error(err, SA_DEVERR_TOPK);
+        for (int64_t i = tid; i < idx_ld; i += kThreads) dst[i] = -1;
+        return;
+    }
+    const int bs = 1 << bs_shift;
+    const int n_blk = (int)((n + bs - 1) >> bs_shift);  // <= kBlockSelectMaxItems (host check)
+    const int kept = n_blocks < n_blk ? n_blocks : n_blk;
+
+    select_kept_blocks(sh, row, pmax ? pmax + r * pmax_ld : nullptr, n, bs_shift, kept, n_blk);
 
     // 3. candidates: the visible tokens of the kept blocks, ascending
     const int last = sh.kept[kept - 1];
@@ -188,7 +200,144 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
     for (int64_t i = m + tid; i < idx_ld; i += kThreads) dst[i] = -1;
 }
 
+// ---------------------------------------------------------------------------------------
+// Two-tier prefill, second pass (bf16, H_I = 64, d_I = 128, blocks of a multiple of 64 tokens): the fused
+// prefill kernel has left, for every row with more than n_blocks blocks, the order key of its best score
+// in each 64-key tile.  One workgroup per row picks the kept blocks from those keys, scores only their
+// tokens -- q of the row and its head weights in LDS, each wave taking 32 candidates at a time as the B
+// operand of v_mfma_f32_32x32x16_bf16, with the fused kernel's k-step and epilogue order, so that every
+// score equals the one the first pass saw bit for bit -- and selects the top k of them.
+// ---------------------------------------------------------------------------------------
+constexpr int kRH = 64;   // index heads
+constexpr int kRD = 128;  // index head width
+
+struct RescoreShared {
+    uint4 qf[2 * (kRD / 16) * kWave];     // q fragment (mt, ks) of lane l at (8 mt + ks) * 64 + l (16 KB)
+    float wv[kRH];
+    uint32_t key[kBlockSelectMaxItems];   // block keys, then candidate keys
+    alignas(16) uint32_t hist[kBins];
+    int32_t kept[kBlockSelectMaxKept];
+    topk::SelectShared<kWaves> sel;
+    int bin, above;
+};
+
+__global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
+    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ k_idx,
+    const int32_t *__restrict__ table, int64_t n_pages, int64_t L, int64_t pos0, int32_t topk, int32_t bs_shift,
+    int32_t n_blocks, const uint32_t *__restrict__ bkeys, int64_t bkeys_ld, int32_t *__restrict__ idx)
+{
+    __shared__ RescoreShared sh;
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const int64_t n = pos0 + r + 1;  // visible keys of the row
+    int32_t *dst = idx + r * topk;
+    const int bs = 1 << bs_shift;
+    const int n_blk = (int)((n + bs - 1) >> bs_shift);
+    const int kept = n_blocks < n_blk ? n_blocks : n_blk;
+    if (kept < n_blk) {
+        select_kept_blocks(sh, nullptr, bkeys + r * bkeys_ld, n, bs_shift, kept, n_blk);
+    } else {
+        for (int j = tid; j < n_blk; j += kThreads) sh.kept[j] = j;
+        __syncthreads();
+    }
+    const int last = sh.kept[kept - 1];
+    const int n_c = (kept << bs_shift) - (last == n_blk - 1 ? (int)(((int64_t)n_blk << bs_shift) - n) : 0);
+    const KeptTokens cand{sh.key, sh.kept, bs_shift};
+    const int m = topk < n_c ? topk : n_c;
+    if (m == n_c) {  // every candidate is selected: nothing to score
+        for (int j = tid; j < n_c; j += kThreads) dst[j] = cand.i(j);
+        for (int j = n_c + tid; j < topk; j += kThreads) dst[j] = -1;
+        return;
+    }
+
+    // q fragments and head weights of the row
+    {
+        const uint16_t *qr = q_idx + r * (int64_t)kRH * kRD;
+        const int l = tid % kWave, mk = tid / kWave;  // 16 fragments of 64 lanes = the 1024 threads
+        sh.qf[tid] = load16(qr + (32 * (mk / 8) + l % 32) * kRD + 16 * (mk % 8) + 8 * (l / 32));
+        if (tid < kRH) sh.wv[tid] = w[r * kRH + tid];
+        for (int j = tid; j < kBins; j += kThreads) sh.hist[j] = 0;
+    }
+    __syncthreads();
+    // this lane's 32 head weights, in the order of its accumulator registers: register g of lane l is
+    // head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4
+    float wr[2][16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int g = 0; g < 16; ++g) wr[mt][g] = sh.wv[32 * mt + 8 * (g / 4) + 4 * (lane / 32) + g % 4];
+
+    // 32 candidates per wave at a time (bs >= 64: a group of 32 lies inside one block)
+    const int n_groups = (n_c + 31) / 32;
+#pragma unroll 1
+    for (int grp = wave; grp < n_groups; grp += kWaves) {
+        const int j = 32 * grp + lane % 32;
+        const bool ok = j < n_c;
+        const int64_t tok = cand.i(ok ? j : 32 * grp);
+        int64_t krow = tok;
+        bool page_ok = true;
+        if (table) {
+            const int32_t pg = table[tok / 64];
+            page_ok = pg >= 0 && pg < n_pages;
+            krow = (int64_t)(page_ok ? pg : 0) * 64 + tok % 64;
+        }
+        const uint16_t *src = k_idx + krow * kRD + 8 * (lane / 32);
+        bf16x8 b[kRD / 16];
+#pragma unroll
+        for (int ks = 0; ks < kRD / 16; ++ks) b[ks] = as_bf16x8(load16(src + 16 * ks));
+        f32x16 acc0, acc1;
+#pragma unroll
+        for (int ks = 0; ks < kRD / 16; ++ks) {
+            const bf16x8 a0 = as_bf16x8(sh.qf[ks * kWave + lane]);
+            const bf16x8 a1 = as_bf16x8(sh.qf[(8 + ks) * kWave + lane]);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[ks], ks == 0 ? f32x16{} : acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[ks], ks == 0 ? f32x16{} : acc1, 0, 0, 0);
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            p = fmaf(wr[0][g], relu(acc0[g]), p);
+            p = fmaf(wr[1][g], relu(acc1[g]), p);
+        }
+        // lanes l and l ^ 32 hold the two halves of the head sum of candidate j
+        float score = p + __shfl_xor(p, 32);
+        if (!page_ok) score = -__builtin_inff();
+        if (lane < 32 && ok) {
+            const uint32_t key = order_key(score);
+            sh.key[j] = key;
+            atomicAdd(&sh.hist[key >> kBinShift], 1u);
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        int above;
+        const int bin = topk::threshold_bin(sh.hist, m, &above, nullptr);
+        if (tid == 0) {
+            sh.bin = bin;
+            sh.above = above;
+        }
+    }
+    __syncthreads();
+    topk::select_and_emit<kWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
+    for (int j = m + tid; j < topk; j += kThreads) dst[j] = -1;
+}
+
 }  // namespace
+
+hipError_t launch_block_rescore_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
+                                     const int32_t *table, int64_t n_pages, int64_t L, int64_t pos0, int32_t topk,
+                                     int32_t block_size, int32_t n_blocks, const uint32_t *bkeys, int64_t bkeys_ld,
+                                     int32_t *idx, hipStream_t st)
+{
+    if (L <= 0) return hipSuccess;
+    int shift = 0;
+    while ((1 << shift) < block_size) ++shift;
+    KernelTimer timer(h, SA_KERNEL_TOPK, st);
+    hipLaunchKernelGGL(block_rescore_topk_kernel, dim3((unsigned)L), dim3(kThreads), 0, st,
+                       reinterpret_cast<const uint16_t *>(q_idx), w, reinterpret_cast<const uint16_t *>(k_idx), table,
+                       n_pages, L, pos0, topk, shift, n_blocks, bkeys, bkeys_ld, idx);
+    return hipGetLastError();
+}
 
 hipError_t launch_block_topk(sa_handle_s &h, const float *scores, int64_t ld, int64_t rows, int64_t cols,
                              const int32_t *valid_len, int64_t causal_row0, const int32_t *k_per_row, int32_t k,

@@ -106,13 +106,21 @@ __device__ __forceinline__ void step_pattern()
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
 }
 
+// Block keys instead of a selection (the first pass of the two-tier selection): for every row that has
+// more than `need` visible keys, the order key of the best visible score of each 64-key tile it sees.
+struct BlockKeysOut {
+    uint32_t *keys;    // [L, ld]: row i, tile j
+    int64_t ld;
+};
+
 // Query rows i = 0 .. L-1 are the tokens at positions pos0 + i of one sequence; keys are its tokens
-// 0 .. pos0 + L - 1 (contiguous rows, or pages of its block-table row when kPaged).
-template <bool kPaged>
+// 0 .. pos0 + L - 1 (contiguous rows, or pages of its block-table row when kPaged).  Rows with at most
+// `need` visible keys are not scored (need = topk: all their keys are selected).
+template <bool kPaged, bool kBlockKeys>
 __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KeySource ks, int64_t L, int64_t pos0,
-    int32_t topk, int32_t *__restrict__ idx, uint2 *__restrict__ cands, int64_t cand_ld,
-    int32_t *__restrict__ counter, int32_t n_tiles)
+    int32_t topk, int64_t need, int32_t *__restrict__ idx, uint2 *__restrict__ cands, int64_t cand_ld,
+    BlockKeysOut bk, int32_t *__restrict__ counter, int32_t n_tiles)
 {
     __shared__ Shared<kPaged> sh;
     const uint16_t *__restrict__ k_idx = ks.base;
@@ -132,11 +140,12 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
         const int64_t row = pos0 + ri;   // and its position: it sees keys 0 .. row
         const bool row_ok = ri < L;
         const int m = row_ok ? (int)((int64_t)topk < row + 1 ? (int64_t)topk : row + 1) : 0;
-        const bool selects = row_ok && row + 1 > topk;  // fewer than all visible keys
-        int n_cand = 0;                                    // this row's candidate list length
+        const bool selects = row_ok && row + 1 > need;  // fewer than all visible keys
+        int n_cand = 0;                                   // this row's candidate list length
 
-        if (t_last + 1 > topk) {  // some row of the tile needs scores
-            for (int i = tid; i < kRows * kBins; i += kThreads) sh.region[i] = 0;
+        if (t_last + 1 > need) {  // some row of the tile needs scores
+            if constexpr (!kBlockKeys)
+                for (int i = tid; i < kRows * kBins; i += kThreads) sh.region[i] = 0;
             if constexpr (kPaged) {
                 // the pool page of every key tile of the prefix, checked once (a bad entry is read as page 0
                 // and its keys score -inf)
@@ -217,6 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             // threshold bin are appended to the row's candidate list in key order
             // the window's keys are s = sb - 32 (sb >= 0; 32-bit is enough: row < 2^31)
             const uint32_t vis_hi = (uint32_t)row + 32u;
+            float prev_hi = -__builtin_inff();  // block keys: best score of the first half of the last tile
             auto finish_window = [&](float part_odd, float part_even, uint32_t sb) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part_odd),
                                                                  __float_as_uint(part_even), false, false);
@@ -229,6 +239,17 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                     const bool bad_lo = kw >= 1 && sh.pages[kw - 1] < 0;
                     const bool bad_hi = sh.pages[kw < kPrefillMaxPages ? kw : kPrefillMaxPages - 1] < 0;
                     if (vis && (lane < 32 ? bad_lo : bad_hi)) score = -__builtin_inff();
+                }
+                if constexpr (kBlockKeys) {
+                    // lanes 0-31 finish tile kw - 1 (its first half was the previous window's lanes 32-63)
+                    const int kw = __builtin_amdgcn_readfirstlane((int)(sb / kKT));
+                    const float hm = half_wave_max(vis ? score : -__builtin_inff());
+                    const float m_lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hm), 0));
+                    const float m_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hm), 32));
+                    if (kw >= 1 && (int64_t)(kw - 1) * kKT <= row && lane == 0)
+                        bk.keys[ri * bk.ld + kw - 1] = order_key(fmaxf(prev_hi, m_lo));
+                    prev_hi = m_hi;
+                    return;
                 }
                 const uint32_t key = order_key(score);
                 atomicAdd(&hist[key >> kBinShift], vis ? 1u : 0u);
@@ -297,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 if (selects) {
                     // window: odd half-tile of tile kt - 1 and even half-tile of tile kt
                     finish_window(part_odd, p, (uint32_t)kt * kKT + lane);
-                    if ((kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
+                    if (!kBlockKeys && (kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
                         const int b = topk::threshold_bin(hist, m, nullptr, nullptr);
                         if (b > run_bin) run_bin = b;
                     }
@@ -313,6 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 finish_window(p, 0.f, (uint32_t)n_kt * kKT + lane);
             }
         }
+        if constexpr (kBlockKeys) continue;  // no selection in this pass
         // final threshold per row (each wave its own row), then free the histograms
         if (selects) {
             int ab, up;
@@ -382,6 +404,8 @@ __global__ void reset_counter_kernel(int32_t *counter) { *counter = 0; }
 
 }  // namespace
 
+size_t prefill_block_keys_ld(int64_t L, int64_t pos0) { return (pos0 + L + kKT - 1) / kKT; }
+
 size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L, int64_t pos0)
 {
     const int64_t n_tiles = (L + kRows - 1) / kRows;
@@ -392,7 +416,8 @@ size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L, int64_t pos0)
 
 hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
                                int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st,
-                               const int32_t *table, int64_t n_pages, int64_t pos0)
+                               const int32_t *table, int64_t n_pages, int64_t pos0, uint32_t *block_keys,
+                               int64_t keys_above)
 {
     const int64_t n_tiles = (L + kRows - 1) / kRows;
     const int64_t slots = n_tiles < h.n_cu ? n_tiles : h.n_cu;
@@ -403,15 +428,26 @@ hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const KeySource ks{reinterpret_cast<const uint16_t *>(k_idx), table, n_pages, h.d_err};
+    const uint16_t *qi = reinterpret_cast<const uint16_t *>(q_idx);
     KernelTimer timer(h, SA_KERNEL_INDEXER, st);
+    if (block_keys) {
+        const BlockKeysOut bk{block_keys, (int64_t)prefill_block_keys_ld(L, pos0)};
+        const int64_t need = keys_above;
+        if (table)
+            hipLaunchKernelGGL((indexer_topk_prefill_kernel<true, true>), dim3((unsigned)slots), dim3(kThreads), 0, st,
+                               qi, w, ks, L, pos0, topk, need, idx, cands, ld, bk, counter, (int32_t)n_tiles);
+        else
+            hipLaunchKernelGGL((indexer_topk_prefill_kernel<false, true>), dim3((unsigned)slots), dim3(kThreads), 0,
+                               st, qi, w, ks, L, pos0, topk, need, idx, cands, ld, bk, counter, (int32_t)n_tiles);
+        return hipGetLastError();
+    }
+    const BlockKeysOut none{nullptr, 0};
     if (table)
-        hipLaunchKernelGGL(indexer_topk_prefill_kernel<true>, dim3((unsigned)slots), dim3(kThreads), 0, st,
-                           reinterpret_cast<const uint16_t *>(q_idx), w, ks, L, pos0, topk, idx, cands, ld, counter,
-                           (int32_t)n_tiles);
+        hipLaunchKernelGGL((indexer_topk_prefill_kernel<true, false>), dim3((unsigned)slots), dim3(kThreads), 0, st,
+                           qi, w, ks, L, pos0, topk, (int64_t)topk, idx, cands, ld, none, counter, (int32_t)n_tiles);
     else
-        hipLaunchKernelGGL(indexer_topk_prefill_kernel<false>, dim3((unsigned)slots), dim3(kThreads), 0, st,
-                           reinterpret_cast<const uint16_t *>(q_idx), w, ks, L, pos0, topk, idx, cands, ld, counter,
-                           (int32_t)n_tiles);
+        hipLaunchKernelGGL((indexer_topk_prefill_kernel<false, false>), dim3((unsigned)slots), dim3(kThreads), 0, st,
+                           qi, w, ks, L, pos0, topk, (int64_t)topk, idx, cands, ld, none, counter, (int32_t)n_tiles);
     return hipGetLastError();
 }
 

@@ -122,10 +122,15 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows,
 // (table != nullptr) 64-token pages of the pool k_idx [n_pages, 64, d_I], page j of the sequence
 // being table[j] (table holds at most kPrefillMaxPages entries for the keys).
 constexpr int64_t kPrefillMaxPages = 8192;
+// With block_keys != nullptr the kernel selects nothing: every row with more than keys_above visible
+// keys gets, in block_keys [L, prefill_block_keys_ld(L, pos0)] (row i, tile j), the order key of the best
+// score among the keys it sees in 64-key tile j (for every tile it sees), and idx is not written.
 size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L, int64_t pos0 = 0);
+size_t prefill_block_keys_ld(int64_t L, int64_t pos0);
 hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
                                int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st,
-                               const int32_t *table = nullptr, int64_t n_pages = 0, int64_t pos0 = 0);
+                               const int32_t *table = nullptr, int64_t n_pages = 0, int64_t pos0 = 0,
+                               uint32_t *block_keys = nullptr, int64_t keys_above = 0);
 
 // ---- paged decode indexer + per-sequence top-k (bf16, H_I = 64, d_I = 128, 64-token pages) --
 struct DecodeTopkLayout {
@@ -139,6 +144,15 @@ hipError_t launch_decode_indexer_topk(sa_handle_s &h, const void *q_idx, const f
                                       int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
                                       const int32_t *ctx_len, const int32_t *topk_b, int32_t B, int32_t max_ctx,
                                       int32_t *idx, void *ws, hipStream_t st);
+
+// Two-tier prefill, second pass (bf16, H_I = 64, d_I = 128, block_size a multiple of 64): row i (position
+// pos0 + i) keeps n_blocks blocks by the tile keys launch_prefill_topk wrote (rows with more than
+// n_blocks * block_size visible keys), scores their tokens and writes its top-topk to idx [L, topk].
+// Keys are rows of k_idx, or (table != nullptr) 64-token pages of the pool k_idx, page j being table[j].
+hipError_t launch_block_rescore_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,
+                                     const int32_t *table, int64_t n_pages, int64_t L, int64_t pos0, int32_t topk,
+                                     int32_t block_size, int32_t n_blocks, const uint32_t *bkeys, int64_t bkeys_ld,
+                                     int32_t *idx, hipStream_t st);
 
 // The paged decode indexer alone: sequence b's scores land at ws + layout.scores, row stride
 // layout.ld (floats), for tokens s < ctx_len[b]; with page_maxima, the order key of the largest

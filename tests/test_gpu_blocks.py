@@ -291,3 +291,55 @@ def test_decode_blocks_rl_sweep_budgets():
         out, lse, idx = _decode_blocks(h, d, 64, 32)
     _check_decode_blocks(d, out, lse, idx, 64, 32, [0, int(np.argmax(k)), int(np.argmin(k)), 128, 255], 512,
                          "decode_blocks rl")
+
+
+@pytest.mark.parametrize("L,topk,bs,nb", [(3000, 512, 128, 3), (3000, 256, 256, 2), (2500, 300, 1024, 1)])
+def test_prefill_blocks_fused_wide_blocks(L, topk, bs, nb):
+    """Blocks of several 64-key tiles: the fused first pass's tile keys are combined per block."""
+    wl = inputs.WORKLOADS["prefill_8k"]
+    say(f"prefill_blocks fused L={L} topk={topk} block={bs} n_blocks={nb}")
+    d = inputs.prefill_inputs(wl, DEV, L=L, seed=77)
+    with sa.Handle(inputs.library_config(wl, max_topk=topk)) as h:
+        out, lse, idx = _prefill_blocks(h, d, topk, bs, nb)
+    rows = np.unique(np.concatenate([np.arange(0, 40), [bs * nb - 1, bs * nb, bs * nb + 1, L // 2, L - 2, L - 1],
+                                     np.random.default_rng(L + bs).integers(0, L, 24)]))
+    _check_prefill_blocks_rows(d, out, lse, idx, topk, bs, nb, rows, latent=True, d_v=512,
+                               what=f"prefill_blocks fused b{bs}")
+
+
+def test_prefill_blocks_fused_equals_flat_when_blocks_cover_k():
+    """n_blocks >= k: the kept blocks hold every flat winner and the second pass scores tokens exactly as
+    the fused indexer does, so the two-tier prefill equals the flat prefill bit for bit (40 of 65 blocks
+    kept here, so the block stage is not trivial)."""
+    wl = inputs.WORKLOADS["prefill_8k"]
+    L, topk = 4100, 32
+    say(f"prefill_blocks fused (64-token blocks, 40 kept) vs sparse_attn_prefill, L={L}, topk={topk}")
+    d = inputs.prefill_inputs(wl, DEV, L=L, seed=78)
+    with sa.Handle(inputs.library_config(wl, max_topk=topk)) as h:
+        out, lse, idx = _prefill_blocks(h, d, topk, 64, 40)
+        out2 = torch.empty_like(out)
+        lse2 = torch.empty_like(lse)
+        idx2 = torch.empty_like(idx)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL, L)
+        sa.sparse_attn_prefill(h, d["q"], d["k"], None, d["q_idx"], d["w"], d["k_idx"], topk, out2, lse2, idx2, ws)
+        assert sa.sparse_attn_check(h) == 0
+    assert torch.equal(idx, idx2)
+    assert torch.equal(out, out2)
+    assert torch.equal(lse, lse2)
+
+
+def test_prefill_blocks_128k_sampled():
+    """The two-tier prefill as the benchmark runs it: L = 131072, blocks of 64, 64 kept, top-2048."""
+    wl = inputs.WORKLOADS["prefill_128k"]
+    say("prefill_blocks prefill_128k L=131072 topk=2048 block=64 n_blocks=64 (sampled rows)")
+    d = inputs.prefill_inputs(wl, DEV)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        out, lse, idx = _prefill_blocks(h, d, wl.topk, 64, 64)
+    sal = d["salient"]
+    rows = np.unique(np.concatenate([[0, 2047, 4095, 4096, 4097, 65535, wl.L - 2, wl.L - 1],
+                                     sal[[0, len(sal) // 2, -1]] + 1,
+                                     np.random.default_rng(129).integers(0, wl.L, 5)]))
+    _check_prefill_blocks_rows(d, out, lse, idx, wl.topk, 64, 64, rows, latent=True, d_v=512,
+                               what="prefill_blocks 128k")
+    del out, lse, idx, d
+    torch.cuda.empty_cache()
