@@ -403,8 +403,9 @@ def measure_two_tier(cfg, P, D, L, K, args, torch):
     """The two-tier (block -> token) selection on the same inputs (not part of `value`): blocks of
     --block-size tokens, --n-blocks kept per query, top-K inside them.  Decode: the paged indexer,
     then one selection workgroup per sequence over its scores (4 B per cached token read back), then
-    the same attention.  Prefill: scores materialised per block of query rows, then the selection
-    per row, then the same attention."""
+    the same attention.  Prefill (blocks of >= 64 tokens): the fused indexer writes each row's best score
+    per 64-key tile, one workgroup per row keeps the best blocks and rescores only their tokens, then the
+    same attention."""
     import numpy as np
 
     import indexer_selected_sparse_scores_amd as sa
@@ -449,8 +450,10 @@ def measure_two_tier(cfg, P, D, L, K, args, torch):
         res["decode"] = {"ms": round(ms, 4), "tokens_per_s": round(B / (ms * 1e-3), 1), "kernels_ms": per}
         if sel_ms:
             gbs = sel_bytes / (sel_ms * 1e-3) / 1e9
+            # a few KB per sequence through dependent phases (block keys, radix selects): bound by their
+            # latency, not by bandwidth; the rate against the HBM peak is given for scale only
             res["decode"]["selection_roofline"] = {
-                "kernel": "block_topk_rows_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                "kernel": "block_topk_rows_kernel", "bound": "latency", "achieved": round(gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                 "algorithmic_per_launch": f"{sel_bytes} B = per sequence ceil(n/{span}) block-maximum keys + "
                                           f"min(n, {nb * bs}) candidate scores read + {K} indices written"}
@@ -464,6 +467,14 @@ def measure_two_tier(cfg, P, D, L, K, args, torch):
             h, P["q"], P["k"], None, P["q_idx"], P["w"], P["k_idx"], K, bs, nb, out, None, idx, ws),
             max(1, min(args.steps, 2)))
         res["prefill"] = {"ms": round(ms, 4), "tokens_per_s": round(L / (ms * 1e-3), 1), "kernels_ms": per}
+        if per.get("indexer") and bs >= 64:
+            pairs = L * (L + 1) // 2
+            flops = pairs * 2 * s.n_idx_heads * s.d_idx
+            tf = flops / (per["indexer"] * 1e-3) / 1e12
+            res["prefill"]["block_key_roofline"] = {
+                "kernel": "indexer_topk_prefill_kernel (block-key mode)", "bound": "mfma", "achieved": round(tf, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_per_launch": f"{flops:.4g} flop = {pairs} causal pairs x {2 * s.n_idx_heads * s.d_idx} flop"}
         del out, idx, ws
     torch.cuda.empty_cache()
     return res
