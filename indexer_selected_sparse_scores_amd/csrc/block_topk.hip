@@ -73,7 +73,7 @@ __device__ __forceinline__ uint32_t group_max(uint32_t x, int g)
 // maxima of its 64-token spans when pmax != nullptr) and the `kept` best blocks, written ascending to
 // sh.kept.  Every thread of the workgroup calls it; it ends with a barrier.
 template <class Sh>
-__device__ void select_kept_blocks(Sh &sh, const float *__restrict__ row, const uint32_t *__restrict__ pmax,
+__device__ __forceinline__ void select_kept_blocks(Sh &sh, const float *__restrict__ row, const uint32_t *__restrict__ pmax,
                                    int64_t n, int bs_shift, int kept, int n_blk)
 {
     const int tid = threadIdx.x;
@@ -134,7 +134,7 @@ __device__ void select_kept_blocks(Sh &sh, const float *__restrict__ row, const 
             }
         }
         __syncthreads();
-        topk::select_and_emit<kWaves>(sh.sel, BlockKeys{sh.key}, n_blk, sh.bin, sh.above, kept, sh.kept);
+        topk::select_and_emit_inline<kWaves>(sh.sel, BlockKeys{sh.key}, n_blk, sh.bin, sh.above, kept, sh.kept);
     }
     __syncthreads();
 }
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
             }
         }
         __syncthreads();
-        topk::select_and_emit<kWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
+        topk::select_and_emit_inline<kWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
     }
     for (int64_t i = m + tid; i < idx_ld; i += kThreads) dst[i] = -1;
 }
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
         }
     }
     __syncthreads();
-    topk::select_and_emit<kWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
+    topk::select_and_emit_inline<kWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
     for (int j = m + tid; j < topk; j += kThreads) dst[j] = -1;
 }
 

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
         load_round(v2, base + 5 * kRoundScores);
     }
     __syncthreads();
-    topk::select_and_emit(sh, topk::LdsCands{ck, ci}, total < kCap ? total : kCap, bin, above, (int)m, dst);
+    topk::select_and_emit_inline(sh, topk::LdsCands{ck, ci}, total < kCap ? total : kCap, bin, above, (int)m, dst);
     for (int i = (int)m + tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
 }
 

@@ -119,10 +119,12 @@ struct GlobalScores {
 // Exact selection of the `need` largest keys among the n candidates whose top bits equal
 // `bin` (the ones in higher bins are all taken: `above` of them), then an ordered emit of the
 // m = above + need selected indices (ascending) into dst[0, m).  Candidates in lower bins are
-// skipped.  Every thread of the workgroup calls this.
+// skipped.  Every thread of the workgroup calls this.  select_and_emit_inline is the body, for
+// kernels with registers to spare (no call frame in scratch memory); select_and_emit keeps it out
+// of line for kernels that hold many live registers around the call.
 template <int kWaves, class Src>
-__device__ __noinline__ void select_and_emit(SelectShared<kWaves> &sh, const Src &src, int n, int bin,
-                                             int above, int m, int32_t *dst)
+__device__ __forceinline__ void select_and_emit_inline(SelectShared<kWaves> &sh, const Src &src, int n, int bin,
+                                                       int above, int m, int32_t *dst)
 {
     constexpr int kThreads = kWaves * kWave;
     const int tid = threadIdx.x;
@@ -194,6 +196,13 @@ __device__ __noinline__ void select_and_emit(SelectShared<kWaves> &sh, const Src
         eq_before += eq_total;
         out_before += take_total;
     }
+}
+
+template <int kWaves, class Src>
+__device__ __noinline__ void select_and_emit(SelectShared<kWaves> &sh, const Src &src, int n, int bin, int above,
+                                             int m, int32_t *dst)
+{
+    select_and_emit_inline<kWaves>(sh, src, n, bin, above, m, dst);
 }
 
 }  // namespace topk
