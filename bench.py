@@ -11,8 +11,9 @@ Prints one JSON line: `value` is prefill tokens/s at 128K context; decode tokens
 per-kernel times (HIP events the library records around each launch on the launch stream),
 the roofline of the dominant kernel (the fused prefill indexer / top-k) and of the decode
 kernels, the index projections, the two-tier (block -> token) selection variant of both
-steps, a chunked prefill against the paged caches, the acceptance-rate statistic, and the CPU
-oracle's throughput on a bounded sample ride along.
+steps, a chunked prefill against the paged caches, the acceptance-rate statistic, the RL-rollout
+decode sweep (256 sequences, context 1K..32K, per-sequence budgets), and the CPU oracle's throughput
+on a bounded sample ride along.
 
 HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
 calibrated on the 1 GiB copy it performs after the warm-up, and stored in
@@ -57,6 +58,7 @@ def parse():
     ap.add_argument("--no-two-tier", action="store_true", help="skip the two-tier (block -> token) measurement")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill (paged query rows) measurement")
     ap.add_argument("--no-acceptance", action="store_true", help="skip the acceptance-rate measurement")
+    ap.add_argument("--no-rl-sweep", action="store_true", help="skip the RL-rollout decode sweep")
     ap.add_argument("--main-only", action="store_true",
                     help="time the step alone (no projections, two-tier, chunked-prefill or acceptance legs)")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -151,7 +153,7 @@ def main():
         ingest_traffic(*args.ingest_traffic)
         return
     if args.main_only:
-        args.no_projections = args.no_two_tier = args.no_chunk = args.no_acceptance = True
+        args.no_projections = args.no_two_tier = args.no_chunk = args.no_acceptance = args.no_rl_sweep = True
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -308,6 +310,7 @@ def main():
     two_tier = None if args.no_two_tier else measure_two_tier(cfg, P, D, L, K, args, torch)
     chunk = None if args.no_chunk else measure_chunk(cfg, P, D, K, args, torch)
     acceptance = None if args.no_acceptance else measure_acceptance(cfg, args, torch)
+    rl_sweep = None if args.no_rl_sweep else measure_rl_sweep(args, torch)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -343,6 +346,7 @@ def main():
         "two_tier": two_tier,
         "chunked_prefill": chunk,
         "acceptance": acceptance,
+        "rl_sweep": rl_sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -553,6 +557,70 @@ def measure_chunk(cfg, P, D, K, args, torch):
         res["per_row_path"]["indexer_roofline"] = roof("indexer_decode_kernel (one row per grid column, all launches)",
                                                        per_r["indexer"])
     return res
+
+
+def measure_rl_sweep(args, torch):
+    """The RL-rollout decode sweep (not part of `value`): 256 sequences whose context grows from 1K to 32K in
+    steps of 1K, each sequence with its own budget k_b(n) = min(n, max(256, floor(rho_b n))), rho_b ~ U(0.05,
+    0.25); one decode step at each n = 1024 i, i = 1..32 (8192 generated tokens in all).  The paged caches are
+    generated once for 32K tokens per sequence and each step sees its first n."""
+    import numpy as np
+
+    import indexer_selected_sparse_scores_amd as sa
+    from indexer_selected_sparse_scores_amd import inputs
+    dev = "cuda"
+    wl = inputs.WORKLOADS["decode_rl_sweep"]
+    n_max = wl.ctx_range[1]
+    B = wl.B
+    log(f"[bench] RL-rollout decode sweep B={B}, n = 1024 .. {n_max}")
+    D = inputs.decode_inputs(wl, dev, ctx=np.full(B, n_max))
+    cfg = inputs.library_config(wl, max_topk=8192)
+    s = cfg
+    steps = list(range(1024, n_max + 1, 1024))
+    with sa.Handle(cfg) as h:
+        out = torch.empty((B, s.n_heads, s.d_v), device=dev)
+        idx = torch.empty((B, s.max_topk), device=dev, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_DECODE, B, n_max)
+        plan = []
+        for n in steps:
+            k = inputs.rl_budget(n, D["rho"])
+            plan.append((n, torch.full((B,), n, dtype=torch.int32, device=dev),
+                         torch.from_numpy(k.astype(np.int32)).to(dev), k))
+
+        def step(p):
+            n, ctx, topk, _ = p
+            sa.sparse_attn_decode(h, D["q"], D["q_idx"], D["w"], D["kv_pages"], None, D["kidx_pages"],
+                                  D["block_table"], ctx, topk, n, out, None, idx, ws)
+
+        for p in plan:  # warm-up pass
+            step(p)
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
+        ev[0].record()
+        for i, p in enumerate(plan):
+            step(p)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(plan))]
+        del out, idx, ws
+    del D
+    torch.cuda.empty_cache()
+    total_ms = sum(per_step)
+    tokens = B * len(steps)
+    nbytes = sum(B * n * s.d_idx * 2 + int(k.sum()) * s.d_qk * 2 for n, _, _, k in plan)
+    gbs = nbytes / (total_ms * 1e-3) / 1e9
+    return {"workload": f"{B} sequences, one decode step at each context n = 1024 i (i = 1..{len(steps)}), "
+                        "per-sequence top-k min(n, max(256, floor(rho n))), rho ~ U(0.05, 0.25)",
+            "steps": len(steps), "tokens": tokens, "ms_total": round(total_ms, 4),
+            "tokens_per_s": round(tokens / (total_ms * 1e-3), 1),
+            "ms_first_last_step": [round(per_step[0], 4), round(per_step[-1], 4)],
+            "roofline": {"kernel": "whole decode step (paged indexer, top-k, gather-attention, merge)", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_per_launch": f"{nbytes} B over the sweep = sum over steps of B n x 256 B index "
+                                                   f"keys + sum_b k_b x 1152 B selected latent rows"}}
 
 
 def measure_acceptance(cfg, args, torch, T=4096, V=151936):
