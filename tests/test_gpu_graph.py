@@ -1,0 +1,111 @@
+"""HIP graph capture of the library's calls: they allocate nothing and clear their counters and
+histograms with kernels (no memset nodes), so a captured step replays to the eager result, bit for bit,
+on every replay -- checked with eager work and synchronisations between the replays."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_selected_sparse_scores_amd as sa
+from indexer_selected_sparse_scores_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _replays_match(run, outputs, n=3):
+    """Eager reference, then capture `run` on a side stream and replay it n times, checking every replay."""
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()  # a warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    for i in range(n):
+        for t in outputs:
+            t.fill_(-7)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outputs, ref):
+            assert torch.equal(a, b), f"replay {i} differs from the eager result"
+    say(f"  {n} replays equal to the eager result")
+
+
+def test_decode_step_replays_from_a_graph():
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [5000, 129, 20000, 64, 777, 4097, 3, 16384]
+    say(f"graph capture: sparse_attn_decode, ctx={ctx}")
+    d = inputs.decode_inputs(inputs.small(wl, topk=2048), DEV, ctx=ctx, seed=41)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        B = len(ctx)
+        out = torch.empty((B, 16, 512), device=DEV)
+        lse = torch.empty((B, 16), device=DEV)
+        idx = torch.empty((B, 2048), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_DECODE, B, d["max_ctx"])
+
+        def run():
+            sa.sparse_attn_decode(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], None, d["kidx_pages"],
+                                  d["block_table"], d["ctx_len"], d["topk"], d["max_ctx"], out, lse, idx, ws)
+
+        _replays_match(run, [out, lse, idx])
+        assert sa.sparse_attn_check(h) == 0
+
+
+def test_prefill_replays_from_a_graph():
+    wl = inputs.WORKLOADS["prefill_8k"]
+    L = 2051
+    say(f"graph capture: sparse_attn_prefill, L={L}, topk=256")
+    P = inputs.prefill_inputs(wl, DEV, L=L, seed=42)
+    with sa.Handle(inputs.library_config(wl, max_topk=256)) as h:
+        out = torch.empty((L, 16, 512), device=DEV)
+        lse = torch.empty((L, 16), device=DEV)
+        idx = torch.empty((L, 256), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL, L)
+
+        def run():
+            sa.sparse_attn_prefill(h, P["q"], P["k"], None, P["q_idx"], P["w"], P["k_idx"], 256, out, lse, idx, ws)
+
+        _replays_match(run, [out, lse, idx])
+        assert sa.sparse_attn_check(h) == 0
+
+
+def test_two_tier_decode_replays_from_a_graph():
+    wl = inputs.WORKLOADS["decode_b64"]
+    ctx = [9000, 300, 20000, 4097]
+    say(f"graph capture: sparse_attn_decode_blocks, ctx={ctx}")
+    d = inputs.decode_inputs(inputs.small(wl, topk=2048), DEV, ctx=ctx, seed=43)
+    with sa.Handle(inputs.library_config(wl)) as h:
+        B = len(ctx)
+        out = torch.empty((B, 16, 512), device=DEV)
+        idx = torch.empty((B, 2048), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_DECODE_BLOCKS, B, d["max_ctx"])
+
+        def run():
+            sa.sparse_attn_decode_blocks(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], None, d["kidx_pages"],
+                                         d["block_table"], d["ctx_len"], d["topk"], d["max_ctx"], 64, 48, out, None,
+                                         idx, ws)
+
+        _replays_match(run, [out, idx])
+        assert sa.sparse_attn_check(h) == 0
