@@ -72,10 +72,11 @@ __device__ __forceinline__ uint32_t group_max(uint32_t x, int g)
 // Steps 1 and 2 for one row: the key of every block's best score (from the row's scores, or from the
 // maxima of its 64-token spans when pmax != nullptr) and the `kept` best blocks, written ascending to
 // sh.kept.  Every thread of the workgroup calls it; it ends with a barrier.
-template <class Sh>
+template <int kW, class Sh>
 __device__ __forceinline__ void select_kept_blocks(Sh &sh, const float *__restrict__ row, const uint32_t *__restrict__ pmax,
                                    int64_t n, int bs_shift, int kept, int n_blk)
 {
+    constexpr int kThreads = kW * kWave;
     const int tid = threadIdx.x;
     const int bs = 1 << bs_shift;
     for (int j = tid; j < kBins; j += kThreads) sh.hist[j] = 0;
@@ -134,7 +135,7 @@ __device__ __forceinline__ void select_kept_blocks(Sh &sh, const float *__restri
             }
         }
         __syncthreads();
-        topk::select_and_emit_inline<kWaves>(sh.sel, BlockKeys{sh.key}, n_blk, sh.bin, sh.above, kept, sh.kept);
+        topk::select_and_emit_inline<kW>(sh.sel, BlockKeys{sh.key}, n_blk, sh.bin, sh.above, kept, sh.kept);
     }
     __syncthreads();
 }
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
     const int n_blk = (int)((n + bs - 1) >> bs_shift);  // <= kBlockSelectMaxItems (host check)
     const int kept = n_blocks < n_blk ? n_blocks : n_blk;
 
-    select_kept_blocks(sh, row, pmax ? pmax + r * pmax_ld : nullptr, n, bs_shift, kept, n_blk);
+    select_kept_blocks<kWaves>(sh, row, pmax ? pmax + r * pmax_ld : nullptr, n, bs_shift, kept, n_blk);
 
     // 3. candidates: the visible tokens of the kept blocks, ascending
     const int last = sh.kept[kept - 1];
@@ -210,23 +211,37 @@ __global__ __launch_bounds__(kThreads) void block_topk_rows_kernel(
 // ---------------------------------------------------------------------------------------
 constexpr int kRH = 64;   // index heads
 constexpr int kRD = 128;  // index head width
+constexpr int kRWaves = 4;
+constexpr int kRThreads = kRWaves * kWave;
 
 struct RescoreShared {
     uint4 qf[2 * (kRD / 16) * kWave];     // q fragment (mt, ks) of lane l at (8 mt + ks) * 64 + l (16 KB)
     float wv[kRH];
-    uint32_t key[kBlockSelectMaxItems];   // block keys, then candidate keys
     alignas(16) uint32_t hist[kBins];
     int32_t kept[kBlockSelectMaxKept];
-    topk::SelectShared<kWaves> sel;
+    topk::SelectShared<kRWaves> sel;
     int bin, above;
 };
 
-__global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
+// The selection helpers' view of the row's shared state; the key array (block keys, then candidate
+// keys) is dynamic LDS sized to the call's largest need, so that several rows share a CU.
+struct RescoreView {
+    uint32_t *key;
+    uint32_t *hist;
+    int32_t *kept;
+    topk::SelectShared<kRWaves> &sel;
+    int &bin;
+    int &above;
+};
+
+__global__ __launch_bounds__(kRThreads) void block_rescore_topk_kernel(
     const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ k_idx,
     const int32_t *__restrict__ table, int64_t n_pages, int64_t L, int64_t pos0, int32_t topk, int32_t bs_shift,
     int32_t n_blocks, const uint32_t *__restrict__ bkeys, int64_t bkeys_ld, int32_t *__restrict__ idx)
 {
     __shared__ RescoreShared sh;
+    extern __shared__ __attribute__((aligned(16))) uint32_t key_lds[];
+    RescoreView v{key_lds, sh.hist, sh.kept, sh.sel, sh.bin, sh.above};
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int64_t n = pos0 + r + 1;  // visible keys of the row
@@ -235,28 +250,31 @@ __global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
     const int n_blk = (int)((n + bs - 1) >> bs_shift);
     const int kept = n_blocks < n_blk ? n_blocks : n_blk;
     if (kept < n_blk) {
-        select_kept_blocks(sh, nullptr, bkeys + r * bkeys_ld, n, bs_shift, kept, n_blk);
+        select_kept_blocks<kRWaves>(v, nullptr, bkeys + r * bkeys_ld, n, bs_shift, kept, n_blk);
     } else {
-        for (int j = tid; j < n_blk; j += kThreads) sh.kept[j] = j;
+        for (int j = tid; j < n_blk; j += kRThreads) sh.kept[j] = j;
         __syncthreads();
     }
     const int last = sh.kept[kept - 1];
     const int n_c = (kept << bs_shift) - (last == n_blk - 1 ? (int)(((int64_t)n_blk << bs_shift) - n) : 0);
-    const KeptTokens cand{sh.key, sh.kept, bs_shift};
+    const KeptTokens cand{key_lds, sh.kept, bs_shift};
     const int m = topk < n_c ? topk : n_c;
     if (m == n_c) {  // every candidate is selected: nothing to score
-        for (int j = tid; j < n_c; j += kThreads) dst[j] = cand.i(j);
-        for (int j = n_c + tid; j < topk; j += kThreads) dst[j] = -1;
+        for (int j = tid; j < n_c; j += kRThreads) dst[j] = cand.i(j);
+        for (int j = n_c + tid; j < topk; j += kRThreads) dst[j] = -1;
         return;
     }
 
     // q fragments and head weights of the row
     {
         const uint16_t *qr = q_idx + r * (int64_t)kRH * kRD;
-        const int l = tid % kWave, mk = tid / kWave;  // 16 fragments of 64 lanes = the 1024 threads
-        sh.qf[tid] = load16(qr + (32 * (mk / 8) + l % 32) * kRD + 16 * (mk % 8) + 8 * (l / 32));
+#pragma unroll
+        for (int u = 0; u < 2 * (kRD / 16) * kWave / kRThreads; ++u) {
+            const int f = tid + u * kRThreads, l = f % kWave, mk = f / kWave;
+            sh.qf[f] = load16(qr + (32 * (mk / 8) + l % 32) * kRD + 16 * (mk % 8) + 8 * (l / 32));
+        }
         if (tid < kRH) sh.wv[tid] = w[r * kRH + tid];
-        for (int j = tid; j < kBins; j += kThreads) sh.hist[j] = 0;
+        for (int j = tid; j < kBins; j += kRThreads) sh.hist[j] = 0;
     }
     __syncthreads();
     // this lane's 32 head weights, in the order of its accumulator registers: register g of lane l is
@@ -270,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
     // 32 candidates per wave at a time (bs >= 64: a group of 32 lies inside one block)
     const int n_groups = (n_c + 31) / 32;
 #pragma unroll 1
-    for (int grp = wave; grp < n_groups; grp += kWaves) {
+    for (int grp = wave; grp < n_groups; grp += kRWaves) {
         const int j = 32 * grp + lane % 32;
         const bool ok = j < n_c;
         const int64_t tok = cand.i(ok ? j : 32 * grp);
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
         if (!page_ok) score = -__builtin_inff();
         if (lane < 32 && ok) {
             const uint32_t key = order_key(score);
-            sh.key[j] = key;
+            key_lds[j] = key;
             atomicAdd(&sh.hist[key >> kBinShift], 1u);
         }
     }
@@ -318,8 +336,8 @@ __global__ __launch_bounds__(kThreads) void block_rescore_topk_kernel(
         }
     }
     __syncthreads();
-    topk::select_and_emit_inline<kWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
-    for (int j = m + tid; j < topk; j += kThreads) dst[j] = -1;
+    topk::select_and_emit_inline<kRWaves>(sh.sel, cand, n_c, sh.bin, sh.above, m, dst);
+    for (int j = m + tid; j < topk; j += kRThreads) dst[j] = -1;
 }
 
 }  // namespace
@@ -332,8 +350,15 @@ hipError_t launch_block_rescore_topk(sa_handle_s &h, const void *q_idx, const fl
     if (L <= 0) return hipSuccess;
     int shift = 0;
     while ((1 << shift) < block_size) ++shift;
+    // the key array holds a row's block keys, then its candidates' keys
+    const int64_t n_blk_max = (pos0 + L + block_size - 1) / block_size;
+    const int64_t items = n_blk_max > (int64_t)n_blocks * block_size ? n_blk_max : (int64_t)n_blocks * block_size;
+    const size_t dyn = (size_t)items * sizeof(uint32_t);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(block_rescore_topk_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
     KernelTimer timer(h, SA_KERNEL_TOPK, st);
-    hipLaunchKernelGGL(block_rescore_topk_kernel, dim3((unsigned)L), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(block_rescore_topk_kernel, dim3((unsigned)L), dim3(kRThreads), dyn, st,
                        reinterpret_cast<const uint16_t *>(q_idx), w, reinterpret_cast<const uint16_t *>(k_idx), table,
                        n_pages, L, pos0, topk, shift, n_blocks, bkeys, bkeys_ld, idx);
     return hipGetLastError();
