@@ -373,7 +373,8 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
 // ---------------------------------------------------------------------------------------
 // Latent layout, decode: selected rows staged in LDS by direct loads
 // ---------------------------------------------------------------------------------------
-constexpr int kDSplitRows = 512;                  // selected rows per decode workgroup
+constexpr int kDSplitRows = 512;                  // selected rows per decode workgroup (many rows: 1024)
+constexpr int kDSplitRowsMax = 2 * kDSplitRows;
 constexpr int kRing = 3;                          // chunk slots in LDS: two chunks in flight
 constexpr int kRowBytes = kLDqk * 2;              // 1152
 constexpr int kSlotBytes = kChunk * kRowBytes;    // 36864
@@ -406,8 +407,8 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((kVm & 0xF) | ((kVm >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Decode attention over one sequence's selected rows, split in ranges of 512 across workgroups
-// (partials merged by attn_merge_kernel).  The rows of a 32-row chunk reach LDS through direct
+// Decode attention over one sequence's selected rows, split in ranges of 512 (or, for many rows, 1024)
+// across workgroups (partials merged by attn_merge_kernel).  The rows of a 32-row chunk reach LDS through direct
 // global-to-LDS loads, 128 contiguous bytes of a row per lane octet, two chunks ahead of the one
 // being computed, so no register holds a row in flight and every row is read once at the full
 // gather rate.  Per chunk the math is that of attn_latent_mfma_kernel: logits on
@@ -416,10 +417,10 @@ __device__ __forceinline__ void wait_vmcnt()
 // slot an in-flight direct load writes, and would otherwise wait for all of them before every read.
 __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
     const uint16_t *__restrict__ q, RowSource kv, Visibility vis, Selection sel, float scale_log2,
-    int n_splits, float *__restrict__ part_o, float *__restrict__ part_ml, uint32_t *err)
+    int split_rows, int n_splits, float *__restrict__ part_o, float *__restrict__ part_ml, uint32_t *err)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char ring[];  // kRing slots of kSlotBytes
-    __shared__ int64_t rows[kDSplitRows];  // pool row of each selected slot of the range (-1: none)
+    __shared__ int64_t rows[kDSplitRowsMax];  // pool row of each selected slot of the range (-1: none)
     __shared__ float logits[2][kLH * kLogitLd];
     __shared__ uint4 p_hi[kLH][4], p_lo[kLH][4];
     __shared__ float alpha_s[kLH];
@@ -432,10 +433,10 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
     const int64_t visible = visible_len(vis, r, err0);
     const int64_t kr = budget(sel, r, err0);
     const int64_t m = kr < visible ? kr : visible;
-    const int64_t j_begin = (int64_t)split * kDSplitRows;
+    const int64_t j_begin = (int64_t)split * split_rows;
     if (j_begin >= m) return;  // the merge kernel ignores unused splits
     const int64_t tb = kv.block_table ? kv.seq_of(r) : r;  // block-table row of the sequence
-    const int n_here = (int)(m - j_begin < kDSplitRows ? m - j_begin : kDSplitRows);
+    const int n_here = (int)(m - j_begin < split_rows ? m - j_begin : split_rows);
     const int n_chunks = (n_here + kChunk - 1) / kChunk;
     const int32_t *idx_row = sel.idx + r * sel.idx_ld + j_begin;
 
@@ -447,15 +448,17 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
 
     // pool row of every selected slot of the range: all indices, then all page lookups
     {
-        int32_t sv[kDSplitRows / kAThreads];
+        // split_rows is 512 or 1024: the second half of the loops runs only for 1024-row ranges
+        int32_t sv[kDSplitRowsMax / kAThreads];
 #pragma unroll
-        for (int k = 0; k < kDSplitRows / kAThreads; ++k) {
+        for (int k = 0; k < kDSplitRowsMax / kAThreads; ++k) {
             const int j = tid + kAThreads * k;
             sv[k] = j < n_here ? idx_row[j] : -1;
         }
 #pragma unroll
-        for (int k = 0; k < kDSplitRows / kAThreads; ++k) {
+        for (int k = 0; k < kDSplitRowsMax / kAThreads; ++k) {
             const int j = tid + kAThreads * k;
+            if (kAThreads * k >= split_rows) break;
             const int64_t s = sv[k];
             int64_t row = -1;
             if (j < n_here) {
@@ -788,7 +791,11 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSo
             return hipGetLastError();
         }
         // decode: the selected rows staged in LDS by direct loads, 512-row ranges per workgroup, then the merge
-        const int n_splits = (h.cfg.max_topk + kDSplitRows - 1) / kDSplitRows;
+        // 512-row ranges while the rows' ranges fill at most two rounds of workgroups on the CUs; beyond,
+        // 1024-row ranges halve the per-workgroup start (the index and page lookups before the first chunk)
+        const int64_t ranges512 = n_rows * ((h.cfg.max_topk + kDSplitRows - 1) / kDSplitRows);
+        const int split_rows = ranges512 <= 2 * (int64_t)h.n_cu ? kDSplitRows : kDSplitRowsMax;
+        const int n_splits = (h.cfg.max_topk + split_rows - 1) / split_rows;
         float *part_o = reinterpret_cast<float *>(ws);
         float *part_ml = part_o + (size_t)n_rows * n_splits * kLH * kLDv;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_decode_lds_kernel),
@@ -797,13 +804,14 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSo
         {
             KernelTimer timer(h, SA_KERNEL_ATTENTION, st);
             hipLaunchKernelGGL(attn_decode_lds_kernel, dim3((unsigned)n_rows, (unsigned)n_splits), dim3(kAThreads),
-                               kRingBytes, st, qq, kv, vis, sel, scale_log2, n_splits, part_o, part_ml, h.d_err);
+                               kRingBytes, st, qq, kv, vis, sel, scale_log2, split_rows, n_splits, part_o, part_ml,
+                               h.d_err);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         KernelTimer timer(h, SA_KERNEL_MERGE, st);
         hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)(n_rows * kLH)), dim3(kLDv / 4), 0, st, vis, sel,
-                           kDSplitRows, n_splits, part_o, part_ml, out, lse);
+                           split_rows, n_splits, part_o, part_ml, out, lse);
         return hipGetLastError();
     }
     const sa_config_t &c = h.cfg;
