@@ -12,8 +12,8 @@ per-kernel times (HIP events the library records around each launch on the launc
 the roofline of the dominant kernel (the fused prefill indexer / top-k) and of the decode
 kernels, the index projections, the two-tier (block -> token) selection variant of both
 steps, a chunked prefill against the paged caches, the acceptance-rate statistic, the RL-rollout
-decode sweep (256 sequences, context 1K..32K, per-sequence budgets), and the CPU oracle's throughput
-on a bounded sample ride along.
+decode sweep (256 sequences, context 1K..32K, per-sequence budgets), cold-cache medians of both calls
+(a 512 MiB write before each timed call), and the CPU oracle's throughput on a bounded sample ride along.
 
 HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
 calibrated on the 1 GiB copy it performs after the warm-up, and stored in
@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill (paged query rows) measurement")
     ap.add_argument("--no-acceptance", action="store_true", help="skip the acceptance-rate measurement")
     ap.add_argument("--no-rl-sweep", action="store_true", help="skip the RL-rollout decode sweep")
+    ap.add_argument("--flush-reps", type=int, default=20,
+                    help="cold-cache timing: reps of each call with a 512 MiB write before each (0 skips)")
     ap.add_argument("--main-only", action="store_true",
                     help="time the step alone (no projections, two-tier, chunked-prefill or acceptance legs)")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -154,6 +156,7 @@ def main():
         return
     if args.main_only:
         args.no_projections = args.no_two_tier = args.no_chunk = args.no_acceptance = args.no_rl_sweep = True
+        args.flush_reps = 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -306,6 +309,21 @@ def main():
                 rf["frac_of_measured"] = round(rf["achieved"] / peaks[key], 4)
                 rf["measured_peak"] = key
 
+    if profile:
+        sa.sparse_attn_profile(h_pre, False)
+        sa.sparse_attn_profile(h_dec, False)
+    flushed = None
+    if args.flush_reps > 0:
+        flushed = {"reps": args.flush_reps, "flush_bytes": FLUSH_BYTES,
+                   "prefill_ms_median": round(cold_median(prefill, args.flush_reps, torch), 4),
+                   "decode_ms_median": round(cold_median(decode, args.flush_reps, torch), 4)}
+        flushed["prefill_tokens_per_s"] = round(L / (flushed["prefill_ms_median"] * 1e-3), 1)
+        flushed["decode_tokens_per_s"] = round(B / (flushed["decode_ms_median"] * 1e-3), 1)
+        sa.sparse_attn_check(h_pre)
+        sa.sparse_attn_check(h_dec)
+        log(f"[bench] cold-cache medians: prefill {flushed['prefill_ms_median']:.3f} ms, "
+            f"decode {flushed['decode_ms_median']:.4f} ms")
+
     projections = None if args.no_projections else measure_projections(h_pre, P, L, args.steps, torch)
     two_tier = None if args.no_two_tier else measure_two_tier(cfg, P, D, L, K, args, torch)
     chunk = None if args.no_chunk else measure_chunk(cfg, P, D, K, args, torch)
@@ -341,6 +359,7 @@ def main():
         "roofline_decode_indexer": roofline_dec_idx,
         "roofline_decode_gather": roofline_dec_attn,
         "kernels": kernels,
+        "cold_cache": flushed,
         "peaks_measured": peaks,
         "projections": projections,
         "two_tier": two_tier,
@@ -352,6 +371,25 @@ def main():
     print(json.dumps(result), flush=True)
     h_pre.close()
     h_dec.close()
+
+
+FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB Infinity Cache
+
+
+def cold_median(fn, reps, torch):
+    """Median over `reps` calls of fn, each timed alone with events on the current stream after a
+    512 MiB write has evicted the L2 and Infinity Cache (the write itself is outside the timed span)."""
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(ev):
+        buf.fill_(i & 0xFF)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    del buf
+    return ms[reps // 2] if reps % 2 else 0.5 * (ms[reps // 2 - 1] + ms[reps // 2])
 
 
 def measure_projections(h, P, L, steps, torch):
@@ -751,7 +789,13 @@ def cpu_baseline(P, wl, K, seconds):
     t0 = run(n0)
     n = int(min(4096, max(n0, n0 * seconds / max(t0, 1e-3))))
     t = run(n)
-    return {"value": round(n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": round(n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model,
             "sample": f"{n} uniformly drawn query rows of the L={L} prefill (indexer over all "
                       f"preceding keys, top-{K}, attention), {t:.1f} s on {threads} threads"}
 
