@@ -642,7 +642,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
 
 // Merge the per-split softmax states of each decode row: O = sum_s 2^(m_s - M) o_s /
 // sum_s 2^(m_s - M) l_s with M = max_s m_s.  One 128-thread workgroup per (row, head), four
-// value columns per thread.
+// value columns per thread.  Every split's (m, l) and o are loaded in one batch (at most
+// kMergeMaxSplits: top-k <= 8192 in ranges of >= 512), then summed in split order.
+constexpr int kMergeMaxSplits = 16;
 __global__ __launch_bounds__(128) void attn_merge_kernel(
     Visibility vis, Selection sel, int split_rows, int n_splits, const float *__restrict__ part_o,
     const float *__restrict__ part_ml, float *__restrict__ out, float *__restrict__ lse)
@@ -656,22 +658,35 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(
     const int64_t m = k < visible ? k : visible;
     const int used = (int)((m + split_rows - 1) / split_rows);
     const float neg_inf = -__builtin_inff();
+    float ms[kMergeMaxSplits], ls[kMergeMaxSplits];
+    float4 o[kMergeMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMergeMaxSplits; ++s) {
+        if (s < used) {
+            const int64_t slot = (r * n_splits + s) * kLH + h;
+            const float2 ml = reinterpret_cast<const float2 *>(part_ml)[slot];
+            ms[s] = ml.x;
+            ls[s] = ml.y;
+            o[s] = reinterpret_cast<const float4 *>(part_o + slot * kLDv)[threadIdx.x];
+        }
+    }
     float M = neg_inf;
-    for (int s = 0; s < used; ++s) M = fmaxf(M, part_ml[((r * n_splits + s) * kLH + h) * 2]);
+#pragma unroll
+    for (int s = 0; s < kMergeMaxSplits; ++s)
+        if (s < used) M = fmaxf(M, ms[s]);
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
     float den = 0.f;
     if (M != neg_inf) {
-        for (int s = 0; s < used; ++s) {
-            const int64_t slot = (r * n_splits + s) * kLH + h;
-            const float ms = part_ml[slot * 2];
-            if (ms == neg_inf) continue;
-            const float f = exp2f(ms - M);
-            den = fmaf(part_ml[slot * 2 + 1], f, den);
-            const float4 o = reinterpret_cast<const float4 *>(part_o + slot * kLDv)[threadIdx.x];
-            num.x = fmaf(o.x, f, num.x);
-            num.y = fmaf(o.y, f, num.y);
-            num.z = fmaf(o.z, f, num.z);
-            num.w = fmaf(o.w, f, num.w);
+#pragma unroll
+        for (int s = 0; s < kMergeMaxSplits; ++s) {
+            if (s < used && ms[s] != neg_inf) {  // a split without a visible row adds nothing
+                const float f = exp2f(ms[s] - M);
+                den = fmaf(ls[s], f, den);
+                num.x = fmaf(o[s].x, f, num.x);
+                num.y = fmaf(o[s].y, f, num.y);
+                num.z = fmaf(o[s].z, f, num.z);
+                num.w = fmaf(o[s].w, f, num.w);
+            }
         }
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -790,12 +805,13 @@ hipError_t launch_attention(sa_handle_s &h, const void *q, int64_t n_rows, RowSo
                                kv, vis, sel, scale_log2, out, lse, h.d_err);
             return hipGetLastError();
         }
-        // decode: the selected rows staged in LDS by direct loads, 512-row ranges per workgroup, then the merge
+        // decode: the selected rows staged in LDS by direct loads, one range of rows per workgroup, then the merge;
         // 512-row ranges while the rows' ranges fill at most two rounds of workgroups on the CUs; beyond,
         // 1024-row ranges halve the per-workgroup start (the index and page lookups before the first chunk)
         const int64_t ranges512 = n_rows * ((h.cfg.max_topk + kDSplitRows - 1) / kDSplitRows);
         const int split_rows = ranges512 <= 2 * (int64_t)h.n_cu ? kDSplitRows : kDSplitRowsMax;
         const int n_splits = (h.cfg.max_topk + split_rows - 1) / split_rows;
+        if (n_splits > kMergeMaxSplits) return hipErrorInvalidValue;  // max_topk <= 8192 keeps it <= 16
         float *part_o = reinterpret_cast<float *>(ws);
         float *part_ml = part_o + (size_t)n_rows * n_splits * kLH * kLDv;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_decode_lds_kernel),

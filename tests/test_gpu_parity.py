@@ -372,6 +372,29 @@ def test_decode_rl_sweep_step(n):
     _check_decode(d, out, lse, idx, [0, 7, 100, 128, 200, 255], 512, f"rl n={n}")
 
 
+def test_decode_1024_row_ranges_at_boundaries():
+    """64 sequences with budgets up to 8192 spread their selected rows over more workgroups than two
+    rounds of the CUs take, so the decode attention runs 1024-row ranges; budgets and contexts sit on
+    and around the range and chunk boundaries (1, 32, 1023..1025, 2047, 2049, 8192)."""
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], topk=8192)
+    base_ctx = [1, 33, 1024, 1025, 2047, 3000, 8192, 9000]
+    base_k = [1, 32, 1023, 1025, 2047, 2049, 8192, 8192]
+    ctx = np.array([base_ctx[b % 8] for b in range(64)])
+    k = np.array([base_k[(b + b // 8) % 8] for b in range(64)])
+    say(f"decode 1024-row ranges B=64 max_topk=8192 ctx={base_ctx} k={base_k}")
+    d = inputs.decode_inputs(wl, DEV, ctx=ctx, seed=21)
+    d["topk"] = torch.from_numpy(k.astype(np.int32)).to(DEV)
+    with sa.Handle(inputs.library_config(wl, max_topk=8192)) as h:
+        out, lse, idx = _decode(h, d)
+    gi = to_np(idx)
+    for b in range(64):
+        m = min(int(k[b]), int(ctx[b]))
+        assert np.all(gi[b][:m] >= 0) and np.all(gi[b][m:] == -1), f"seq {b}: {m} selected slots"
+    # one sequence per distinct (context, budget) pair
+    seqs = sorted({(int(c), int(kb)): b for b, (c, kb) in enumerate(zip(ctx, k))}.values())
+    _check_decode(d, out, lse, idx, seqs, 512, "decode 1024-row ranges")
+
+
 # ---------------------------------------------------------------------------------------
 # error paths that need a device
 # ---------------------------------------------------------------------------------------
