@@ -395,6 +395,19 @@ def test_decode_1024_row_ranges_at_boundaries():
     _check_decode(d, out, lse, idx, seqs, 512, "decode 1024-row ranges")
 
 
+def test_decode_sixteen_512_row_ranges():
+    """Few sequences with budgets up to 8192: 512-row ranges, up to 16 partial states merged per head."""
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], topk=8192)
+    ctx = np.array([9000, 8192, 8193, 5000])
+    k = np.array([8192, 8192, 7681, 4097])
+    say(f"decode 512-row ranges B=4 max_topk=8192 ctx={ctx.tolist()} k={k.tolist()}")
+    d = inputs.decode_inputs(wl, DEV, ctx=ctx, seed=22)
+    d["topk"] = torch.from_numpy(k.astype(np.int32)).to(DEV)
+    with sa.Handle(inputs.library_config(wl, max_topk=8192)) as h:
+        out, lse, idx = _decode(h, d)
+    _check_decode(d, out, lse, idx, np.arange(4), 512, "decode 16 ranges")
+
+
 # ---------------------------------------------------------------------------------------
 # error paths that need a device
 # ---------------------------------------------------------------------------------------
