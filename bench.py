@@ -330,9 +330,10 @@ def main():
     acceptance = None if args.no_acceptance else measure_acceptance(cfg, args, torch)
     rl_sweep = None if args.no_rl_sweep else measure_rl_sweep(args, torch)
 
-    cpu = None
+    cpu = cpu_dec = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(P, pre_wl, K, args.cpu_seconds)
+        cpu_dec = cpu_baseline_decode(D, dec_wl, K, args.cpu_seconds / 3)
 
     result = {
         "metric": METRIC,
@@ -367,6 +368,7 @@ def main():
         "acceptance": acceptance,
         "rl_sweep": rl_sweep,
         "cpu_baseline": cpu,
+        "cpu_baseline_decode": cpu_dec,
     }
     print(json.dumps(result), flush=True)
     h_pre.close()
@@ -798,6 +800,54 @@ def cpu_baseline(P, wl, K, seconds):
     return {"value": round(n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model,
             "sample": f"{n} uniformly drawn query rows of the L={L} prefill (indexer over all "
                       f"preceding keys, top-{K}, attention), {t:.1f} s on {threads} threads"}
+
+
+def cpu_baseline_decode(D, wl, K, seconds):
+    """The oracle's decode step on a bounded sample of the decode workload: whole sequences (index
+    keys of every cached token scored, top-k, attention over the selected latent rows), their pages
+    copied to the host beforehand and only the oracle call timed.  Sequences/s = decode tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    page = D["kv_pages"].shape[1]
+    threads = oracle.num_threads()
+
+    def host_seqs(seqs):
+        tabs, kv, ki = [], [], []
+        base = 0
+        for b in seqs:
+            n_pg = -(-int(D["ctx_np"][b]) // page)
+            pages = D["block_table"][b, :n_pg].long()
+            kv.append(D["kv_pages"][pages].float().cpu().numpy())
+            ki.append(D["kidx_pages"][pages].float().cpu().numpy())
+            tabs.append(np.arange(base, base + n_pg, dtype=np.int32))
+            base += n_pg
+        width = max(len(t) for t in tabs)
+        table = np.full((len(seqs), width), -1, dtype=np.int32)
+        for i, t in enumerate(tabs):
+            table[i, :len(t)] = t
+        sel = torch.as_tensor(np.asarray(seqs), device=D["q"].device)
+        pick = lambda t: t[sel].float().cpu().numpy()
+        return (pick(D["q"]), pick(D["q_idx"]), pick(D["w"]), np.concatenate(kv), np.concatenate(ki), table,
+                D["ctx_np"][seqs], D["topk"][sel].cpu().numpy())
+
+    def run(seqs):
+        q, q_idx, w, kv, ki, table, ctx, topk = host_seqs(seqs)
+        t0 = time.perf_counter()
+        oracle.decode(q, q_idx, w, kv, None, ki, table, ctx, topk, k_max=K, d_v=512)
+        return time.perf_counter() - t0
+
+    B = D["q"].shape[0]
+    log(f"[bench] cpu baseline: oracle decode on sampled sequences (~{seconds:.0f} s, {threads} threads)")
+    t1 = run([0])
+    n = int(min(B, 16, max(1, seconds / max(t1, 1e-3))))  # at most 16 sequences' pages on the host
+    seqs = list(range(1, 1 + n)) if n < B else list(range(B))
+    t = run(seqs)
+    return {"value": round(len(seqs) / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(seqs)} of the B={B} sequences of the decode step at ctx={int(D['ctx_np'].max())} "
+                      f"(indexer over every cached token, top-{K}, attention), {t:.1f} s on {threads} threads"}
 
 
 if __name__ == "__main__":
