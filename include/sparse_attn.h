@@ -92,6 +92,7 @@ typedef struct {
 #define SA_OP_DECODE_BLOCKS  6  /* sparse_attn_decode_blocks: as SA_OP_DECODE             */
 #define SA_OP_PREFILL_PAGED  7  /* sparse_attn_prefill_paged: n = T query rows, max_ctx   */
 #define SA_OP_PREFILL_CHUNK  8  /* sparse_attn_prefill_chunk: n = C rows, max_ctx = pos0 + C */
+#define SA_OP_PREFILL_VARLEN 9  /* sparse_attn_prefill_varlen: n = T rows, max_ctx           */
 
 /* Create a handle for one configuration.  Validates the config, allocates the 4-byte
  * device error word on the current device (the only device allocation the library makes)
@@ -258,6 +259,32 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
                                       int32_t max_blocks, const int32_t *row_seq, const int32_t *row_pos,
                                       int64_t T, int32_t max_ctx, int32_t topk, float *out, float *lse,
                                       int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Prefill of a batch of sequences against their paged caches (varlen layout): sequence b owns the
+ * query rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1, which are its newest tokens, at positions
+ * ctx_len[b] - n_new .. ctx_len[b] - 1 (n_new = cu_seqlens[b + 1] - cu_seqlens[b]); the caches must
+ * already hold all ctx_len[b] tokens.  The same computation as sparse_attn_prefill_paged with those
+ * (row_seq, row_pos) pairs -- "Sparse Attention and RL Optimization...", sections 2.2, 2.3 and 2.5
+ * (the batched teacher-forcing pass); "Long-Context LLMs Explained...", section 2.3 -- for the case
+ * where each sequence's rows are contiguous but the layout is known only on the device: with bf16,
+ * H_I = 64, d_I = 128 and 64-token pages (and max_ctx <= 524288) every sequence's rows run as tiles of
+ * 8 rows of the fused prefill indexer / top-k, sharing every key tile (one page) between them.
+ *   q [T, H, d_qk], q_idx [T, H_I, d_I], w [T, H_I] fp32; pools and block_table [n_seqs, max_blocks]
+ *   as in sparse_attn_decode
+ *   cu_seqlens [n_seqs + 1] int32 (device): 0 = cu_seqlens[0] <= ... <= cu_seqlens[n_seqs] = T
+ *   ctx_len [n_seqs] int32 (device): cached tokens per sequence, n_new <= ctx_len[b] <= max_ctx
+ *   max_ctx    host-side bound of every ctx_len, <= max_blocks * page_size; topk in [1, max_topk]
+ *   out [T, H, d_v] fp32; lse [T, H] or NULL; idx_out [T, topk] or NULL (positions, ascending, -1 pad)
+ *   ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_PREFILL_VARLEN, T, max_ctx)
+ * A sequence that breaks these bounds sets SA_DEVERR_ROW and its rows are skipped (a row of no valid
+ * sequence gets -1 indices when the fused tiles run; its outputs are otherwise unspecified).  Errors:
+ * SA_ERR_INVALID_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP; device-side bits as in sparse_attn_decode. */
+sa_status_t sparse_attn_prefill_varlen(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                       const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                       int64_t n_pages, const int32_t *block_table, int32_t n_seqs,
+                                       int32_t max_blocks, const int32_t *cu_seqlens, const int32_t *ctx_len,
+                                       int64_t T, int32_t max_ctx, int32_t topk, float *out, float *lse,
+                                       int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Chunked prefill of one sequence against its paged caches: query row i is the token at position
  * pos0 + i (i < C) of the sequence whose block-table row is block_table_row [max_blocks]; it sees the

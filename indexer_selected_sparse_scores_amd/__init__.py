@@ -28,14 +28,15 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_DEVICE_CHECK = range(6)
 SA_F32, SA_BF16 = 0, 1
 SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK, SA_OP_PROJECT, SA_OP_PREFILL_BLOCKS, SA_OP_DECODE_BLOCKS = 1, 2, 3, 4, 5, 6
-SA_OP_PREFILL_PAGED, SA_OP_PREFILL_CHUNK = 7, 8
+SA_OP_PREFILL_PAGED, SA_OP_PREFILL_CHUNK, SA_OP_PREFILL_VARLEN = 7, 8, 9
 SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK, SA_DEVERR_ROW = 1, 2, 4, 8, 16
 
 # Every symbol include/sparse_attn.h declares.
 EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error",
             "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
             "topk_select_blocks", "sparse_attn_prefill", "sparse_attn_prefill_blocks", "sparse_attn_decode",
-            "sparse_attn_decode_blocks", "sparse_attn_prefill_paged", "sparse_attn_prefill_chunk", "indexer_project_q",
+            "sparse_attn_decode_blocks", "sparse_attn_prefill_paged", "sparse_attn_prefill_chunk", "sparse_attn_prefill_varlen",
+            "indexer_project_q",
             "indexer_project_k",
             "acceptance_rate", "acceptance_bin_stats",
             "sparse_attn_profile", "sparse_attn_profile_read")
@@ -107,6 +108,8 @@ def load_library() -> ctypes.CDLL:
         "sparse_attn_prefill_paged": ([P, P, P, P, P, P, P, i64, P, i32, i32, P, P, i64, i32, i32, P, P, P, P, sz,
                                        P], st),
         "sparse_attn_prefill_chunk": ([P, P, P, P, P, P, P, i64, P, i32, i64, i64, i32, P, P, P, P, sz, P], st),
+        "sparse_attn_prefill_varlen": ([P, P, P, P, P, P, P, i64, P, i32, i32, P, P, i64, i32, i32, P, P, P, P, sz,
+                                        P], st),
         "indexer_project_q": ([P, P, i64, P, P, P, P, P, sz, P], st),
         "acceptance_rate": ([P, P, P, i64, i64, i64, P, P], st),
         "acceptance_bin_stats": ([P, P, P, i64, i32, i32, ctypes.c_float, P, P, P, P], st),
@@ -282,6 +285,21 @@ def sparse_attn_prefill_paged(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pa
     _check(h.ptr, load_library().sparse_attn_prefill_paged(
         h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
         _ptr(block_table), n_seqs, max_blocks, _ptr(row_seq), _ptr(row_pos), T, int(max_ctx), int(topk), _ptr(out),
+        _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_prefill_varlen(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, cu_seqlens,
+                               ctx_len, max_ctx: int, topk: int, out, lse=None, idx_out=None, ws=None,
+                               stream=None) -> None:
+    """Sequence b owns query rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1, its newest tokens among its
+    ctx_len[b] cached ones (device int32 arrays), over its paged caches."""
+    T = q.shape[0]
+    n_pages = kv_pages.shape[0]
+    n_seqs, max_blocks = block_table.shape
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(h.ptr, load_library().sparse_attn_prefill_varlen(
+        h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
+        _ptr(block_table), n_seqs, max_blocks, _ptr(cu_seqlens), _ptr(ctx_len), T, int(max_ctx), int(topk), _ptr(out),
         _ptr(lse), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
 
 

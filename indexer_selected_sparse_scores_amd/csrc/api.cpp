@@ -215,6 +215,42 @@ sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const f
                         const BlockSelect *blocks, float *out, float *lse, int32_t *idx_out, void *ws,
                         size_t ws_bytes, void *stream);
 
+// A batch of sequences with their new rows contiguous: the fused row tiles need the fast kernels and at
+// most kPrefillMaxPages pages per sequence; otherwise the rows run as sparse_attn_prefill_paged's rows.
+bool varlen_fused(const sa_handle_s &h, int64_t max_ctx)
+{
+    return h.fast_decode && (max_ctx + 63) / 64 <= sa::kPrefillMaxPages;
+}
+
+// Fused: [row_seq | row_pos | seq | ctx | budget | idx | split-attention partials (few rows) | fused
+// indexer/top-k workspace].  Otherwise: [row_seq | row_pos | sparse_attn_prefill_paged's workspace].
+struct VarlenApiLayout {
+    size_t row_seq, row_pos, seq, ctx, budget, idx, attn, rest, total;
+    bool split;
+};
+
+VarlenApiLayout varlen_api_layout(const sa_handle_s &h, int64_t T, int64_t max_ctx)
+{
+    VarlenApiLayout v{};
+    const size_t rows = align_up((size_t)T * sizeof(int32_t));
+    v.row_seq = 0;
+    v.row_pos = rows;
+    if (!varlen_fused(h, max_ctx)) {
+        v.rest = 2 * rows;
+        v.total = v.rest + paged_layout(h, T, max_ctx).total;
+        return v;
+    }
+    v.split = h.fast_attn && T < h.n_cu;
+    v.seq = 2 * rows;
+    v.ctx = 3 * rows;
+    v.budget = 4 * rows;
+    v.idx = 5 * rows;
+    v.attn = v.idx + align_up((size_t)T * (size_t)h.cfg.max_topk * sizeof(int32_t));
+    v.rest = v.attn + align_up(v.split ? sa::attention_workspace(h, T, true) : 0);
+    v.total = v.rest + align_up(sa::prefill_varlen_workspace(h, T, (int32_t)max_ctx));
+    return v;
+}
+
 }  // namespace
 
 namespace sa {
@@ -407,6 +443,11 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
         if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T exceeds the launch limit");
         if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
         *bytes = paged_layout(*h, n, max_ctx).total;
+        return SA_OK;
+    case SA_OP_PREFILL_VARLEN:
+        if (n > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T exceeds the launch limit");
+        if (max_ctx < 1 || max_ctx > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be in [1, 2^31)");
+        *bytes = varlen_api_layout(*h, n, max_ctx).total;
         return SA_OK;
     case SA_OP_TOPK:
         *bytes = 0;
@@ -796,6 +837,76 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
         }
         if (s != SA_OK) return s;
     }
+    sa::RowSource kv{kv_pages, (int64_t)c.n_kv_heads * c.d_qk, block_table, max_blocks, c.page_size, n_pages, seq};
+    sa::RowSource vv{v_pages, (int64_t)c.n_kv_heads * c.d_v, block_table, max_blocks, c.page_size, n_pages, seq};
+    sa::Visibility vis{0, ctx, max_ctx};
+    sa::Selection sel{idx, topk, topk, nullptr};
+    return hip_status(h, sa::launch_attention(*h, q, T, kv, vv, vis, sel, out, lse, base + lay.attn, st, lay.split),
+                      "attention launch");
+}
+
+sa_status_t sparse_attn_prefill_varlen(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                       const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                       int64_t n_pages, const int32_t *block_table, int32_t n_seqs,
+                                       int32_t max_blocks, const int32_t *cu_seqlens, const int32_t *ctx_len,
+                                       int64_t T, int32_t max_ctx, int32_t topk, float *out, float *lse,
+                                       int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    const sa_config_t &c = h->cfg;
+    if (!q || !q_idx || !w || !kv_pages || !kidx_pages || !block_table || !cu_seqlens || !ctx_len || !out)
+        return fail(h, SA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (c.v_from_k ? v_pages != nullptr : v_pages == nullptr)
+        return fail(h, SA_ERR_INVALID_ARG, c.v_from_k ? "v_pages must be NULL when v_from_k = 1"
+                                                      : "v_pages must not be NULL when v_from_k = 0");
+    if (T < 1 || T > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T must be in [1, 2^31)");
+    if (n_seqs < 1) return fail(h, SA_ERR_INVALID_ARG, "n_seqs must be >= 1");
+    if (n_pages < 1) return fail(h, SA_ERR_INVALID_ARG, "n_pages must be >= 1");
+    if (max_blocks < 1) return fail(h, SA_ERR_INVALID_ARG, "max_blocks must be >= 1");
+    if (max_ctx < 1 || (int64_t)max_ctx > (int64_t)max_blocks * c.page_size)
+        return fail(h, SA_ERR_INVALID_ARG, "max_ctx (%d) must be in [1, max_blocks * page_size = %lld]",
+                    max_ctx, (long long)max_blocks * c.page_size);
+    if (topk < 1 || topk > c.max_topk)
+        return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
+    if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
+        (v_pages && !aligned16(v_pages)))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+    const VarlenApiLayout lay = varlen_api_layout(*h, T, max_ctx);
+    if (!ws || ws_bytes < lay.total)
+        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
+    sa_status_t s = check_device(h);
+    if (s != SA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *base = reinterpret_cast<char *>(ws);
+    int32_t *row_seq = reinterpret_cast<int32_t *>(base + lay.row_seq);
+    int32_t *row_pos = reinterpret_cast<int32_t *>(base + lay.row_pos);
+    if (!varlen_fused(*h, max_ctx)) {
+        // the rows' (sequence, position) pairs, then the paged rows' path
+        s = hip_status(h, sa::launch_varlen_rows(*h, cu_seqlens, ctx_len, n_seqs, T, max_ctx, topk, nullptr, row_seq,
+                                                 row_pos, st),
+                       "row layout launch");
+        if (s != SA_OK) return s;
+        return sparse_attn_prefill_paged(h, q, q_idx, w, kv_pages, v_pages, kidx_pages, n_pages, block_table, n_seqs,
+                                         max_blocks, row_seq, row_pos, T, max_ctx, topk, out, lse, idx_out,
+                                         base + lay.rest, ws_bytes - lay.rest, stream);
+    }
+    int32_t *seq = reinterpret_cast<int32_t *>(base + lay.seq);
+    int32_t *ctx = reinterpret_cast<int32_t *>(base + lay.ctx);
+    int32_t *budget = reinterpret_cast<int32_t *>(base + lay.budget);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(base + lay.idx);
+    s = hip_status(h, sa::launch_varlen_rows(*h, cu_seqlens, ctx_len, n_seqs, T, max_ctx, topk, idx, row_seq, row_pos,
+                                             st),
+                   "row layout launch");
+    if (s != SA_OK) return s;
+    s = hip_status(h, sa::launch_paged_rows(*h, row_seq, row_pos, T, n_seqs, max_ctx, topk, seq, ctx, budget, st),
+                   "row check launch");
+    if (s != SA_OK) return s;
+    s = hip_status(h, sa::launch_prefill_varlen(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks,
+                                                cu_seqlens, ctx_len, n_seqs, T, max_ctx, topk, idx, base + lay.rest,
+                                                st),
+                   "indexer/top-k launch");
+    if (s != SA_OK) return s;
     sa::RowSource kv{kv_pages, (int64_t)c.n_kv_heads * c.d_qk, block_table, max_blocks, c.page_size, n_pages, seq};
     sa::RowSource vv{v_pages, (int64_t)c.n_kv_heads * c.d_v, block_table, max_blocks, c.page_size, n_pages, seq};
     sa::Visibility vis{0, ctx, max_ctx};

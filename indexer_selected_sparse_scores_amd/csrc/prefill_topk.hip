@@ -73,13 +73,21 @@ struct Shared {
     int32_t pages[kPaged ? kPrefillMaxPages : 1];  // pool page of each 64-key tile (-1: bad entry)
 };
 
+// One row tile of a batch of sequences (32 bytes): rows q0 .. min(q0 + 8, len) - 1 of sequence seq.
+struct VarlenTile {
+    int32_t seq, q0, len, pos0, rowbase, pad[3];
+};
+
 // Where the index keys come from: contiguous rows, or the 64-token pages of one sequence's block-table
-// row (a key tile is exactly one page).
+// row (a key tile is exactly one page).  With a tile table (a batch of sequences), each row tile names
+// its sequence, whose block-table row is table + seq * table_ld.
 struct KeySource {
     const uint16_t *base;
-    const int32_t *table;   // paged: the sequence's block-table row
+    const int32_t *table;   // paged: the sequence's block-table row (tile table: the whole block table)
     int64_t n_pages;
     uint32_t *err;
+    const VarlenTile *tiles = nullptr;
+    int64_t table_ld = 0;
 };
 
 // Key tile layout: the 16-byte piece holding dims 8 j .. 8 j + 7 of key r sits at
@@ -116,11 +124,13 @@ struct BlockKeysOut {
 // Query rows i = 0 .. L-1 are the tokens at positions pos0 + i of one sequence; keys are its tokens
 // 0 .. pos0 + L - 1 (contiguous rows, or pages of its block-table row when kPaged).  Rows with at most
 // `need` visible keys are not scored (need = topk: all their keys are selected).
+// With a tile table (kPaged only), tile e = ks.tiles[e] holds rows q0 .. q0 + 7 (< len) of sequence seq,
+// whose len query rows sit at rows rowbase .. of q_idx, w and idx and at positions pos0 .. pos0 + len - 1.
 template <bool kPaged, bool kBlockKeys>
 __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
-    const uint16_t *__restrict__ q_idx, const float *__restrict__ w, KeySource ks, int64_t L, int64_t pos0,
-    int32_t topk, int64_t need, int32_t *__restrict__ idx, uint2 *__restrict__ cands, int64_t cand_ld,
-    BlockKeysOut bk, int32_t *__restrict__ counter, int32_t n_tiles)
+    const uint16_t *__restrict__ q_idx_all, const float *__restrict__ w_all, KeySource ks, int64_t L_all,
+    int64_t pos0_all, int32_t topk, int64_t need, int32_t *__restrict__ idx_all, uint2 *__restrict__ cands,
+    int64_t cand_ld, BlockKeysOut bk, int32_t *__restrict__ counter, int32_t n_tiles)
 {
     __shared__ Shared<kPaged> sh;
     const uint16_t *__restrict__ k_idx = ks.base;
@@ -133,7 +143,26 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
         __syncthreads();
         const int it = sh.tile;
         if (it >= n_tiles) break;
-        const int64_t q0 = (int64_t)(n_tiles - 1 - it) * kRows;  // latest rows first
+        int64_t q0 = (int64_t)(n_tiles - 1 - it) * kRows;  // latest rows first
+        int64_t L = L_all, pos0 = pos0_all, rb = 0;         // this tile's sequence, and its first query row
+        const int32_t *table = ks.table;
+        if constexpr (kPaged) {
+            if (ks.tiles) {
+                const VarlenTile vt = ks.tiles[n_tiles - 1 - it];
+                if (vt.len <= 0) {  // unused entry; the barrier keeps sh.tile until every thread has read it
+                    __syncthreads();
+                    continue;
+                }
+                q0 = vt.q0;
+                L = vt.len;
+                pos0 = vt.pos0;
+                rb = vt.rowbase;
+                table = ks.table + (int64_t)vt.seq * ks.table_ld;
+            }
+        }
+        const uint16_t *q_idx = q_idx_all + rb * kH * kD;
+        const float *w = w_all + rb * kH;
+        int32_t *idx = idx_all + rb * topk;
         // position of the tile's last row (keys 0 .. t_last are streamed)
         const int64_t t_last = pos0 + ((q0 + kRows - 1 < L - 1) ? q0 + kRows - 1 : L - 1);
         const int64_t ri = q0 + wave;    // this wave's query row
@@ -150,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 // the pool page of every key tile of the prefix, checked once (a bad entry is read as page 0
                 // and its keys score -inf)
                 for (int j = tid; j <= (int)(t_last / kKT); j += kThreads) {
-                    const int32_t pg = ks.table[j];
+                    const int32_t pg = table[j];
                     const bool ok = pg >= 0 && pg < ks.n_pages;
                     if (!ok) flag_error(ks.err, SA_DEVERR_BLOCK_TABLE);
                     sh.pages[j] = ok ? pg : -1;
@@ -402,6 +431,73 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
 
 __global__ void reset_counter_kernel(int32_t *counter) { *counter = 0; }
 
+// Sequence b of a batch is valid when 0 <= cu[b] <= cu[b + 1] <= T and its n_b = ctx_len[b] cached tokens
+// (the new ones last) satisfy cu[b + 1] - cu[b] <= n_b <= max_ctx.
+__device__ __forceinline__ bool varlen_seq(const int32_t *cu, const int32_t *ctx_len, int64_t T, int32_t max_ctx,
+                                           int b, int32_t *start, int32_t *len, int32_t *n)
+{
+    *start = cu[b];
+    const int32_t end = cu[b + 1];
+    *n = ctx_len[b];
+    *len = end - *start;
+    return *start >= 0 && *len >= 0 && end <= T && *n >= *len && *n <= max_ctx;
+}
+
+// One workgroup: the row tiles of every valid sequence, in sequence order (an exclusive scan of the
+// per-sequence tile counts), then empty entries up to n_tiles.  An invalid sequence gets no tile.
+constexpr int kVarlenThreads = 1024;
+__global__ __launch_bounds__(kVarlenThreads) void varlen_tiles_kernel(
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ ctx_len, int32_t n_seqs, int64_t T, int32_t max_ctx,
+    VarlenTile *__restrict__ tiles, int32_t n_tiles, uint32_t *err)
+{
+    __shared__ int wave_sums[kVarlenThreads / kWave];
+    const int tid = threadIdx.x;
+    int running = 0;
+#pragma unroll 1
+    for (int b0 = 0; b0 < n_seqs; b0 += kVarlenThreads) {
+        const int b = b0 + tid;
+        int32_t start = 0, len = 0, n = 0;
+        if (b < n_seqs && !varlen_seq(cu, ctx_len, T, max_ctx, b, &start, &len, &n)) {
+            flag_error(err, SA_DEVERR_ROW);
+            len = 0;
+        }
+        const int nt = (len + kRows - 1) / kRows;
+        int total;
+        const int off = running + topk::block_scan<kVarlenThreads / kWave>(nt, wave_sums, &total);
+        for (int i = 0; i < nt; ++i)
+            if (off + i < n_tiles) tiles[off + i] = VarlenTile{b, kRows * i, len, n - len, start, {0, 0, 0}};
+        running += total;
+    }
+    for (int j = running + tid; j < n_tiles; j += kVarlenThreads) tiles[j] = VarlenTile{0, 0, 0, 0, 0, {0, 0, 0}};
+}
+
+// One thread per query row r: its sequence b (cu[b] <= r < cu[b + 1], by binary search) and position
+// n_b - (cu[b + 1] - cu[b]) + (r - cu[b]); a row of no valid sequence gets (-1, -1) and (idx given)
+// an empty selection.
+__global__ void varlen_rows_kernel(const int32_t *__restrict__ cu, const int32_t *__restrict__ ctx_len,
+                                   int32_t n_seqs, int64_t T, int32_t max_ctx, int32_t topk,
+                                   int32_t *__restrict__ row_seq, int32_t *__restrict__ row_pos,
+                                   int32_t *__restrict__ idx, uint32_t *err)
+{
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= T) return;
+    int lo = 0, hi = n_seqs - 1;  // the last b with cu[b] <= r (b = 0 if none)
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (cu[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    int32_t start, len, n;
+    const bool ok = varlen_seq(cu, ctx_len, T, max_ctx, lo, &start, &len, &n) && r >= start && r < start + len;
+    if (!ok) {
+        flag_error(err, SA_DEVERR_ROW);
+        if (idx)
+            for (int i = 0; i < topk; ++i) idx[r * topk + i] = -1;
+    }
+    row_seq[r] = ok ? lo : -1;
+    row_pos[r] = ok ? n - len + (int32_t)(r - start) : -1;
+}
+
 }  // namespace
 
 size_t prefill_block_keys_ld(int64_t L, int64_t pos0) { return (pos0 + L + kKT - 1) / kKT; }
@@ -412,6 +508,66 @@ size_t prefill_topk_workspace(const sa_handle_s &h, int64_t L, int64_t pos0)
     const int64_t slots = n_tiles < h.n_cu ? n_tiles : h.n_cu;
     const int64_t ld = (pos0 + L + 63) / 64 * 64;  // a candidate list holds at most every key
     return 256 + (size_t)slots * kRows * (size_t)ld * sizeof(uint2);
+}
+
+// Capacity for T rows (any number of sequences: at most min(n_seqs, T) of them own rows):
+// [counter | candidate lists of the workgroup slots | tile table]
+struct VarlenLayout {
+    int64_t tiles_cap, slots_cap, ld;
+    size_t cands, tiles, total;
+};
+VarlenLayout varlen_layout(const sa_handle_s &h, int64_t T, int32_t max_ctx)
+{
+    VarlenLayout v;
+    v.tiles_cap = (T + kRows - 1) / kRows + T;
+    v.slots_cap = v.tiles_cap < h.n_cu ? v.tiles_cap : h.n_cu;
+    v.ld = ((int64_t)max_ctx + 63) / 64 * 64;  // a candidate list holds at most every key
+    v.cands = 256;
+    v.tiles = v.cands + (size_t)v.slots_cap * kRows * (size_t)v.ld * sizeof(uint2);
+    v.total = v.tiles + (size_t)v.tiles_cap * sizeof(VarlenTile);
+    return v;
+}
+
+size_t prefill_varlen_workspace(const sa_handle_s &h, int64_t T, int32_t max_ctx)
+{
+    return varlen_layout(h, T, max_ctx).total;
+}
+
+hipError_t launch_varlen_rows(sa_handle_s &h, const int32_t *cu, const int32_t *ctx_len, int32_t n_seqs, int64_t T,
+                              int32_t max_ctx, int32_t topk, int32_t *idx, int32_t *row_seq, int32_t *row_pos,
+                              hipStream_t st)
+{
+    hipLaunchKernelGGL(varlen_rows_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, cu, ctx_len, n_seqs, T,
+                       max_ctx, topk, row_seq, row_pos, idx, h.d_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_varlen(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                 int64_t n_pages, const int32_t *block_table, int32_t max_blocks, const int32_t *cu,
+                                 const int32_t *ctx_len, int32_t n_seqs, int64_t T, int32_t max_ctx, int32_t topk,
+                                 int32_t *idx, void *ws, hipStream_t st)
+{
+    const VarlenLayout v = varlen_layout(h, T, max_ctx);
+    const int64_t n_tiles = (T + kRows - 1) / kRows + (n_seqs < T ? n_seqs : T);
+    const int64_t slots = n_tiles < h.n_cu ? n_tiles : h.n_cu;
+    char *base = reinterpret_cast<char *>(ws);
+    int32_t *counter = reinterpret_cast<int32_t *>(base);
+    uint2 *cands = reinterpret_cast<uint2 *>(base + v.cands);
+    VarlenTile *tiles = reinterpret_cast<VarlenTile *>(base + v.tiles);
+    hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(1), 0, st, counter);
+    hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(kVarlenThreads), 0, st, cu, ctx_len, n_seqs, T, max_ctx,
+                       tiles, (int32_t)n_tiles, h.d_err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    KeySource ks{reinterpret_cast<const uint16_t *>(kidx_pages), block_table, n_pages, h.d_err};
+    ks.tiles = tiles;
+    ks.table_ld = max_blocks;
+    const BlockKeysOut none{nullptr, 0};
+    KernelTimer timer(h, SA_KERNEL_INDEXER, st);
+    hipLaunchKernelGGL((indexer_topk_prefill_kernel<true, false>), dim3((unsigned)slots), dim3(kThreads), 0, st,
+                       reinterpret_cast<const uint16_t *>(q_idx), w, ks, (int64_t)0, (int64_t)0, topk, (int64_t)topk,
+                       idx, cands, v.ld, none, counter, (int32_t)n_tiles);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w, const void *k_idx,

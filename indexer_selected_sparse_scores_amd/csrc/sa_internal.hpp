@@ -131,6 +131,19 @@ hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w
                                int64_t L, int32_t topk, int32_t *idx, void *ws, hipStream_t st,
                                const int32_t *table = nullptr, int64_t n_pages = 0, int64_t pos0 = 0,
                                uint32_t *block_keys = nullptr, int64_t keys_above = 0);
+// A batch of sequences on the same row tiles: sequence b owns query rows cu[b] .. cu[b + 1] - 1, the newest
+// of its ctx_len[b] cached tokens (64-token pages of kidx_pages, block-table row b of block_table with
+// stride max_blocks); max_ctx <= kPrefillMaxPages * 64.  ws holds prefill_varlen_workspace(h, T, max_ctx)
+// bytes.  launch_varlen_rows writes each row's sequence and position to row_seq / row_pos [T] ((-1, -1)
+// and an empty selection in idx for a row of no valid sequence); it runs first.
+size_t prefill_varlen_workspace(const sa_handle_s &h, int64_t T, int32_t max_ctx);
+hipError_t launch_varlen_rows(sa_handle_s &h, const int32_t *cu, const int32_t *ctx_len, int32_t n_seqs, int64_t T,
+                              int32_t max_ctx, int32_t topk, int32_t *idx, int32_t *row_seq, int32_t *row_pos,
+                              hipStream_t st);
+hipError_t launch_prefill_varlen(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                                 int64_t n_pages, const int32_t *block_table, int32_t max_blocks, const int32_t *cu,
+                                 const int32_t *ctx_len, int32_t n_seqs, int64_t T, int32_t max_ctx, int32_t topk,
+                                 int32_t *idx, void *ws, hipStream_t st);
 
 // ---- paged decode indexer + per-sequence top-k (bf16, H_I = 64, d_I = 128, 64-token pages) --
 struct DecodeTopkLayout {

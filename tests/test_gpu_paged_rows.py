@@ -301,3 +301,82 @@ def test_prefill_chunk_at_128k():
     _check(d, out, lse, idx, [0, 1, 2000, C - 2, C - 1], 2048, 512, "prefill_chunk 128k")
     del d, out, lse, idx
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------
+# sparse_attn_prefill_varlen: contiguous rows per sequence, layout on the device only
+# ---------------------------------------------------------------------------------------
+def _varlen(ctx, n_new, topk, seed):
+    """Sequence b's n_new[b] newest tokens as its contiguous rows; cu_seqlens and ctx_len on the device."""
+    rs = np.concatenate([np.full(k, b) for b, k in enumerate(n_new)])
+    rp = np.concatenate([np.arange(c - k, c) for c, k in zip(ctx, n_new)])
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], topk=topk)
+    d = inputs.paged_rows_inputs(wl, ctx, rs, rp, DEV, seed=seed)
+    d["cu"] = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).to(DEV)
+    d["ctx_len"] = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).to(DEV)
+    return wl, d
+
+
+def _run_varlen(h, d, topk, max_ctx, check=True):
+    T = d["q"].shape[0]
+    s = h.cfg
+    out = torch.empty((T, s.n_heads, s.d_v), device=DEV, dtype=torch.float32)
+    lse = torch.empty((T, s.n_heads), device=DEV, dtype=torch.float32)
+    idx = torch.empty((T, topk), device=DEV, dtype=torch.int32)
+    ws = sa.workspace(h, sa.SA_OP_PREFILL_VARLEN, T, max_ctx)
+    sa.sparse_attn_prefill_varlen(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], d["v_pages"], d["kidx_pages"],
+                                  d["block_table"], d["cu"], d["ctx_len"], max_ctx, topk, out, lse, idx, ws)
+    if check:
+        assert sa.sparse_attn_check(h) == 0
+    return out, lse, idx
+
+
+def test_varlen_row_tiles_match_the_oracle():
+    """Six sequences with ragged new-row counts (a full 700-token prefill, tails of 1, 9 and 13 rows, a
+    1-token sequence) on the fused row tiles, k = 512."""
+    ctx, n_new = [3000, 700, 64, 1500, 2049, 1], [1000, 700, 13, 9, 1, 1]
+    say(f"prefill_varlen ctx={ctx} new={n_new} topk=512")
+    wl, d = _varlen(ctx, n_new, 512, seed=31)
+    with sa.Handle(inputs.library_config(wl, max_topk=512)) as h:
+        out, lse, idx = _run_varlen(h, d, 512, max(ctx))
+    cu = np.concatenate([[0], np.cumsum(n_new)])
+    rows = [0, 1, 7, 8, 511, 999, 1000, 1511, 1512, 1699, 1700, 1712, 1713, 1721, 1722, 1723]
+    rows += list(np.random.default_rng(5).integers(0, int(cu[-1]), 16))
+    _check(d, out, lse, idx, rows, 512, 512, "prefill_varlen")
+
+
+def test_varlen_one_sequence_equals_the_chunk_bit_for_bit():
+    """One sequence's last 1000 tokens: the varlen call and the chunk call run the same row tiles."""
+    n, C = 5000, 1000
+    say(f"prefill_varlen vs prefill_chunk: positions {n - C}..{n - 1} of {n}, topk=2048")
+    wl, d = _varlen([n], [C], 2048, seed=32)
+    s = inputs.library_config(wl, max_topk=2048)
+    with sa.Handle(s) as h:
+        out, lse, idx = _run_varlen(h, d, 2048, n)
+        out2 = torch.empty_like(out)
+        lse2 = torch.empty_like(lse)
+        idx2 = torch.empty_like(idx)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL_CHUNK, C, n)
+        sa.sparse_attn_prefill_chunk(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], d["v_pages"], d["kidx_pages"],
+                                     d["block_table"][0], n - C, 2048, out2, lse2, idx2, ws)
+        assert sa.sparse_attn_check(h) == 0
+    assert torch.equal(idx, idx2), "selections differ"
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "outputs differ"
+
+
+def test_varlen_bad_layout_is_flagged():
+    """cu_seqlens that decrease: the device flags SA_DEVERR_ROW, and the rows of no valid sequence
+    get empty selections."""
+    ctx, n_new = [300, 200], [100, 50]
+    say("prefill_varlen with a decreasing cu_seqlens")
+    wl, d = _varlen(ctx, n_new, 64, seed=33)
+    d["cu"] = torch.tensor([0, 120, 100], dtype=torch.int32, device=DEV)  # sequence 1 has -20 rows
+    with sa.Handle(inputs.library_config(wl, max_topk=64)) as h:
+        out, lse, idx = _run_varlen(h, d, 64, max(ctx), check=False)
+        bits = ctypes.c_uint32()
+        st = sa.load_library().sparse_attn_check(h.ptr, torch.cuda.current_stream().cuda_stream, ctypes.byref(bits))
+        assert st == sa.SA_ERR_DEVICE_CHECK
+        assert bits.value & sa.SA_DEVERR_ROW, bits.value
+        assert sa.sparse_attn_check(h) == 0  # cleared
+    gi = to_np(idx)
+    assert np.all(gi[120:] == -1), "rows outside every valid sequence must select nothing"
