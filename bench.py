@@ -573,10 +573,23 @@ def measure_chunk(cfg, P, D, K, args, torch):
             sa.sparse_attn_check(h)
             return e0.elapsed_time(e1) / reps, {k: round(v / reps, 4) for k, (v, c) in kern.items() if c}
 
+        # a varlen batch of the same size: 8 sequences, C / 8 new tokens at the end of each context
+        n_seq = 8
+        per = C // n_seq
+        cu = torch.arange(0, n_seq + 1, dtype=torch.int32, device=dev) * per
+        ws_v = sa.workspace(h, sa.SA_OP_PREFILL_VARLEN, n_seq * per, n)
+
+        def run_varlen():  # the layout known only on the device: fused row tiles per sequence
+            sa.sparse_attn_prefill_varlen(h, P["q"][:n_seq * per], P["q_idx"][:n_seq * per], P["w"][:n_seq * per],
+                                          D["kv_pages"], None, D["kidx_pages"], D["block_table"][:n_seq], cu,
+                                          D["ctx_len"][:n_seq], n, K, out[:n_seq * per], None, idx[:n_seq * per], ws_v)
+
         log(f"[bench] chunked prefill: {C} new tokens at positions {n - C}..{n - 1}")
         ms_c, per_c = timed(run_chunk)
         ms_r, per_r = timed(run_rows)
-        del out, idx, ws, ws_c
+        log(f"[bench] varlen prefill: {n_seq} sequences x {per} new tokens at the end of their contexts")
+        ms_v, per_v = timed(run_varlen)
+        del out, idx, ws, ws_c, ws_v
     torch.cuda.empty_cache()
     pairs = int((pos + 1).sum())
     flops = pairs * 2 * s.n_idx_heads * s.d_idx
@@ -596,6 +609,13 @@ def measure_chunk(cfg, P, D, K, args, torch):
     if per_r.get("indexer"):
         res["per_row_path"]["indexer_roofline"] = roof("indexer_decode_kernel (one row per grid column, all launches)",
                                                        per_r["indexer"])
+    ctx8 = D["ctx_np"][:n_seq].astype(np.int64)
+    vpairs = int(sum((np.arange(c - per, c) + 1).sum() for c in ctx8))
+    vtf = vpairs * 2 * s.n_idx_heads * s.d_idx / (per_v["indexer"] * 1e-3) / 1e12 if per_v.get("indexer") else None
+    res["varlen"] = {"workload": f"{n_seq} sequences x {per} new tokens at the end of their {int(ctx8.max())}-token "
+                                 f"paged contexts (sparse_attn_prefill_varlen)",
+                     "ms": round(ms_v, 4), "tokens_per_s": round(n_seq * per / (ms_v * 1e-3), 1), "kernels_ms": per_v,
+                     "indexer_tflops": round(vtf, 2) if vtf else None}
     return res
 
 
