@@ -109,3 +109,31 @@ def test_two_tier_decode_replays_from_a_graph():
 
         _replays_match(run, [out, idx])
         assert sa.sparse_attn_check(h) == 0
+
+
+def test_varlen_prefill_replays_from_a_graph():
+    """The varlen prefill builds its tile table and row layout on the device, so the captured call replays
+    to the eager result."""
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], topk=512)
+    ctx, n_new = [3000, 700, 64, 1500], [300, 700, 13, 9]
+    say(f"graph capture: sparse_attn_prefill_varlen, ctx={ctx} new={n_new}")
+    rs = np.concatenate([np.full(k, b) for b, k in enumerate(n_new)])
+    rp = np.concatenate([np.arange(c - k, c) for c, k in zip(ctx, n_new)])
+    d = inputs.paged_rows_inputs(wl, ctx, rs, rp, DEV, seed=43)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).to(DEV)
+    ctx_len = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).to(DEV)
+    T = len(rs)
+    with sa.Handle(inputs.library_config(wl, max_topk=512)) as h:
+        s = h.cfg
+        out = torch.empty((T, s.n_heads, s.d_v), device=DEV)
+        lse = torch.empty((T, s.n_heads), device=DEV)
+        idx = torch.empty((T, 512), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL_VARLEN, T, max(ctx))
+
+        def run():
+            sa.sparse_attn_prefill_varlen(h, d["q"], d["q_idx"], d["w"], d["kv_pages"], d["v_pages"],
+                                          d["kidx_pages"], d["block_table"], cu, ctx_len, max(ctx), 512, out, lse,
+                                          idx, ws)
+
+        _replays_match(run, [out, lse, idx])
+        assert sa.sparse_attn_check(h) == 0
