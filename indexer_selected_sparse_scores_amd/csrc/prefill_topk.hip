@@ -362,6 +362,8 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 }
                 finish_window(p, 0.f, (uint32_t)n_kt * kKT + lane);
             }
+        } else if constexpr (kBlockKeys) {
+            __syncthreads();  // no barrier followed the read of sh.tile: keep it until every thread has read it
         }
         if constexpr (kBlockKeys) continue;  // no selection in this pass
         // final threshold per row (each wave its own row), then free the histograms
