@@ -233,6 +233,23 @@ sa_status_t sparse_attn_decode_blocks(sa_handle_t h, const void *q, const void *
                                       int32_t max_ctx, int32_t block_size, int32_t n_blocks, float *out,
                                       float *lse, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream);
 
+/* sparse_attn_decode for callers that cannot allocate device memory or size a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * device-side checks as sparse_attn_decode, without ws / ws_bytes: its scratch (scores, histograms,
+ * indices, split-attention partials) is a device array of 64 MiB that the library holds on every device
+ * it runs on until the process ends; its address is looked up once per device in sparse_attn_create.
+ * The call allocates nothing and calls no allocating routine.  All calls on one device share that array
+ * and each leaves it holding its own state: calls that overlap on one device (several streams or host
+ * threads at once) race and give undefined results; serialise them.
+ * Errors: those of sparse_attn_decode; SA_ERR_UNSUPPORTED when the step needs more than the array holds
+ * (sparse_attn_workspace_size(SA_OP_DECODE, B, max_ctx) > 64 MiB; B = 64 at max_ctx = 131072 with
+ * max_topk = 2048 needs about 44 MB). */
+sa_status_t sparse_attn_decode_noalloc(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                       const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                       int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                       const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                                       float *out, float *lse, int32_t *idx_out, void *stream);
+
 /* Query rows against paged caches: chunked prefill (new tokens of a sequence whose earlier tokens
  * are already cached), varlen batches of several sequences, and several new tokens per sequence in
  * one decode step.  Query row t is the token at position p = row_pos[t] of sequence

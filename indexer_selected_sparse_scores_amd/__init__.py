@@ -35,7 +35,7 @@ SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK,
 EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error",
             "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
             "topk_select_blocks", "sparse_attn_prefill", "sparse_attn_prefill_blocks", "sparse_attn_decode",
-            "sparse_attn_decode_blocks", "sparse_attn_prefill_paged", "sparse_attn_prefill_chunk", "sparse_attn_prefill_varlen",
+            "sparse_attn_decode_blocks", "sparse_attn_decode_noalloc", "sparse_attn_prefill_paged", "sparse_attn_prefill_chunk", "sparse_attn_prefill_varlen",
             "indexer_project_q",
             "indexer_project_k",
             "acceptance_rate", "acceptance_bin_stats",
@@ -105,6 +105,7 @@ def load_library() -> ctypes.CDLL:
         "sparse_attn_decode": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, P, P, P, P, sz, P], st),
         "sparse_attn_decode_blocks": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, i32, i32, P, P, P, P, sz,
                                        P], st),
+        "sparse_attn_decode_noalloc": ([P, P, P, P, P, P, P, i64, P, i32, P, P, i32, i32, P, P, P, P], st),
         "sparse_attn_prefill_paged": ([P, P, P, P, P, P, P, i64, P, i32, i32, P, P, i64, i32, i32, P, P, P, P, sz,
                                        P], st),
         "sparse_attn_prefill_chunk": ([P, P, P, P, P, P, P, i64, P, i32, i64, i64, i32, P, P, P, P, sz, P], st),
@@ -272,6 +273,18 @@ def sparse_attn_decode(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, bl
         h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
         _ptr(block_table), max_blocks, _ptr(ctx_len), _ptr(topk), B, int(max_ctx), _ptr(out), _ptr(lse),
         _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_decode_noalloc(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, ctx_len,
+                               topk, max_ctx: int, out, lse=None, idx_out=None, stream=None) -> None:
+    """sparse_attn_decode on the library's own device array instead of a workspace (nothing allocated)."""
+    B = q.shape[0]
+    n_pages = kv_pages.shape[0]
+    max_blocks = block_table.shape[1]
+    _check(h.ptr, load_library().sparse_attn_decode_noalloc(
+        h.ptr, _ptr(q), _ptr(q_idx), _ptr(w), _ptr(kv_pages), _ptr(v_pages), _ptr(kidx_pages), n_pages,
+        _ptr(block_table), max_blocks, _ptr(ctx_len), _ptr(topk), B, int(max_ctx), _ptr(out), _ptr(lse),
+        _ptr(idx_out), _stream(stream)))
 
 
 def sparse_attn_prefill_paged(h: Handle, q, q_idx, w, kv_pages, v_pages, kidx_pages, block_table, row_seq, row_pos,

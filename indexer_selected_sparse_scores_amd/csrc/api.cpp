@@ -7,14 +7,28 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 
 #include "sa_internal.hpp"
 
+// Device memory of sparse_attn_decode_noalloc, the decode step for callers that cannot allocate: one
+// array per device, used in place of a caller workspace.  Host code never passes the array's name (on
+// the host it is only a stand-in): it uses the address hipGetSymbolAddress returns on each device, looked
+// up once per device when the first handle is created there and kept in g_scratch.  The array sits at
+// file scope, outside any unnamed namespace: there its device symbol would be local to the code object,
+// and the runtime could not find it by the name the host side registers.
+static __device__ __align__(256) unsigned char scratch[size_t(64) << 20];
+
 namespace {
 
 thread_local std::string g_create_error;
+
+constexpr size_t kNoAllocBytes = sizeof(scratch);
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
 
 constexpr int64_t kMaxIndexerScoresL = 16384;
 constexpr int32_t kMaxTopk = 8192;
@@ -361,6 +375,23 @@ sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
         delete h;
         return fail(nullptr, SA_ERR_HIP, "hipGetDevice failed (no HIP device?)");
     }
+    if (h->device < 0 || h->device >= kMaxDevices) {
+        delete h;
+        return fail(nullptr, SA_ERR_UNSUPPORTED, "device ordinal %d beyond the library's %d", h->device, kMaxDevices);
+    }
+    {
+        // the allocation-free decode's array on this device (the current one): its address, once
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch[h->device]) {
+            void *ptr = nullptr;
+            const hipError_t es = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (es != hipSuccess || !ptr) {
+                delete h;
+                return fail(nullptr, SA_ERR_HIP, "looking up the device scratch array: %s", hipGetErrorString(es));
+            }
+            g_scratch[h->device] = ptr;
+        }
+    }
     hipError_t e = hipMalloc(reinterpret_cast<void **>(&h->d_err), sizeof(uint32_t));
     if (e == hipSuccess) e = hipMemset(h->d_err, 0, sizeof(uint32_t));
     if (e != hipSuccess) {
@@ -578,6 +609,27 @@ sa_status_t sparse_attn_decode_blocks(sa_handle_t h, const void *q, const void *
     const BlockSelect b{block_size, n_blocks};
     return decode_impl(h, q, q_idx, w, kv_pages, v_pages, kidx_pages, n_pages, block_table, max_blocks, ctx_len,
                        topk, B, max_ctx, &b, out, lse, idx_out, ws, ws_bytes, stream);
+}
+
+sa_status_t sparse_attn_decode_noalloc(sa_handle_t h, const void *q, const void *q_idx, const float *w,
+                                       const void *kv_pages, const void *v_pages, const void *kidx_pages,
+                                       int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
+                                       const int32_t *ctx_len, const int32_t *topk, int32_t B, int32_t max_ctx,
+                                       float *out, float *lse, int32_t *idx_out, void *stream)
+{
+    if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    h->last_error.clear();
+    if (B < 1 || B > 65535) return fail(h, SA_ERR_INVALID_ARG, "B must be in [1, 65535]");
+    if (max_ctx < 1) return fail(h, SA_ERR_INVALID_ARG, "max_ctx must be >= 1");
+    const size_t need = decode_layout(*h, B, max_ctx).total;
+    if (need > kNoAllocBytes)
+        return fail(h, SA_ERR_UNSUPPORTED,
+                    "the allocation-free decode holds %zu bytes of device scratch; B = %d, max_ctx = %d, max_topk = %d "
+                    "need %zu (use sparse_attn_decode with a workspace)",
+                    kNoAllocBytes, B, max_ctx, h->cfg.max_topk, need);
+    void *ptr = g_scratch[h->device];  // set when the handle was created on this device
+    return decode_impl(h, q, q_idx, w, kv_pages, v_pages, kidx_pages, n_pages, block_table, max_blocks, ctx_len,
+                       topk, B, max_ctx, nullptr, out, lse, idx_out, ptr, kNoAllocBytes, stream);
 }
 
 }  // extern "C"

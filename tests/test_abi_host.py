@@ -78,6 +78,8 @@ def test_create_null_arguments():
                                          None) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_prefill_varlen(None, *([None] * 6), 1, None, 1, 1, None, None, 1, 1, 1, None, None, None,
                                           None, 0, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sparse_attn_decode_noalloc(None, *([None] * 6), 1, None, 1, None, None, 1, 1, None, None, None,
+                                          None) == sa.SA_ERR_INVALID_ARG
     size = ctypes.c_size_t()
     assert lib.sparse_attn_workspace_size(None, 1, 1, 1, ctypes.byref(size)) == sa.SA_ERR_INVALID_ARG
     assert lib.sparse_attn_last_error(None)
