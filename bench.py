@@ -59,8 +59,9 @@ def parse():
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked-prefill (paged query rows) measurement")
     ap.add_argument("--no-acceptance", action="store_true", help="skip the acceptance-rate measurement")
     ap.add_argument("--no-rl-sweep", action="store_true", help="skip the RL-rollout decode sweep")
-    ap.add_argument("--flush-reps", type=int, default=20,
-                    help="cold-cache timing: reps of each call with a 512 MiB write before each (0 skips)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the decode step replayed from a HIP graph")
+    ap.add_argument("--no-c1", action="store_true", help="skip the 8192-token prefill workload")
+    ap.add_argument("--no-c2", action="store_true", help="skip the ragged decode workload (contexts 16K..64K)")
     ap.add_argument("--main-only", action="store_true",
                     help="time the step alone (no projections, two-tier, chunked-prefill or acceptance legs)")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -156,7 +157,7 @@ def main():
         return
     if args.main_only:
         args.no_projections = args.no_two_tier = args.no_chunk = args.no_acceptance = args.no_rl_sweep = True
-        args.flush_reps = 0
+        args.no_graph = args.no_c1 = args.no_c2 = True
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -222,31 +223,56 @@ def main():
     torch.cuda.synchronize()
     del cal_src, cal_dst
 
-    peaks = None if args.no_peaks else measured_peaks(torch)
+    peaks = None if args.no_peaks else measured_peaks(h_pre, torch)
 
+    # K timed steps, each after a 512 MiB write that evicts the L2 and Infinity Cache (the write is outside
+    # the timed span): per-step prefill and decode times from events on the stream, and per-kernel times of
+    # the step from the events the library records around each launch.  Medians over the K steps.
     profile = not args.no_profile
-    if profile:
-        sa.sparse_attn_profile(h_pre, True)
-        sa.sparse_attn_profile(h_dec, True)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    step_kern = []
+    log(f"[bench] timing {args.steps} steps (each after a {FLUSH_BYTES >> 20} MiB cache flush)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush_buf.fill_(i & 0xFF)
+        if profile:
+            sa.sparse_attn_profile(h_pre, True)
+            sa.sparse_attn_profile(h_dec, True)
         ev[3 * i].record()
         prefill()
         ev[3 * i + 1].record()
         decode()
         ev[3 * i + 2].record()
+        if profile:
+            step_kern.append((sa.sparse_attn_profile_read(h_pre), sa.sparse_attn_profile_read(h_dec)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)) / args.steps
-    dec_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)) / args.steps
-    kern_pre = sa.sparse_attn_profile_read(h_pre) if profile else {}
-    kern_dec = sa.sparse_attn_profile_read(h_dec) if profile else {}
+    if profile:
+        sa.sparse_attn_profile(h_pre, False)
+        sa.sparse_attn_profile(h_dec, False)
+    pre_steps = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)]
+    dec_steps = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)]
+    pre_ms, dec_ms = median(pre_steps), median(dec_steps)
+    step_ms = median([a + b for a, b in zip(pre_steps, dec_steps)])
     sa.sparse_attn_check(h_pre)
     sa.sparse_attn_check(h_dec)
-    log(f"[bench] prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms per step (wall {wall:.2f} s)")
+    log(f"[bench] cold-step medians: prefill {pre_ms:.3f} ms, decode {dec_ms:.4f} ms (wall {wall:.2f} s)")
+
+    # the same steps back to back, without flushes (warm caches), for comparison
+    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev_w[0].record()
+    for _ in range(args.steps):
+        prefill()
+    ev_w[1].record()
+    for _ in range(args.steps):
+        decode()
+    ev_w[2].record()
+    torch.cuda.synchronize()
+    warm = {"prefill_ms_mean": round(ev_w[0].elapsed_time(ev_w[1]) / args.steps, 4),
+            "decode_ms_mean": round(ev_w[1].elapsed_time(ev_w[2]) / args.steps, 4)}
+    del flush_buf
 
     # algorithmic work (per step)
     pairs = L * (L + 1) // 2
@@ -259,70 +285,47 @@ def main():
     row_bytes = s.d_qk * 2
     dec_gather_bytes = sel_rows * row_bytes
 
-    def per_launch(kern, kind):
-        ms, n = kern.get(kind, (0.0, 0))
-        return (ms / n, n, ms) if n else (None, 0, 0.0)
-
     kernels = {}
     roofline = roofline_dec_idx = roofline_dec_attn = None
     if profile:
-        for name, kern in (("prefill", kern_pre), ("decode", kern_dec)):
+        kern_med = {}
+        for j, name in enumerate(("prefill", "decode")):
             for kind in sa.KERNEL_KINDS:
-                avg, n, tot = per_launch(kern, kind)
-                if n:
-                    kernels[f"{name}.{kind}"] = {"launches_per_step": n / args.steps,
-                                                 "avg_ms": round(avg, 5),
-                                                 "ms_per_step": round(tot / args.steps, 4)}
-        avg, n, tot = per_launch(kern_pre, "indexer")
-        if n:
-            tflops = idx_flops / (avg * 1e-3) / 1e12
-            roofline = {"kernel": "indexer_topk_prefill_kernel", "bound": "mfma",
-                        "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                        "traffic": stored_traffic("indexer_topk_prefill_kernel"),
-                        "algorithmic_per_launch": f"{idx_flops:.4g} flop = {pairs} causal (t,s) pairs x "
-                                                  f"{flop_per_pair} flop (2 H_I d_I)"}
-        avg, n, tot = per_launch(kern_dec, "indexer")
-        if n:
-            gbs = dec_idx_bytes / (avg * 1e-3) / 1e9
-            roofline_dec_idx = {"kernel": "indexer_decode_kernel", "bound": "hbm",
-                                "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": stored_traffic("indexer_decode_kernel"),
-                                "algorithmic_per_launch": f"{dec_idx_bytes} B = {ctx_total} cached tokens x "
-                                                          f"{key_bytes} B of index key"}
-        avg, n, tot = per_launch(kern_dec, "attention")
-        if n:
-            gbs = dec_gather_bytes / (avg * 1e-3) / 1e9
-            roofline_dec_attn = {"kernel": "attn_decode_lds_kernel (paged decode gather)",
-                                 "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                 "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                 "traffic": stored_traffic("attn_decode_lds_kernel"),
-                                 "algorithmic_per_launch": f"{dec_gather_bytes} B = {sel_rows} selected rows x "
-                                                           f"{row_bytes} B latent row"}
+                per_step = [k[j].get(kind, (0.0, 0)) for k in step_kern]
+                if per_step and per_step[0][1]:
+                    kern_med[(name, kind)] = median([ms for ms, _ in per_step])
+                    kernels[f"{name}.{kind}"] = {"launches_per_step": per_step[0][1],
+                                                 "ms_per_step_median": round(kern_med[(name, kind)], 5)}
+        launches = lambda name, kind: kernels[f"{name}.{kind}"]["launches_per_step"]
+        if ("prefill", "indexer") in kern_med:
+            ms = kern_med[("prefill", "indexer")] / launches("prefill", "indexer")
+            roofline = mfma_roofline("indexer_topk_prefill_kernel", idx_flops, ms,
+                                     f"{idx_flops:.4g} flop = {pairs} causal (t,s) pairs x {flop_per_pair} flop "
+                                     f"(2 H_I d_I)", peaks)
+            roofline["traffic"] = stored_traffic("indexer_topk_prefill_kernel")
+        if ("decode", "indexer") in kern_med:
+            ms = kern_med[("decode", "indexer")] / launches("decode", "indexer")
+            roofline_dec_idx = hbm_roofline("indexer_decode_kernel", dec_idx_bytes, ms,
+                                            f"{dec_idx_bytes} B = {ctx_total} cached tokens x {key_bytes} B of "
+                                            f"index key", peaks)
+            roofline_dec_idx["traffic"] = stored_traffic("indexer_decode_kernel")
+        if ("decode", "attention") in kern_med:
+            ms = kern_med[("decode", "attention")] / launches("decode", "attention")
+            roofline_dec_attn = hbm_roofline("attn_decode_lds_kernel (paged decode gather)", dec_gather_bytes, ms,
+                                             f"{dec_gather_bytes} B = {sel_rows} selected rows x {row_bytes} B "
+                                             f"latent row", peaks)
+            roofline_dec_attn["traffic"] = stored_traffic("attn_decode_lds_kernel")
+        # the whole decode step against HBM: index keys + selected rows over the step's median time
+        dec_all = dec_idx_bytes + dec_gather_bytes
+        decode_step_roofline = hbm_roofline("whole decode step (reset, paged indexer, top-k, gather, merge)", dec_all,
+                                            dec_ms, f"{dec_all} B = index keys of every cached token + the "
+                                                    f"selected latent rows", peaks)
+    else:
+        decode_step_roofline = None
 
-    # the same achieved rates against the peaks measured on this machine (bf16 GEMM, 4 GiB copy)
-    if peaks:
-        for rf, key in ((roofline, "bf16_gemm_8192_tflops"), (roofline_dec_idx, "gemv_4GiB_read_gbs"),
-                        (roofline_dec_attn, "gemv_4GiB_read_gbs")):
-            if rf and peaks.get(key):
-                rf["frac_of_measured"] = round(rf["achieved"] / peaks[key], 4)
-                rf["measured_peak"] = key
-
-    if profile:
-        sa.sparse_attn_profile(h_pre, False)
-        sa.sparse_attn_profile(h_dec, False)
-    flushed = None
-    if args.flush_reps > 0:
-        flushed = {"reps": args.flush_reps, "flush_bytes": FLUSH_BYTES,
-                   "prefill_ms_median": round(cold_median(prefill, args.flush_reps, torch), 4),
-                   "decode_ms_median": round(cold_median(decode, args.flush_reps, torch), 4)}
-        flushed["prefill_tokens_per_s"] = round(L / (flushed["prefill_ms_median"] * 1e-3), 1)
-        flushed["decode_tokens_per_s"] = round(B / (flushed["decode_ms_median"] * 1e-3), 1)
-        sa.sparse_attn_check(h_pre)
-        sa.sparse_attn_check(h_dec)
-        log(f"[bench] cold-cache medians: prefill {flushed['prefill_ms_median']:.3f} ms, "
-            f"decode {flushed['decode_ms_median']:.4f} ms")
+    graph = None if args.no_graph else measure_decode_graph(decode, args.steps, torch)
+    c1 = None if args.no_c1 else measure_prefill_8k(cfg, args, peaks, torch)
+    c2 = None if args.no_c2 else measure_decode_ragged(cfg, args, peaks, torch)
 
     projections = None if args.no_projections else measure_projections(h_pre, P, L, args.steps, torch)
     two_tier = None if args.no_two_tier else measure_two_tier(cfg, P, D, L, K, args, torch)
@@ -342,7 +345,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(pre_ms + dec_ms, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -351,7 +354,8 @@ def main():
         "config": {"workload": f"prefill L={L} (prefill_128k) + paged decode B={B} at ctx={N} "
                                f"(decode_b64_128k)", "topk": K,
                    "index_heads": s.n_idx_heads, "d_index": s.d_idx, "heads": s.n_heads,
-                   "d_qk": s.d_qk, "d_v": s.d_v, "page_size": s.page_size},
+                   "d_qk": s.d_qk, "d_v": s.d_v, "page_size": s.page_size,
+                   "timing": f"median over {args.steps} steps, each after a {FLUSH_BYTES >> 20} MiB cache flush"},
         "prefill_tokens_per_s": round(L / (pre_ms * 1e-3), 1),
         "decode_tokens_per_s": round(B / (dec_ms * 1e-3), 1),
         "prefill_ms": round(pre_ms, 4),
@@ -359,8 +363,12 @@ def main():
         "roofline": roofline,
         "roofline_decode_indexer": roofline_dec_idx,
         "roofline_decode_gather": roofline_dec_attn,
+        "roofline_decode_step": decode_step_roofline,
         "kernels": kernels,
-        "cold_cache": flushed,
+        "warm_cache": warm,
+        "decode_graph": graph,
+        "prefill_8k": c1,
+        "decode_ragged": c2,
         "peaks_measured": peaks,
         "projections": projections,
         "two_tier": two_tier,
@@ -375,23 +383,173 @@ def main():
     h_dec.close()
 
 
-FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB Infinity Cache
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
-def cold_median(fn, reps, torch):
-    """Median over `reps` calls of fn, each timed alone with events on the current stream after a
-    512 MiB write has evicted the L2 and Infinity Cache (the write itself is outside the timed span)."""
+def mfma_roofline(kernel, flops, ms, what, peaks):
+    tf = flops / (ms * 1e-3) / 1e12
+    rf = {"kernel": kernel, "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(ms, 5), "algorithmic_per_launch": what}
+    if peaks and peaks.get("mfma_loop_tflops"):
+        rf["frac_of_measured"] = round(tf / peaks["mfma_loop_tflops"], 4)
+        rf["measured_peak"] = "mfma_loop_tflops"
+    return rf
+
+
+def hbm_roofline(kernel, nbytes, ms, what, peaks):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rf = {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 5), "algorithmic_per_launch": what}
+    if peaks and peaks.get("stream_read_gbs"):
+        rf["frac_of_measured"] = round(gbs / peaks["stream_read_gbs"], 4)
+        rf["measured_peak"] = "stream_read_gbs"
+    return rf
+
+
+def cold_runs(fn, reps, torch, profile_handle=None):
+    """fn timed `reps` times, each alone after a 512 MiB write that evicts the L2 and Infinity Cache (the write
+    is outside the timed span); returns the per-call times and, with a handle, its per-kernel times per call."""
+    import indexer_selected_sparse_scores_amd as sa
     buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i, (e0, e1) in enumerate(ev):
+    times, kerns = [], []
+    for i in range(reps):
         buf.fill_(i & 0xFF)
+        if profile_handle is not None:
+            sa.sparse_attn_profile(profile_handle, True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
         e1.record()
-    torch.cuda.synchronize()
-    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        if profile_handle is not None:
+            kerns.append(sa.sparse_attn_profile_read(profile_handle))
+    if profile_handle is not None:
+        sa.sparse_attn_profile(profile_handle, False)
     del buf
-    return ms[reps // 2] if reps % 2 else 0.5 * (ms[reps // 2 - 1] + ms[reps // 2])
+    return times, kerns
+
+
+def kernel_medians(kerns):
+    """{kind: median ms per call} over calls (each call's summed launches of that kind)."""
+    out = {}
+    for kind in (kerns[0] if kerns else {}):
+        if kerns[0][kind][1]:
+            out[kind] = median([k[kind][0] for k in kerns])
+    return out
+
+
+def measure_decode_graph(decode, reps, torch):
+    """The benchmark's decode step captured once in a HIP graph and replayed (not part of `value`): the same
+    kernels without the per-launch host work between them; median of cold replays."""
+    log("[bench] decode step replayed from a HIP graph")
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        decode()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        decode()
+    g.replay()
+    torch.cuda.synchronize()
+    times, _ = cold_runs(g.replay, max(reps, 5), torch)
+    del g
+    return {"ms_median": round(median(times), 4), "reps": len(times),
+            "note": "one replay per timed call, each after a 512 MiB cache flush"}
+
+
+def measure_prefill_8k(cfg, args, peaks, torch):
+    """The 8192-token prefill workload (prefill_8k: one sequence, k = 2048; not part of `value`), cold median
+    over the steps, with the roofline of the fused indexer."""
+    import indexer_selected_sparse_scores_amd as sa
+    from indexer_selected_sparse_scores_amd import inputs
+    wl = inputs.WORKLOADS["prefill_8k"]
+    L, K = wl.L, wl.topk
+    log(f"[bench] prefill_8k L={L}")
+    P8 = inputs.prefill_inputs(wl, "cuda")
+    s = cfg
+    with sa.Handle(inputs.library_config(wl, max_topk=K)) as h:
+        out = torch.empty((L, s.n_heads, s.d_v), device="cuda")
+        idx = torch.empty((L, K), device="cuda", dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL, L)
+        run = lambda: sa.sparse_attn_prefill(h, P8["q"], P8["k"], None, P8["q_idx"], P8["w"], P8["k_idx"], K, out,
+                                             None, idx, ws)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        times, kerns = cold_runs(run, max(args.steps, 5), torch, h)
+        sa.sparse_attn_check(h)
+        km = kernel_medians(kerns)
+        del out, idx, ws
+    del P8
+    torch.cuda.empty_cache()
+    pairs = L * (L + 1) // 2
+    flops = pairs * 2 * s.n_idx_heads * s.d_idx
+    ms = median(times)
+    res = {"workload": f"prefill_8k: one sequence, L={L}, top-{K}", "ms_median": round(ms, 4),
+           "tokens_per_s": round(L / (ms * 1e-3), 1), "kernels_ms_median": {k: round(v, 5) for k, v in km.items()}}
+    if km.get("indexer"):
+        res["roofline"] = mfma_roofline("indexer_topk_prefill_kernel", flops, km["indexer"],
+                                        f"{flops:.4g} flop = {pairs} causal pairs x {2 * s.n_idx_heads * s.d_idx} flop",
+                                        peaks)
+    return res
+
+
+def measure_decode_ragged(cfg, args, peaks, torch):
+    """The ragged decode workload (decode_b64: 64 sequences, contexts uniform in [16K, 64K], k = 2048; not part of
+    `value`), cold median over the steps, with the rooflines of the decode indexer, the gather and the step."""
+    import numpy as np
+
+    import indexer_selected_sparse_scores_amd as sa
+    from indexer_selected_sparse_scores_amd import inputs
+    wl = inputs.WORKLOADS["decode_b64"]
+    log("[bench] decode_b64: B=64, contexts uniform in [16384, 65536]")
+    D2 = inputs.decode_inputs(wl, "cuda")
+    B, K = D2["q"].shape[0], wl.topk
+    s = cfg
+    with sa.Handle(inputs.library_config(wl, max_topk=K)) as h:
+        out = torch.empty((B, s.n_heads, s.d_v), device="cuda")
+        idx = torch.empty((B, K), device="cuda", dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_DECODE, B, D2["max_ctx"])
+        run = lambda: sa.sparse_attn_decode(h, D2["q"], D2["q_idx"], D2["w"], D2["kv_pages"], None, D2["kidx_pages"],
+                                            D2["block_table"], D2["ctx_len"], D2["topk"], D2["max_ctx"], out, None,
+                                            idx, ws)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        sa.sparse_attn_check(h)
+        times, kerns = cold_runs(run, max(args.steps, 9), torch, h)
+        sa.sparse_attn_check(h)
+        km = kernel_medians(kerns)
+        del out, idx, ws
+    ctx = D2["ctx_np"].astype(np.int64)
+    del D2
+    torch.cuda.empty_cache()
+    idx_bytes = int(ctx.sum()) * s.d_idx * 2
+    gather_bytes = int(np.minimum(ctx, K).sum()) * s.d_qk * 2
+    ms = median(times)
+    res = {"workload": f"decode_b64: {B} sequences, contexts {int(ctx.min())}..{int(ctx.max())} (uniform in "
+                       f"[16384, 65536]), top-{K}, paged 64-token blocks", "ms_median": round(ms, 4),
+           "tokens_per_s": round(B / (ms * 1e-3), 1), "kernels_ms_median": {k: round(v, 5) for k, v in km.items()},
+           "roofline_step": hbm_roofline("whole decode step", idx_bytes + gather_bytes, ms,
+                                         f"{idx_bytes + gather_bytes} B = index keys of every cached token + the "
+                                         f"selected latent rows", peaks)}
+    if km.get("indexer"):
+        res["roofline_indexer"] = hbm_roofline("indexer_decode_kernel", idx_bytes, km["indexer"],
+                                               f"{idx_bytes} B of index keys", peaks)
+    if km.get("attention"):
+        res["roofline_gather"] = hbm_roofline("attn_decode_lds_kernel", gather_bytes, km["attention"],
+                                              f"{gather_bytes} B of selected latent rows", peaks)
+    return res
+
+
+FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB Infinity Cache
 
 
 def measure_projections(h, P, L, steps, torch):
@@ -733,48 +891,67 @@ def measure_acceptance(cfg, args, torch, T=4096, V=151936):
     return res
 
 
-def measured_peaks(torch):
-    """The chip's attainable rates on this machine, as references beside the spec peaks: a large
-    bf16 GEMM (hipBLASLt through torch), a 4 GiB device-to-device copy and a read-bound bf16
-    matrix-vector product over a 4 GiB matrix."""
-    n = 8192
-    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
-    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
-    for _ in range(3):
-        torch.matmul(a, b)
+def measured_peaks(h, torch):
+    """Rates measured on this machine, references beside the spec peaks: the library's bf16 MFMA loop on random
+    operands (the fused indexer's instruction and occupancy; with the shader clock it ran at, from the
+    s_memtime / s_memrealtime counters it reads), its streaming read and copy kernels over 4 GiB, and for
+    context a large bf16 GEMM (hipBLASLt through torch)."""
+    import indexer_selected_sparse_scores_amd as sa
+    dev = "cuda"
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device=dev).manual_seed(20261202)
+    operands = torch.randn(1 << 19, generator=g, device=dev).to(torch.bfloat16)  # 1 MiB of random bf16
+    clocks = torch.zeros(256, dtype=torch.int64, device=dev)
+    sink = torch.zeros(1, device=dev)
+    iters = 40000                      # about 20 ms per launch; 6 launches ~ the fused indexer's 0.1 s
+    flop_per_launch = n_cu * 8 * iters * 8 * 32768
+    for _ in range(2):
+        sa.sparse_attn_peak_mfma(h, operands, iters, clocks, sink)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
+    reps = 6
     e0.record()
     for _ in range(reps):
-        torch.matmul(a, b)
+        sa.sparse_attn_peak_mfma(h, operands, iters, clocks, sink)
     e1.record()
     torch.cuda.synchronize()
-    gemm_tflops = 2 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
-    del a, b
-    src = torch.empty(1 << 32, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0.record()
-    for _ in range(3):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    mfma_ms = e0.elapsed_time(e1) / reps
+    mfma_tflops = flop_per_launch / (mfma_ms * 1e-3) / 1e12
+    c = clocks.view(-1, 4).cpu().numpy()[:min(n_cu, 64)].astype("float64")
+    ghz = sorted(((c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6) / 1e9).tolist())  # s_memrealtime: 100 MHz
+    clock_ghz = ghz[len(ghz) // 2]
+    del operands, clocks
+    nbytes = 1 << 32
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+
+    def timed(fn, n=5):
+        fn()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    read_ms = timed(lambda: sa.sparse_attn_peak_stream(h, src, None, nbytes, sink))
+    copy_ms = timed(lambda: sa.sparse_attn_peak_stream(h, src[:nbytes // 2], dst, nbytes // 2))
+    sa.sparse_attn_check(h)
     del src, dst
-    # a read-bound pass: a bf16 matrix-vector product over a 4 GiB matrix (rocBLAS through torch)
-    mat = torch.randn((65536, 32768), dtype=torch.bfloat16, device="cuda")
-    vec = torch.randn((32768,), dtype=torch.bfloat16, device="cuda")
-    torch.mv(mat, vec)
-    e0.record()
-    for _ in range(3):
-        torch.mv(mat, vec)
-    e1.record()
-    torch.cuda.synchronize()
-    read_gbs = mat.numel() * 2 * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del mat, vec
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    gemm_ms = timed(lambda: torch.matmul(a, b), 10)
+    del a, b
     torch.cuda.empty_cache()
-    return {"bf16_gemm_8192_tflops": round(gemm_tflops, 1), "copy_4GiB_read_plus_write_gbs": round(copy_gbs, 1),
-            "gemv_4GiB_read_gbs": round(read_gbs, 1)}
+    return {"mfma_loop_tflops": round(mfma_tflops, 1), "mfma_loop_clock_ghz": round(clock_ghz, 3),
+            "mfma_loop": f"{n_cu} workgroups x 8 waves, v_mfma_f32_32x32x16_bf16 on eight random bf16 fragment "
+                         f"pairs per wave, {reps} launches of {mfma_ms:.2f} ms; clock = median over workgroups of "
+                         f"shader cycles / (reference ticks / 100 MHz)",
+            "stream_read_gbs": round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+            "stream_copy_read_plus_write_gbs": round(nbytes / (copy_ms * 1e-3) / 1e9, 1),
+            "stream": "4 GiB read once (16-byte non-temporal loads), and 2 GiB copied, by the library's stream kernel",
+            "bf16_gemm_8192_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
 
 
 def cpu_baseline(P, wl, K, seconds):
@@ -811,6 +988,13 @@ def cpu_baseline(P, wl, K, seconds):
     t0 = run(n0)
     n = int(min(4096, max(n0, n0 * seconds / max(t0, 1e-3))))
     t = run(n)
+    # the same oracle on one thread, on a smaller sample of the same rows' distribution
+    oracle.set_num_threads(1)
+    try:
+        n1 = max(1, int(n * (seconds / 3) / max(t, 1e-3) / threads))
+        t1 = run(n1)
+    finally:
+        oracle.set_num_threads(threads)
     cpu_model = None
     try:
         with open("/proc/cpuinfo") as fh:
@@ -819,7 +1003,9 @@ def cpu_baseline(P, wl, K, seconds):
         pass
     return {"value": round(n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model,
             "sample": f"{n} uniformly drawn query rows of the L={L} prefill (indexer over all "
-                      f"preceding keys, top-{K}, attention), {t:.1f} s on {threads} threads"}
+                      f"preceding keys, top-{K}, attention), {t:.1f} s on {threads} threads",
+            "one_thread": {"value": round(n1 / t1, 4), "unit": "tokens/s", "cores": 1,
+                           "sample": f"{n1} uniformly drawn query rows, {t1:.1f} s on 1 thread"}}
 
 
 def cpu_baseline_decode(D, wl, K, seconds):
@@ -865,9 +1051,16 @@ def cpu_baseline_decode(D, wl, K, seconds):
     n = int(min(B, 16, max(1, seconds / max(t1, 1e-3))))  # at most 16 sequences' pages on the host
     seqs = list(range(1, 1 + n)) if n < B else list(range(B))
     t = run(seqs)
+    oracle.set_num_threads(1)
+    try:
+        t1 = run([0])
+    finally:
+        oracle.set_num_threads(threads)
     return {"value": round(len(seqs) / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(seqs)} of the B={B} sequences of the decode step at ctx={int(D['ctx_np'].max())} "
-                      f"(indexer over every cached token, top-{K}, attention), {t:.1f} s on {threads} threads"}
+                      f"(indexer over every cached token, top-{K}, attention), {t:.1f} s on {threads} threads",
+            "one_thread": {"value": round(1 / t1, 4), "unit": "tokens/s", "cores": 1,
+                           "sample": f"sequence 0 of the step, {t1:.1f} s on 1 thread"}}
 
 
 if __name__ == "__main__":

@@ -99,6 +99,14 @@ typedef struct {
  * and picks kernels.  Returns SA_ERR_INVALID_ARG for an inconsistent config. */
 sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out);
 
+/* A handle for host-side planning, on a machine with or without a GPU: the same configuration checks as
+ * sparse_attn_create, workspace sizes for a device of n_cu compute units (1 .. 65535; the fused prefill's
+ * candidate lists scale with it), and every call's host-side validation -- but no device is touched:
+ * a call whose arguments pass validation returns SA_ERR_UNSUPPORTED instead of launching (and so does
+ * sparse_attn_check).  For schedulers that size workspaces ahead of time, and for testing the argument
+ * checks where no GPU is present.  Release it with sparse_attn_destroy. */
+sa_status_t sparse_attn_create_host(const sa_config_t *cfg, int32_t n_cu, sa_handle_t *out);
+
 /* Release a handle (synchronises the device before freeing the error word). */
 void sparse_attn_destroy(sa_handle_t h);
 
@@ -401,6 +409,29 @@ sa_status_t acceptance_bin_stats(sa_handle_t h, const float *alpha, const int32_
 #define SA_KERNEL_COUNT     6
 sa_status_t sparse_attn_profile(sa_handle_t h, int enable);
 sa_status_t sparse_attn_profile_read(sa_handle_t h, double *total_ms, int64_t *launches);
+
+/* Device peaks measured on the box -- the denominators a benchmark reports beside the published ones.
+ * Measurement aids only: nothing of the method runs in them.
+ *
+ * sparse_attn_peak_mfma: one workgroup of eight waves per compute unit (two per SIMD, the fused prefill
+ * indexer's occupancy) runs `iters` iterations of eight v_mfma_f32_32x32x16_bf16 each (32768 flop per
+ * MFMA, four independent fp32 accumulators), every MFMA on a different pair of A / B fragments taken from
+ * `operands` (caller-filled random bf16, at least 1 MiB, 16-byte aligned), so the multipliers switch as
+ * on real data.  Flop per launch = n_cu * 8 waves * iters * 8 * 32768.  clocks [256] uint64 (device):
+ * for workgroups 0 .. min(n_cu, 64) - 1, four counters each -- shader-clock counter (s_memtime) before and
+ * after the loop, then the 100 MHz reference counter (s_memrealtime) before and after -- from which the
+ * clock the loop ran at follows.  sink: one float of device memory (written only to keep results live).
+ *
+ * sparse_attn_peak_stream: bytes (a positive multiple of 16) of src read once with 16-byte non-temporal
+ * loads (dst == NULL; sink: one float of device memory) or copied to dst (sink may be NULL), by 8
+ * workgroups of 256 threads per compute unit, grid-stride.
+ *
+ * Both are asynchronous on `stream`; time them with events.  Errors: SA_ERR_INVALID_ARG (NULL handle or
+ * pointer, misaligned pointer, iters < 1, bad bytes, not the handle's device), SA_ERR_HIP. */
+sa_status_t sparse_attn_peak_mfma(sa_handle_t h, const void *operands, int32_t iters, uint64_t *clocks,
+                                  float *sink, void *stream);
+sa_status_t sparse_attn_peak_stream(sa_handle_t h, const void *src, void *dst, int64_t bytes, float *sink,
+                                    void *stream);
 
 #ifdef __cplusplus
 }

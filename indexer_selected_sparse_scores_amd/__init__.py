@@ -32,14 +32,14 @@ SA_OP_PREFILL_PAGED, SA_OP_PREFILL_CHUNK, SA_OP_PREFILL_VARLEN = 7, 8, 9
 SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK, SA_DEVERR_ROW = 1, 2, 4, 8, 16
 
 # Every symbol include/sparse_attn.h declares.
-EXPORTED = ("sparse_attn_create", "sparse_attn_destroy", "sparse_attn_last_error",
+EXPORTED = ("sparse_attn_create", "sparse_attn_create_host", "sparse_attn_destroy", "sparse_attn_last_error",
             "sparse_attn_workspace_size", "sparse_attn_check", "indexer_scores", "topk_select",
             "topk_select_blocks", "sparse_attn_prefill", "sparse_attn_prefill_blocks", "sparse_attn_decode",
             "sparse_attn_decode_blocks", "sparse_attn_decode_noalloc", "sparse_attn_prefill_paged", "sparse_attn_prefill_chunk", "sparse_attn_prefill_varlen",
             "indexer_project_q",
             "indexer_project_k",
             "acceptance_rate", "acceptance_bin_stats",
-            "sparse_attn_profile", "sparse_attn_profile_read")
+            "sparse_attn_profile", "sparse_attn_profile_read", "sparse_attn_peak_mfma", "sparse_attn_peak_stream")
 KERNEL_KINDS = ("indexer", "topk", "attention", "merge", "project", "accept")
 
 
@@ -93,6 +93,7 @@ def load_library() -> ctypes.CDLL:
     st = ctypes.c_int
     sig = {
         "sparse_attn_create": ([ctypes.POINTER(sa_config_t), ctypes.POINTER(P)], st),
+        "sparse_attn_create_host": ([ctypes.POINTER(sa_config_t), i32, ctypes.POINTER(P)], st),
         "sparse_attn_destroy": ([P], None),
         "sparse_attn_last_error": ([P], ctypes.c_char_p),
         "sparse_attn_workspace_size": ([P, ctypes.c_int, i64, i64, ctypes.POINTER(sz)], st),
@@ -115,6 +116,8 @@ def load_library() -> ctypes.CDLL:
         "acceptance_rate": ([P, P, P, i64, i64, i64, P, P], st),
         "acceptance_bin_stats": ([P, P, P, i64, i32, i32, ctypes.c_float, P, P, P, P], st),
         "indexer_project_k": ([P, P, i64, P, P, P, i32, i32, i64, P, P, i64, P], st),
+        "sparse_attn_peak_mfma": ([P, P, i32, P, P, P], st),
+        "sparse_attn_peak_stream": ([P, P, P, i64, P, P], st),
         "sparse_attn_profile": ([P, ctypes.c_int], st),
         "sparse_attn_profile_read": ([P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)], st),
     }
@@ -153,12 +156,17 @@ def _check(h, status: int):
 class Handle:
     """Owns an sa_handle_t (created on the current device)."""
 
-    def __init__(self, cfg: Config):
+    def __init__(self, cfg: Config, host_cus: int | None = None):
+        """host_cus: create a host-only planning handle for a device of that many compute units
+        (sparse_attn_create_host): calls validate their arguments and launch nothing."""
         lib = load_library()
         self.cfg = cfg
         self._c = cfg.to_c()
         h = ctypes.c_void_p()
-        st = lib.sparse_attn_create(ctypes.byref(self._c), ctypes.byref(h))
+        if host_cus is None:
+            st = lib.sparse_attn_create(ctypes.byref(self._c), ctypes.byref(h))
+        else:
+            st = lib.sparse_attn_create_host(ctypes.byref(self._c), int(host_cus), ctypes.byref(h))
         if st != SA_OK:
             raise SparseAttnError(st, lib.sparse_attn_last_error(None).decode())
         self.ptr = h.value
@@ -377,6 +385,18 @@ def sparse_attn_profile_read(h: Handle) -> dict:
     n = (ctypes.c_int64 * len(KERNEL_KINDS))()
     _check(h.ptr, load_library().sparse_attn_profile_read(h.ptr, ms, n))
     return {k: (ms[i], n[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def sparse_attn_peak_mfma(h: Handle, operands, iters: int, clocks, sink, stream=None) -> None:
+    """Measurement aid: the bf16 MFMA loop on random operands (see the header for the counters)."""
+    _check(h.ptr, load_library().sparse_attn_peak_mfma(h.ptr, _ptr(operands), int(iters), _ptr(clocks), _ptr(sink),
+                                                       _stream(stream)))
+
+
+def sparse_attn_peak_stream(h: Handle, src, dst, nbytes: int, sink=None, stream=None) -> None:
+    """Measurement aid: a streaming read (dst None) or copy of nbytes."""
+    _check(h.ptr, load_library().sparse_attn_peak_stream(h.ptr, _ptr(src), _ptr(dst), int(nbytes), _ptr(sink),
+                                                         _stream(stream)))
 
 
 def workspace(h: Handle, op: int, n: int, max_ctx: int = 0, device=None):

@@ -12,7 +12,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
 SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "attention.hip", "prefill_topk.hip", "decode.hip",
            "projections.hip", "block_topk.hip", "paged_rows.hip",
-           "acceptance.hip"]
+           "acceptance.hip", "peaks.hip"]
 ARCH = os.environ.get("SA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

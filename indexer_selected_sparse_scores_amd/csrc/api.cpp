@@ -63,6 +63,9 @@ size_t elem_size(const sa_handle_s &h) { return h.cfg.dtype == SA_BF16 ? 2 : 4; 
 
 sa_status_t check_device(sa_handle_t h)
 {
+    if (h->device < 0)
+        return fail(h, SA_ERR_UNSUPPORTED,
+                    "a host-only handle (sparse_attn_create_host) validates and sizes calls but launches nothing");
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return fail(h, SA_ERR_HIP, "hipGetDevice failed");
     if (dev != h->device)
@@ -331,9 +334,15 @@ hipError_t drain_profile(sa_handle_s &h)
 
 extern "C" {
 
-sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
+}  // extern "C"
+
+namespace {
+
+// The configuration checks and the host half of a handle (kernels picked, nothing on a device yet).
+sa_status_t new_handle(const sa_config_t *cfg, sa_handle_t *out, sa_handle_s **made)
 {
     g_create_error.clear();
+    *made = nullptr;
     if (!cfg || !out) return fail(nullptr, SA_ERR_INVALID_ARG, "cfg and out must not be NULL");
     *out = nullptr;
     const sa_config_t &c = *cfg;
@@ -369,6 +378,19 @@ sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
         delete h;
         return fail(nullptr, SA_ERR_UNSUPPORTED, "d_qk + max_topk too large for the generic attention");
     }
+    *made = h;
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
+{
+    sa_handle_s *h = nullptr;
+    const sa_status_t sv = new_handle(cfg, out, &h);
+    if (sv != SA_OK) return sv;
     if (hipGetDevice(&h->device) != hipSuccess ||
         hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess ||
         h->n_cu < 1) {
@@ -403,14 +425,33 @@ sa_status_t sparse_attn_create(const sa_config_t *cfg, sa_handle_t *out)
     return SA_OK;
 }
 
+sa_status_t sparse_attn_create_host(const sa_config_t *cfg, int32_t n_cu, sa_handle_t *out)
+{
+    sa_handle_s *h = nullptr;
+    if (n_cu < 1 || n_cu > 65535) {
+        g_create_error.clear();
+        if (out) *out = nullptr;
+        return fail(nullptr, SA_ERR_INVALID_ARG, "n_cu must be in [1, 65535]");
+    }
+    const sa_status_t sv = new_handle(cfg, out, &h);
+    if (sv != SA_OK) return sv;
+    h->device = -1;  // no device: every launching call stops after its host validation
+    h->n_cu = n_cu;
+    h->d_err = nullptr;
+    *out = h;
+    return SA_OK;
+}
+
 void sparse_attn_destroy(sa_handle_t h)
 {
     if (!h) return;
-    (void)hipDeviceSynchronize();
-    (void)sa::drain_profile(*h);
-    for (hipEvent_t e : h->spare_events) (void)hipEventDestroy(e);
-    sa::destroy_projection_state(*h);
-    (void)hipFree(h->d_err);
+    if (h->device >= 0) {
+        (void)hipDeviceSynchronize();
+        (void)sa::drain_profile(*h);
+        for (hipEvent_t e : h->spare_events) (void)hipEventDestroy(e);
+        sa::destroy_projection_state(*h);
+        (void)hipFree(h->d_err);
+    }
     delete h;
 }
 
@@ -495,6 +536,7 @@ sa_status_t sparse_attn_check(sa_handle_t h, void *stream, uint32_t *bits)
 {
     if (bits) *bits = 0;
     if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
+    if (h->device < 0) return check_device(h);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     sa_status_t s = hip_status(h, hipStreamSynchronize(st), "hipStreamSynchronize");
     if (s != SA_OK) return s;
@@ -627,6 +669,7 @@ sa_status_t sparse_attn_decode_noalloc(sa_handle_t h, const void *q, const void 
                     "the allocation-free decode holds %zu bytes of device scratch; B = %d, max_ctx = %d, max_topk = %d "
                     "need %zu (use sparse_attn_decode with a workspace)",
                     kNoAllocBytes, B, max_ctx, h->cfg.max_topk, need);
+    if (h->device < 0) return check_device(h);
     void *ptr = g_scratch[h->device];  // set when the handle was created on this device
     return decode_impl(h, q, q_idx, w, kv_pages, v_pages, kidx_pages, n_pages, block_table, max_blocks, ctx_len,
                        topk, B, max_ctx, nullptr, out, lse, idx_out, ptr, kNoAllocBytes, stream);
@@ -650,8 +693,9 @@ sa_status_t prefill_impl(sa_handle_t h, const void *q, const void *k, const void
     if (L < 1 || L > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "L must be in [1, 2^31)");
     if (topk < 1 || topk > c.max_topk)
         return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
-    if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(q_idx) || !aligned16(k_idx))
-        return fail(h, SA_ERR_INVALID_ARG, "q, k, v, q_idx and k_idx must be 16-byte aligned");
+    if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(q_idx) || !aligned16(k_idx) ||
+        !aligned16(w) || !aligned16(out))
+        return fail(h, SA_ERR_INVALID_ARG, "q, k, v, q_idx, w, k_idx and out must be 16-byte aligned");
     if (blocks) {
         const sa_status_t sb = check_block_select(h, *blocks, L);
         if (sb != SA_OK) return sb;
@@ -749,8 +793,8 @@ sa_status_t decode_impl(sa_handle_t h, const void *q, const void *q_idx, const f
         return fail(h, SA_ERR_INVALID_ARG, "max_ctx (%d) must be in [1, max_blocks * page_size = %lld]",
                     max_ctx, (long long)max_blocks * c.page_size);
     if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
-        (v_pages && !aligned16(v_pages)))
-        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+        (v_pages && !aligned16(v_pages)) || !aligned16(w) || !aligned16(out))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx, w, out and the page pools must be 16-byte aligned");
     if (blocks) {
         const sa_status_t sb = check_block_select(h, *blocks, max_ctx);
         if (sb != SA_OK) return sb;
@@ -845,8 +889,8 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
     if (topk < 1 || topk > c.max_topk)
         return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
     if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
-        (v_pages && !aligned16(v_pages)))
-        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+        (v_pages && !aligned16(v_pages)) || !aligned16(w) || !aligned16(out))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx, w, out and the page pools must be 16-byte aligned");
     const PagedLayout lay = paged_layout(*h, T, max_ctx);
     if (!ws || ws_bytes < lay.total)
         return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
@@ -922,8 +966,8 @@ sa_status_t sparse_attn_prefill_varlen(sa_handle_t h, const void *q, const void 
     if (topk < 1 || topk > c.max_topk)
         return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
     if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
-        (v_pages && !aligned16(v_pages)))
-        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+        (v_pages && !aligned16(v_pages)) || !aligned16(w) || !aligned16(out))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx, w, out and the page pools must be 16-byte aligned");
     const VarlenApiLayout lay = varlen_api_layout(*h, T, max_ctx);
     if (!ws || ws_bytes < lay.total)
         return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);
@@ -989,8 +1033,8 @@ sa_status_t sparse_attn_prefill_chunk(sa_handle_t h, const void *q, const void *
     if (topk < 1 || topk > c.max_topk)
         return fail(h, SA_ERR_INVALID_ARG, "topk (%d) must be in [1, max_topk=%d]", topk, c.max_topk);
     if (!aligned16(q) || !aligned16(q_idx) || !aligned16(kv_pages) || !aligned16(kidx_pages) ||
-        (v_pages && !aligned16(v_pages)))
-        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx and the page pools must be 16-byte aligned");
+        (v_pages && !aligned16(v_pages)) || !aligned16(w) || !aligned16(out))
+        return fail(h, SA_ERR_INVALID_ARG, "q, q_idx, w, out and the page pools must be 16-byte aligned");
     const PrefillLayout lay = chunk_layout(*h, pos0, C);
     if (!ws || ws_bytes < lay.total)
         return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws_bytes);

@@ -69,6 +69,8 @@ def _load():
     lib.orc_attention.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -84,6 +86,11 @@ def _ptr(a: np.ndarray):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP loops (a timing aid; results do not depend on it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def default_scale(d_qk: int) -> float:

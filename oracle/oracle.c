@@ -270,3 +270,13 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads later OpenMP loops of this oracle use (n >= 1; timing aid, no effect on results). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
