@@ -447,14 +447,20 @@ __device__ __forceinline__ bool varlen_seq(const int32_t *cu, const int32_t *ctx
 
 // One workgroup: the row tiles of every valid sequence, in sequence order (an exclusive scan of the
 // per-sequence tile counts), then empty entries up to n_tiles.  An invalid sequence gets no tile.
+// Sequences go 1024 at a time: each thread scans its sequence's tile count, then all threads write that
+// block of sequences' tiles together, tile e finding its sequence by binary search over the block's
+// scanned offsets.  Offsets are 64-bit and every write is bounded by n_tiles (sequences that are each
+// valid may still overlap when cu_seqlens is not monotone overall).
 constexpr int kVarlenThreads = 1024;
 __global__ __launch_bounds__(kVarlenThreads) void varlen_tiles_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ ctx_len, int32_t n_seqs, int64_t T, int32_t max_ctx,
-    VarlenTile *__restrict__ tiles, int32_t n_tiles, uint32_t *err)
+    VarlenTile *__restrict__ tiles, int64_t n_tiles, uint32_t *err)
 {
     __shared__ int wave_sums[kVarlenThreads / kWave];
+    __shared__ int64_t first[kVarlenThreads + 1];  // first tile of each sequence of the block, then the end
+    __shared__ VarlenTile seq_tile[kVarlenThreads];  // each sequence's tile 0 (q0 = 0)
     const int tid = threadIdx.x;
-    int running = 0;
+    int64_t running = 0;
 #pragma unroll 1
     for (int b0 = 0; b0 < n_seqs; b0 += kVarlenThreads) {
         const int b = b0 + tid;
@@ -463,14 +469,32 @@ __global__ __launch_bounds__(kVarlenThreads) void varlen_tiles_kernel(
             flag_error(err, SA_DEVERR_ROW);
             len = 0;
         }
+        // a sequence of the fused path has at most max_ctx <= 524288 rows (65536 tiles): the clamp only keeps
+        // the 32-bit block scan from overflowing on sizes that never reach this kernel
         const int nt = (len + kRows - 1) / kRows;
+        const int ntc = nt < (1 << 20) ? nt : (1 << 20);
         int total;
-        const int off = running + topk::block_scan<kVarlenThreads / kWave>(nt, wave_sums, &total);
-        for (int i = 0; i < nt; ++i)
-            if (off + i < n_tiles) tiles[off + i] = VarlenTile{b, kRows * i, len, n - len, start, {0, 0, 0}};
+        const int excl = topk::block_scan<kVarlenThreads / kWave>(ntc, wave_sums, &total);
+        first[tid] = running + excl;
+        if (tid == kVarlenThreads - 1) first[kVarlenThreads] = running + total;
+        seq_tile[tid] = VarlenTile{b, 0, len, n - len, start, {0, 0, 0}};
+        __syncthreads();
+        const int64_t end = running + total < n_tiles ? running + total : n_tiles;
+        for (int64_t e = running + tid; e < end; e += kVarlenThreads) {
+            int lo = 0, hi = kVarlenThreads - 1;  // the last sequence with first[seq] <= e
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) / 2;
+                if (first[mid] <= e) lo = mid;
+                else hi = mid - 1;
+            }
+            VarlenTile t = seq_tile[lo];
+            t.q0 = kRows * (int32_t)(e - first[lo]);
+            tiles[e] = t;
+        }
         running += total;
+        __syncthreads();  // first / seq_tile are rewritten for the next block
     }
-    for (int j = running + tid; j < n_tiles; j += kVarlenThreads) tiles[j] = VarlenTile{0, 0, 0, 0, 0, {0, 0, 0}};
+    for (int64_t j = running + tid; j < n_tiles; j += kVarlenThreads) tiles[j] = VarlenTile{0, 0, 0, 0, 0, {0, 0, 0}};
 }
 
 // One thread per query row r: its sequence b (cu[b] <= r < cu[b + 1], by binary search) and position
@@ -558,7 +582,7 @@ hipError_t launch_prefill_varlen(sa_handle_s &h, const void *q_idx, const float 
     VarlenTile *tiles = reinterpret_cast<VarlenTile *>(base + v.tiles);
     hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(1), 0, st, counter);
     hipLaunchKernelGGL(varlen_tiles_kernel, dim3(1), dim3(kVarlenThreads), 0, st, cu, ctx_len, n_seqs, T, max_ctx,
-                       tiles, (int32_t)n_tiles, h.d_err);
+                       tiles, n_tiles, h.d_err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     KeySource ks{reinterpret_cast<const uint16_t *>(kidx_pages), block_table, n_pages, h.d_err};

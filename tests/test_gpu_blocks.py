@@ -343,3 +343,52 @@ def test_prefill_blocks_128k_sampled():
                                what="prefill_blocks 128k")
     del out, lse, idx, d
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------------
+# the fused prefill kernel's own scores, at the score tolerance
+# ---------------------------------------------------------------------------------------
+def _key_to_float(keys: np.ndarray) -> np.ndarray:
+    """Inverse of the library's order-preserving map of fp32 scores to uint32 (sign bit set for scores >= 0,
+    all bits flipped for negative ones)."""
+    k = keys.astype(np.uint32)
+    u = np.where(k & np.uint32(0x80000000), k & np.uint32(0x7FFFFFFF), ~k)
+    return u.view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("L", [1500, 4100])
+def test_fused_prefill_scores_at_the_score_tolerance(L):
+    """The two-tier prefill's first pass is the fused prefill indexer in its block-key mode: the same MFMA
+    tiles and epilogue as the per-query selection, keeping for each row and 64-key tile the order key of the
+    row's best score there.  Read back from the documented workspace layout ([index lists | 256-byte counter |
+    block keys [L, ceil(L / 64)] uint32]), they must equal the oracle's per-tile maxima within
+    2e-3 * (largest |w| ReLU sum of the tile) -- a direct check of the fused kernel's scores."""
+    wl = inputs.WORKLOADS["prefill_8k"]
+    K, bs, nb = 64, 64, 1  # rows with more than 64 visible keys keep block keys
+    say(f"fused prefill block keys L={L} (scores of the fused kernel vs the oracle)")
+    d = inputs.prefill_inputs(wl, DEV, L=L, seed=L + 3)
+    with sa.Handle(inputs.library_config(wl, max_topk=K)) as h:
+        out = torch.empty((L, 16, 512), device=DEV)
+        idx = torch.empty((L, K), device=DEV, dtype=torch.int32)
+        ws = sa.workspace(h, sa.SA_OP_PREFILL_BLOCKS, L)
+        sa.sparse_attn_prefill_blocks(h, d["q"], d["k"], None, d["q_idx"], d["w"], d["k_idx"], K, bs, nb, out, None,
+                                      idx, ws)
+        assert sa.sparse_attn_check(h) == 0
+        ld = (L + 63) // 64
+        off = (L * K * 4 + 255) // 256 * 256 + 256
+        keys = ws[off:off + L * ld * 4].view(torch.int32).view(L, ld)
+        rng = np.random.default_rng(L)
+        rows = np.unique(np.concatenate([[64, 65, 127, 128, L - 1], rng.integers(64, L, 19)]))
+        got = _key_to_float(to_np(keys[torch.as_tensor(rows, device=DEV)]).view(np.uint32))
+    ref, ref_abs = oracle.indexer_scores(to_np(d["q_idx"])[rows], to_np(d["w"])[rows], to_np(d["k_idx"]), rows + 1,
+                                         with_abs=True)
+    worst = 0.0
+    for i, t in enumerate(rows):
+        for j in range(t // 64 + 1):
+            seg = slice(64 * j, min(64 * j + 64, t + 1))
+            m_ref = ref[i, seg].max()
+            bound = 2e-3 * ref_abs[i, seg].max() + 1e-6
+            err = abs(got[i, j] - m_ref)
+            worst = max(worst, err / bound)
+            assert err <= bound, f"row {t} tile {j}: {got[i, j]} vs {m_ref} (bound {bound:.3g})"
+    say(f"  {len(rows)} rows, every visible tile: worst error {worst:.3f} of the bound")

@@ -380,3 +380,44 @@ def test_varlen_bad_layout_is_flagged():
         assert sa.sparse_attn_check(h) == 0  # cleared
     gi = to_np(idx)
     assert np.all(gi[120:] == -1), "rows outside every valid sequence must select nothing"
+
+
+def test_varlen_generic_kernels_fp32():
+    """An fp32 handle takes the varlen call's other path: the device row layout, then the rows as
+    sparse_attn_prefill_paged rows (generic kernels), against the oracle on every row."""
+    ctx, n_new = [100, 333, 7], [40, 333, 7]
+    rs = np.concatenate([np.full(k, b) for b, k in enumerate(n_new)])
+    rp = np.concatenate([np.arange(c - k, c) for c, k in zip(ctx, n_new)])
+    wl = inputs.small(inputs.WORKLOADS["decode_b64"], shapes=inputs.TINY, topk=16)
+    say(f"prefill_varlen tiny (fp32, generic path) ctx={ctx} new={n_new} topk=16")
+    d = inputs.paged_rows_inputs(wl, ctx, rs, rp, DEV, seed=35)
+    d["cu"] = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).to(DEV)
+    d["ctx_len"] = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).to(DEV)
+    with sa.Handle(inputs.library_config(wl, max_topk=16)) as h:
+        out, lse, idx = _run_varlen(h, d, 16, max(ctx))
+    _check(d, out, lse, idx, np.arange(len(rs)), 16, 64, "prefill_varlen tiny", latent=False)
+
+
+def test_varlen_few_rows_split_attention():
+    """Fewer rows than compute units: the fused row tiles, then the split decode attention over the varlen
+    rows.  Eight sequences with 0 to 4 new rows each (one sequence contributes none)."""
+    ctx, n_new = [900, 5000, 64, 2049, 3000, 1, 700, 4100], [3, 4, 0, 1, 2, 1, 4, 2]
+    say(f"prefill_varlen few rows ctx={ctx} new={n_new} topk=2048")
+    wl, d = _varlen(ctx, n_new, 2048, seed=36)
+    with sa.Handle(inputs.library_config(wl, max_topk=2048)) as h:
+        out, lse, idx = _run_varlen(h, d, 2048, max(ctx))
+    _check(d, out, lse, idx, np.arange(sum(n_new)), 2048, 512, "prefill_varlen few rows")
+
+
+def test_varlen_at_128k_sampled():
+    """The varlen batch the benchmark times: 8 sequences of 131072 cached tokens, the last 512 of each as
+    new rows; 4 rows of each sequence checked."""
+    n, per, n_seq = 131072, 512, 8
+    say(f"prefill_varlen {n_seq} x {per} new rows at the end of {n}-token contexts (32 rows checked)")
+    wl, d = _varlen([n] * n_seq, [per] * n_seq, 2048, seed=37)
+    with sa.Handle(inputs.library_config(wl, max_topk=2048)) as h:
+        out, lse, idx = _run_varlen(h, d, 2048, n)
+    rows = [b * per + r for b in range(n_seq) for r in (0, 1, per // 2 + b, per - 1)]
+    _check(d, out, lse, idx, rows, 2048, 512, "prefill_varlen 128k")
+    del d, out, lse, idx
+    torch.cuda.empty_cache()

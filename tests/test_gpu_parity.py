@@ -233,16 +233,21 @@ def test_prefill_all_scores_tied():
 
 
 def test_prefill_128k_sampled():
-    """The 131072-token prefill exactly as the benchmark runs it, checked on sampled rows."""
+    """The 131072-token prefill exactly as the benchmark runs it, checked on 256 rows: the first 64, the
+    last 64, the rows right after 32 salient positions (spread over the sequence) and 96 drawn at random."""
     wl = inputs.WORKLOADS["prefill_128k"]
-    say(f"prefill prefill_128k L={wl.L} topk={wl.topk} (sampled rows)")
+    say(f"prefill prefill_128k L={wl.L} topk={wl.topk} (256 sampled rows)")
     d = inputs.prefill_inputs(wl, DEV)
     with sa.Handle(inputs.library_config(wl)) as h:
         out, lse, idx = _prefill(h, d, wl.topk)
-    sal = d["salient"]
-    rows = np.unique(np.concatenate([[0, 2047, 2048, 65535, wl.L - 2, wl.L - 1],
-                                     sal[[0, len(sal) // 2, -1]] + 1,
-                                     np.random.default_rng(128).integers(0, wl.L, 6)]))
+    sal = np.sort(d["salient"])
+    after = sal[np.linspace(0, len(sal) - 1, 32).astype(np.int64)] + 1
+    after = after[after < wl.L]
+    rng = np.random.default_rng(128)
+    fixed = np.unique(np.concatenate([np.arange(64), np.arange(wl.L - 64, wl.L), after]))
+    pool = np.setdiff1d(np.arange(wl.L), fixed)
+    rows = np.unique(np.concatenate([fixed, rng.choice(pool, 256 - len(fixed), replace=False)]))
+    assert len(rows) == 256
     _check_prefill_rows(d, out, lse, idx, wl.topk, rows, latent=True, d_v=512, what="128k")
     del out, lse, idx, d
     torch.cuda.empty_cache()
@@ -297,6 +302,29 @@ def _check_decode(d, out, lse, idx, seqs, d_v, what, latent=True):
     say(f"{what}: seqs={len(seqs)} near-tie set diffs={diffs} max|dO|={err:.2e}")
 
 
+def _check_decode_light(d, out, lse, idx, seqs, what):
+    """_check_decode for long contexts, moving to the host only each checked sequence's index keys and its
+    selected latent rows: the oracle's scores over every cached token decide the top-k check, and the
+    oracle's attention runs on the GPU's own selection (rows gathered through the block table)."""
+    P = d["kidx_pages"].shape[1]
+    gi = to_np(idx)
+    topk = to_np(d["topk"])
+    diffs, err = 0, 0.0
+    for b in np.asarray(seqs):
+        n = int(d["ctx_np"][b])
+        m = min(int(topk[b]), n)
+        pages = d["block_table"][b, :(n + P - 1) // P].long()
+        kI = to_np(d["kidx_pages"][pages].reshape(-1, d["kidx_pages"].shape[-1])[:n])
+        sc = oracle.indexer_scores(to_np(d["q_idx"])[b:b + 1], to_np(d["w"])[b:b + 1], kI, [n])[0]
+        diffs += check_topk_row(gi[b], sc, m, n, what=f"{what} seq {b}")
+        sel = torch.as_tensor(gi[b][:m].astype(np.int64), device=DEV)
+        rows = to_np(d["kv_pages"][pages[sel // P], sel % P].reshape(m, 1, -1))
+        o, l = oracle.attention_rows(to_np(d["q"])[b:b + 1], rows, None, np.arange(m)[None, :],
+                                     oracle.default_scale(d["q"].shape[-1]), d_v=512)
+        err = max(err, check_attention(to_np(out)[b:b + 1], to_np(lse)[b:b + 1], o, l, what=f"{what} seq {b}"))
+    say(f"{what}: seqs={len(seqs)} near-tie set diffs={diffs} max|dO|={err:.2e}")
+
+
 def test_decode_small_paged():
     wl = inputs.WORKLOADS["decode_b64"]
     ctx = [1, 63, 64, 65, 300, 1000, 2500, 129]
@@ -332,11 +360,11 @@ def test_decode_b64_sampled():
 def test_decode_b64_128k_sampled():
     """The decode step exactly as the benchmark runs it (64 sequences at 131072 tokens)."""
     wl = inputs.WORKLOADS["decode_b64_128k"]
-    say("decode decode_b64_128k B=64 ctx=131072 topk=2048 (4 sequences checked)")
+    say("decode decode_b64_128k B=64 ctx=131072 topk=2048 (16 sequences checked)")
     d = inputs.decode_inputs(wl, DEV)
     with sa.Handle(inputs.library_config(wl)) as h:
         out, lse, idx = _decode(h, d)
-    _check_decode(d, out, lse, idx, [0, 21, 42, 63], 512, "decode_b64_128k")
+    _check_decode_light(d, out, lse, idx, np.arange(0, 64, 4), "decode_b64_128k")
     del out, lse, idx, d
     torch.cuda.empty_cache()
 
@@ -359,17 +387,26 @@ def test_decode_all_scores_tied():
     _check_decode(d, out, lse, idx, np.arange(len(ctx)), 512, "decode all-tied")
 
 
-@pytest.mark.parametrize("n", [1024, 5120, 32768])
-def test_decode_rl_sweep_step(n):
+def test_decode_rl_sweep_every_step():
+    """The RL-rollout sweep as the benchmark runs it: caches generated once for 32768 tokens per sequence,
+    one decode step of all 256 sequences at each n = 1024 i (i = 1..32) with the per-sequence budgets
+    min(n, max(256, floor(rho n))); 16 sequences checked at every step (a different 16 each time)."""
     wl = inputs.WORKLOADS["decode_rl_sweep"]
-    say(f"decode decode_rl_sweep B=256 n={n} (per-sequence k; 6 sequences checked)")
-    ctx = np.full(wl.B, n)
-    d = inputs.decode_inputs(wl, DEV, ctx=ctx)
-    k = inputs.rl_budget(n, d["rho"])
-    d["topk"] = torch.from_numpy(k.astype(np.int32)).to(DEV)
+    n_max = wl.ctx_range[1]
+    say(f"decode decode_rl_sweep B={wl.B}, all 32 steps n = 1024..{n_max} (16 sequences checked per step)")
+    d = inputs.decode_inputs(wl, DEV, ctx=np.full(wl.B, n_max))
     with sa.Handle(inputs.library_config(wl, max_topk=8192)) as h:
-        out, lse, idx = _decode(h, d)
-    _check_decode(d, out, lse, idx, [0, 7, 100, 128, 200, 255], 512, f"rl n={n}")
+        ws = sa.workspace(h, sa.SA_OP_DECODE, wl.B, n_max)
+        for i, n in enumerate(range(1024, n_max + 1, 1024)):
+            k = inputs.rl_budget(n, d["rho"])
+            step = dict(d)
+            step["topk"] = torch.from_numpy(k.astype(np.int32)).to(DEV)
+            step["ctx_len"] = torch.full((wl.B,), n, dtype=torch.int32, device=DEV)
+            step["ctx_np"] = np.full(wl.B, n)
+            step["max_ctx"] = n
+            out, lse, idx = _decode(h, step, ws)
+            seqs = (np.arange(16) * 16 + i) % wl.B
+            _check_decode_light(step, out, lse, idx, seqs, f"rl n={n}")
 
 
 def test_decode_1024_row_ranges_at_boundaries():
