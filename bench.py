@@ -685,7 +685,8 @@ def measure_two_tier(cfg, P, D, L, K, args, torch):
 def measure_chunk(cfg, P, D, K, args, torch):
     """Chunked prefill (not part of `value`): the last --chunk positions of sequence 0 of the decode
     caches as query rows, each over its own causal prefix of the paged caches, through
-    sparse_attn_prefill_chunk (fused row tiles) and through sparse_attn_prefill_paged (per-row path);
+    sparse_attn_prefill_chunk (fused row tiles) and through sparse_attn_prefill_paged (rows naming their own
+    sequence and position, cut into row tiles on the device);
     the query rows are the first rows of the prefill inputs (synthetic, same distribution)."""
     import numpy as np
 
@@ -705,7 +706,7 @@ def measure_chunk(cfg, P, D, K, args, torch):
         ws_c = sa.workspace(h, sa.SA_OP_PREFILL_CHUNK, C, n)
         table_row = D["block_table"][0].contiguous()
 
-        def run_rows():   # each row names its (sequence, position): the per-row path
+        def run_rows():   # each row names its (sequence, position): row tiles sorted on the device
             sa.sparse_attn_prefill_paged(h, P["q"][:C], P["q_idx"][:C], P["w"][:C], D["kv_pages"], None,
                                          D["kidx_pages"], D["block_table"][:1], row_seq, row_pos, n, K, out, None,
                                          idx, ws)
@@ -761,12 +762,13 @@ def measure_chunk(cfg, P, D, K, args, torch):
 
     res = {"workload": f"{C} new tokens of one sequence at positions {n - C}..{n - 1} over its paged caches",
            "ms": round(ms_c, 4), "tokens_per_s": round(C / (ms_c * 1e-3), 1), "kernels_ms": per_c,
-           "per_row_path": {"ms": round(ms_r, 4), "tokens_per_s": round(C / (ms_r * 1e-3), 1), "kernels_ms": per_r}}
+           "paged_rows_call": {"ms": round(ms_r, 4), "tokens_per_s": round(C / (ms_r * 1e-3), 1), "kernels_ms": per_r,
+                               "call": "sparse_attn_prefill_paged (rows naming their own sequence and position)"}}
     if per_c.get("indexer"):
         res["indexer_roofline"] = roof("indexer_topk_prefill_kernel (paged row tiles)", per_c["indexer"])
     if per_r.get("indexer"):
-        res["per_row_path"]["indexer_roofline"] = roof("indexer_decode_kernel (one row per grid column, all launches)",
-                                                       per_r["indexer"])
+        res["paged_rows_call"]["indexer_roofline"] = roof("indexer_topk_prefill_kernel (row tiles sorted by sequence "
+                                                          "and position on the device)", per_r["indexer"])
     ctx8 = D["ctx_np"][:n_seq].astype(np.int64)
     vpairs = int(sum((np.arange(c - per, c) + 1).sum() for c in ctx8))
     vtf = vpairs * 2 * s.n_idx_heads * s.d_idx / (per_v["indexer"] * 1e-3) / 1e12 if per_v.get("indexer") else None

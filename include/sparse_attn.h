@@ -275,6 +275,10 @@ sa_status_t sparse_attn_decode_noalloc(sa_handle_t h, const void *q, const void 
  *   out [T, H, d_v] fp32; lse [T, H] fp32 or NULL; idx_out [T, topk] int32 or NULL (positions,
  *   ascending, -1 padded)
  *   ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_PREFILL_PAGED, T, max_ctx)
+ * With bf16, H_I = 64, d_I = 128, 64-token pages, T <= 16384 and max_ctx <= 524288 the rows are sorted by
+ * (sequence, position) on the device and each sequence's rows run as tiles of 8 rows of the fused prefill
+ * indexer / top-k, sharing every key tile (one page); otherwise each row is scored alone.  Both give the
+ * same scores, term for term in the same order.
  * A row whose (row_seq, row_pos) is out of range sets SA_DEVERR_ROW and is skipped (its outputs
  * are unspecified).  Errors: SA_ERR_INVALID_ARG, SA_ERR_WORKSPACE, SA_ERR_HIP; device-side bits as
  * in sparse_attn_decode. */

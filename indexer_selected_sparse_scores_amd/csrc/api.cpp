@@ -143,13 +143,15 @@ DecodeLayout decode_layout(const sa_handle_s &h, int64_t B, int64_t max_ctx)
 // block of rows | idx | split-attention partials (few rows only)].
 struct PagedLayout {
     size_t seq, ctx, budget, scores, idx, attn, total;
-    int64_t chunk;   // query rows scored at once
+    int64_t chunk;   // query rows scored at once (per-row path)
     bool split;      // attention splits each row's selection over workgroups
+    bool fused;      // the rows run as fused prefill row tiles (sorted by sequence and position on the device)
 };
 
 PagedLayout paged_layout(const sa_handle_s &h, int64_t T, int64_t max_ctx)
 {
     PagedLayout p;
+    p.fused = sa::prefill_rows_fused(h, T, (int32_t)max_ctx);
     const int64_t ld = h.fast_decode ? (max_ctx + 63) / 64 * 64 : max_ctx;
     int64_t chunk = (int64_t)(kPrefillChunkBytes / (sizeof(float) * (size_t)ld));
     if (chunk < 1) chunk = 1;
@@ -165,8 +167,11 @@ PagedLayout paged_layout(const sa_handle_s &h, int64_t T, int64_t max_ctx)
     p.budget = at;
     at += align_up((size_t)T * sizeof(int32_t));
     p.scores = at;
-    at += align_up(h.fast_decode ? sa::decode_topk_layout(chunk, max_ctx).total
-                                 : (size_t)chunk * (size_t)max_ctx * sizeof(float));
+    if (p.fused)  // the fused row tiles' workspace (candidate lists, row table)
+        at += align_up(sa::prefill_rows_workspace(h, T, (int32_t)max_ctx));
+    else
+        at += align_up(h.fast_decode ? sa::decode_topk_layout(chunk, max_ctx).total
+                                     : (size_t)chunk * (size_t)max_ctx * sizeof(float));
     p.idx = at;
     at += align_up((size_t)T * (size_t)h.cfg.max_topk * sizeof(int32_t));
     p.attn = at;
@@ -908,8 +913,16 @@ sa_status_t sparse_attn_prefill_paged(sa_handle_t h, const void *q, const void *
     s = hip_status(h, sa::launch_paged_rows(*h, row_seq, row_pos, T, n_seqs, max_ctx, topk, seq, ctx, budget, st),
                    "row check launch");
     if (s != SA_OK) return s;
-    // indexer -> top-k per block of query rows, each row over its own sequence's pages
-    for (int64_t r0 = 0; r0 < T; r0 += lay.chunk) {
+    if (lay.fused) {
+        // rows sorted by (sequence, position) on the device, each sequence's run in tiles of 8 rows sharing
+        // every key tile (one page)
+        s = hip_status(h, sa::launch_prefill_rows(*h, q_idx, w, kidx_pages, n_pages, block_table, max_blocks, row_seq,
+                                                  row_pos, n_seqs, T, max_ctx, topk, idx, base + lay.scores, st),
+                       "row-tile indexer/top-k launch");
+        if (s != SA_OK) return s;
+    }
+    // otherwise indexer -> top-k per block of query rows, each row over its own sequence's pages
+    for (int64_t r0 = 0; !lay.fused && r0 < T; r0 += lay.chunk) {
         const int32_t rows = (int32_t)(r0 + lay.chunk < T ? lay.chunk : T - r0);
         const void *qi = reinterpret_cast<const char *>(q_idx) + r0 * c.n_idx_heads * c.d_idx * es;
         const float *wr = w + r0 * c.n_idx_heads;

@@ -139,19 +139,21 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bc[ks], acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bc[ks], acc1, 0, 0, 0);
             }
-            // register g of lane l: head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4, key l % 32
+            // register g of lane l: head 32 mt + 8 (g / 4) + 4 (l / 32) + g % 4, key l % 32.  The terms are
+            // summed in the fused prefill kernel's order (g ascending, the two head tiles alternating), so a
+            // query row gets bit-identical scores from either kernel.
             float part = 0.f;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const float4 w0 = sh.wq[8 * gq / 4 + lane / 32];
                 const float4 w1 = sh.wq[(32 + 8 * gq) / 4 + lane / 32];
                 part = fmaf(w0.x, relu(acc0[4 * gq]), part);
-                part = fmaf(w0.y, relu(acc0[4 * gq + 1]), part);
-                part = fmaf(w0.z, relu(acc0[4 * gq + 2]), part);
-                part = fmaf(w0.w, relu(acc0[4 * gq + 3]), part);
                 part = fmaf(w1.x, relu(acc1[4 * gq]), part);
+                part = fmaf(w0.y, relu(acc0[4 * gq + 1]), part);
                 part = fmaf(w1.y, relu(acc1[4 * gq + 1]), part);
+                part = fmaf(w0.z, relu(acc0[4 * gq + 2]), part);
                 part = fmaf(w1.z, relu(acc1[4 * gq + 2]), part);
+                part = fmaf(w0.w, relu(acc0[4 * gq + 3]), part);
                 part = fmaf(w1.w, relu(acc1[4 * gq + 3]), part);
             }
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),

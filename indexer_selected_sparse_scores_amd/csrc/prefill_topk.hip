@@ -78,16 +78,25 @@ struct VarlenTile {
     int32_t seq, q0, len, pos0, rowbase, pad[3];
 };
 
+// One row tile of query rows that name their own (sequence, position): n <= 8 rows of sequence seq, with
+// their row indices in q_idx, w and idx and their positions, in ascending position order (72 bytes).
+struct RowTile {
+    int32_t seq, n;
+    int32_t row[kRows], pos[kRows];
+};
+
 // Where the index keys come from: contiguous rows, or the 64-token pages of one sequence's block-table
-// row (a key tile is exactly one page).  With a tile table (a batch of sequences), each row tile names
-// its sequence, whose block-table row is table + seq * table_ld.
+// row (a key tile is exactly one page).  With a tile table (a batch of sequences) or a row table (rows
+// naming their own sequence and position), each row tile names its sequence, whose block-table row is
+// table + seq * table_ld.
 struct KeySource {
     const uint16_t *base;
-    const int32_t *table;   // paged: the sequence's block-table row (tile table: the whole block table)
+    const int32_t *table;   // paged: the sequence's block-table row (tile / row table: the whole block table)
     int64_t n_pages;
     uint32_t *err;
     const VarlenTile *tiles = nullptr;
     int64_t table_ld = 0;
+    const RowTile *rows = nullptr;
 };
 
 // Key tile layout: the 16-byte piece holding dims 8 j .. 8 j + 7 of key r sits at
@@ -141,11 +150,12 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
     for (;;) {
         if (tid == 0) sh.tile = atomicAdd(counter, 1);
         __syncthreads();
-        const int it = sh.tile;
+        const int it = __builtin_amdgcn_readfirstlane(sh.tile);
         if (it >= n_tiles) break;
         int64_t q0 = (int64_t)(n_tiles - 1 - it) * kRows;  // latest rows first
         int64_t L = L_all, pos0 = pos0_all, rb = 0;         // this tile's sequence, and its first query row
         const int32_t *table = ks.table;
+        const RowTile *rt = nullptr;  // row table: each row's own query row and position
         if constexpr (kPaged) {
             if (ks.tiles) {
                 const VarlenTile vt = ks.tiles[n_tiles - 1 - it];
@@ -158,16 +168,27 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 pos0 = vt.pos0;
                 rb = vt.rowbase;
                 table = ks.table + (int64_t)vt.seq * ks.table_ld;
+            } else if (ks.rows) {
+                rt = ks.rows + (n_tiles - 1 - it);
+                const int32_t nr = rt->n;
+                if (nr <= 0) {  // unused entry
+                    __syncthreads();
+                    continue;
+                }
+                q0 = 0;
+                L = nr;
+                table = ks.table + (int64_t)rt->seq * ks.table_ld;
             }
         }
-        const uint16_t *q_idx = q_idx_all + rb * kH * kD;
-        const float *w = w_all + rb * kH;
-        int32_t *idx = idx_all + rb * topk;
-        // position of the tile's last row (keys 0 .. t_last are streamed)
-        const int64_t t_last = pos0 + ((q0 + kRows - 1 < L - 1) ? q0 + kRows - 1 : L - 1);
-        const int64_t ri = q0 + wave;    // this wave's query row
-        const int64_t row = pos0 + ri;   // and its position: it sees keys 0 .. row
-        const bool row_ok = ri < L;
+        // query row (index into q_idx_all, w_all, idx_all) and position of row r < L - q0 of the tile
+        auto abs_row = [&](int r) -> int64_t { return rt ? (int64_t)rt->row[r] : rb + q0 + r; };
+        auto pos_of = [&](int r) -> int64_t { return rt ? (int64_t)rt->pos[r] : pos0 + q0 + r; };
+        const int n_rows = (int)(L - q0 < kRows ? L - q0 : kRows);
+        // position of the tile's last row (keys 0 .. t_last are streamed; positions ascend within a tile)
+        const int64_t t_last = pos_of(n_rows - 1);
+        const int64_t ri = q0 + wave;    // this wave's query row within the call (block keys) or tile
+        const bool row_ok = wave < n_rows;
+        const int64_t row = row_ok ? pos_of(wave) : 0;   // its position: it sees keys 0 .. row
         const int m = row_ok ? (int)((int64_t)topk < row + 1 ? (int64_t)topk : row + 1) : 0;
         const bool selects = row_ok && row + 1 > need;  // fewer than all visible keys
         int n_cand = 0;                                   // this row's candidate list length
@@ -190,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             // A operand and weights of this wave's query row
             bf16x8 a[2][kD / 16];
             float wv[2][16];
-            const int64_t qrow = row_ok ? ri : L - 1;
-            const uint16_t *qr = q_idx + qrow * (int64_t)kH * kD;
+            const int64_t qrow = abs_row(row_ok ? wave : n_rows - 1);
+            const uint16_t *qr = q_idx_all + qrow * (int64_t)kH * kD;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int g = 0; g < 16; ++g)
-                    wv[mt][g] = w[qrow * kH + 32 * mt + 8 * (g / 4) + 4 * (lane / 32) + g % 4];
+                    wv[mt][g] = w_all[qrow * kH + 32 * mt + 8 * (g / 4) + 4 * (lane / 32) + g % 4];
 
             // key tile loader: thread i moves chunks i and i + 512 of the 1024 in a tile
             const int n_kt = (int)(t_last / kKT) + 1;
@@ -380,11 +401,9 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
         __syncthreads();
 
 #pragma unroll 1
-        for (int r = 0; r < kRows; ++r) {
-            const int64_t rr = q0 + r;
-            if (rr >= L) break;
-            int32_t *dst = idx + rr * topk;
-            const int64_t pr = pos0 + rr;  // the row's position
+        for (int r = 0; r < n_rows; ++r) {
+            int32_t *dst = idx_all + abs_row(r) * topk;
+            const int64_t pr = pos_of(r);  // the row's position
             if (pr + 1 <= topk) {  // every visible key is selected
                 for (int i = tid; i < topk; i += kThreads) dst[i] = i <= pr ? i : -1;
                 continue;
@@ -524,6 +543,108 @@ __global__ void varlen_rows_kernel(const int32_t *__restrict__ cu, const int32_t
     row_pos[r] = ok ? n - len + (int32_t)(r - start) : -1;
 }
 
+// Query rows that each name their sequence and position, cut into row tiles of one sequence: one workgroup
+// sorts the T <= kRowTileMaxRows rows by (sequence, position, row) -- a 64-bit key per row in LDS, bitonic
+// sort -- and cuts each sequence's run of the sorted order into tiles of 8 rows; tiles past the last get
+// n = 0.  A row whose sequence or position is out of range sets SA_DEVERR_ROW, sorts last, belongs to no
+// tile and gets an empty index list.  Key: sequence (31 bits) | position (19 bits) | row (14 bits).
+constexpr int kRowTileMaxRows = 16384;
+constexpr int kRowTileThreads = 1024;
+constexpr int kRowTilePer = kRowTileMaxRows / kRowTileThreads;  // sorted entries per thread in the cut (16)
+constexpr uint64_t kNoKey = ~0ull;
+
+__global__ __launch_bounds__(kRowTileThreads) void row_tiles_kernel(
+    const int32_t *__restrict__ row_seq, const int32_t *__restrict__ row_pos, int32_t T, int32_t n_seqs,
+    int32_t max_ctx, int32_t topk, RowTile *__restrict__ tiles, int32_t n_tiles, int32_t *__restrict__ idx,
+    uint32_t *err)
+{
+    __shared__ uint64_t key[kRowTileMaxRows];
+    __shared__ int scan[kRowTileThreads];
+    __shared__ int wave_sums[kRowTileThreads / kWave];
+    const int tid = threadIdx.x;
+    int N = 2;
+    while (N < T) N *= 2;
+    for (int i = tid; i < N; i += kRowTileThreads) {
+        uint64_t k = kNoKey;
+        if (i < T) {
+            const int32_t b = row_seq[i], p = row_pos[i];
+            if (b >= 0 && b < n_seqs && p >= 0 && p < max_ctx) {
+                k = ((uint64_t)b << 33) | ((uint64_t)p << 14) | (uint64_t)i;
+            } else {
+                flag_error(err, SA_DEVERR_ROW);
+                for (int j = 0; j < topk; ++j) idx[(int64_t)i * topk + j] = -1;
+            }
+        }
+        key[i] = k;
+    }
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int k = 2; k <= N; k *= 2) {
+        for (int j = k / 2; j > 0; j /= 2) {
+            for (int i = tid; i < N; i += kRowTileThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t a = key[i], c = key[ixj];
+                    if ((a > c) == ((i & k) == 0)) {
+                        key[i] = c;
+                        key[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // cut: thread c takes sorted entries [16 c, 16 c + 16).  Entry i starts a tile when its offset from the
+    // start of its sequence's run is a multiple of 8; tile of entry i = tile starts up to i, minus one.
+    const int i0 = tid * kRowTilePer;
+    const auto seq_of = [&](int i) { return (int)(key[i] >> 33); };
+    const auto valid = [&](int i) { return i < N && key[i] != kNoKey; };
+    int last_start = -1;  // last run start in this thread's entries
+    for (int u = 0; u < kRowTilePer; ++u) {
+        const int i = i0 + u;
+        if (valid(i) && (i == 0 || seq_of(i - 1) != seq_of(i))) last_start = i;
+    }
+    // inclusive max-scan of the run starts over the threads (Hillis-Steele), then this thread's carry
+    scan[tid] = last_start;
+    __syncthreads();
+    for (int d = 1; d < kRowTileThreads; d *= 2) {
+        const int v = tid >= d ? scan[tid - d] : -1;
+        __syncthreads();
+        if (v > scan[tid]) scan[tid] = v;
+        __syncthreads();
+    }
+    int begin = tid > 0 ? scan[tid - 1] : -1;  // run start before this thread's entries
+    int starts = 0;
+    for (int u = 0; u < kRowTilePer; ++u) {
+        const int i = i0 + u;
+        if (!valid(i)) break;
+        if (i == 0 || seq_of(i - 1) != seq_of(i)) begin = i;
+        starts += ((i - begin) % kRows) == 0 ? 1 : 0;
+    }
+    int n_total;
+    int tile = topk::block_scan<kRowTileThreads / kWave>(starts, wave_sums, &n_total) - 1;
+    begin = tid > 0 ? scan[tid - 1] : -1;
+    for (int u = 0; u < kRowTilePer; ++u) {
+        const int i = i0 + u;
+        if (!valid(i)) break;
+        const int sq = seq_of(i);
+        if (i == 0 || seq_of(i - 1) != sq) begin = i;
+        const int slot = (i - begin) % kRows;
+        if (slot == 0) ++tile;
+        if (tile >= n_tiles) break;  // cannot happen: n_tiles bounds the tiles of T rows
+        RowTile &t = tiles[tile];
+        t.row[slot] = (int32_t)(key[i] & 0x3FFF);
+        t.pos[slot] = (int32_t)((key[i] >> 14) & 0x7FFFF);
+        if (slot == 0) t.seq = sq;
+        const bool last = slot == kRows - 1 || !valid(i + 1) || seq_of(i + 1) != sq;
+        if (last) t.n = slot + 1;
+    }
+    for (int e = n_total + tid; e < n_tiles; e += kRowTileThreads) {
+        tiles[e].seq = 0;
+        tiles[e].n = 0;
+    }
+}
+
 }  // namespace
 
 size_t prefill_block_keys_ld(int64_t L, int64_t pos0) { return (pos0 + L + kKT - 1) / kKT; }
@@ -593,6 +714,60 @@ hipError_t launch_prefill_varlen(sa_handle_s &h, const void *q_idx, const float 
     hipLaunchKernelGGL((indexer_topk_prefill_kernel<true, false>), dim3((unsigned)slots), dim3(kThreads), 0, st,
                        reinterpret_cast<const uint16_t *>(q_idx), w, ks, (int64_t)0, (int64_t)0, topk, (int64_t)topk,
                        idx, cands, v.ld, none, counter, (int32_t)n_tiles);
+    return hipGetLastError();
+}
+
+// Rows naming their own (sequence, position): [counter | candidate lists of the workgroup slots | row table]
+struct RowsLayout {
+    int64_t tiles_cap, slots, ld;
+    size_t cands, table, total;
+};
+RowsLayout rows_layout(const sa_handle_s &h, int64_t T, int32_t max_ctx)
+{
+    RowsLayout r;
+    r.tiles_cap = T;  // never more tiles than rows (one row per tile when every row has its own sequence)
+    r.slots = r.tiles_cap < h.n_cu ? r.tiles_cap : h.n_cu;
+    r.ld = ((int64_t)max_ctx + 63) / 64 * 64;
+    r.cands = 256;
+    r.table = r.cands + (size_t)r.slots * kRows * (size_t)r.ld * sizeof(uint2);
+    r.total = r.table + (size_t)r.tiles_cap * sizeof(RowTile);
+    return r;
+}
+
+bool prefill_rows_fused(const sa_handle_s &h, int64_t T, int32_t max_ctx)
+{
+    static_assert(kPrefillMaxPages * 64 <= (1 << 19), "positions take 19 bits of the sort key");
+    return h.fast_decode && T <= kRowTileMaxRows && ((int64_t)max_ctx + 63) / 64 <= kPrefillMaxPages;
+}
+
+size_t prefill_rows_workspace(const sa_handle_s &h, int64_t T, int32_t max_ctx)
+{
+    return rows_layout(h, T, max_ctx).total;
+}
+
+hipError_t launch_prefill_rows(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks, const int32_t *row_seq,
+                               const int32_t *row_pos, int32_t n_seqs, int64_t T, int32_t max_ctx, int32_t topk,
+                               int32_t *idx, void *ws, hipStream_t st)
+{
+    const RowsLayout r = rows_layout(h, T, max_ctx);
+    char *base = reinterpret_cast<char *>(ws);
+    int32_t *counter = reinterpret_cast<int32_t *>(base);
+    uint2 *cands = reinterpret_cast<uint2 *>(base + r.cands);
+    RowTile *tiles = reinterpret_cast<RowTile *>(base + r.table);
+    hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(1), 0, st, counter);
+    hipLaunchKernelGGL(row_tiles_kernel, dim3(1), dim3(kRowTileThreads), 0, st, row_seq, row_pos, (int32_t)T, n_seqs,
+                       max_ctx, topk, tiles, (int32_t)r.tiles_cap, idx, h.d_err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    KeySource ks{reinterpret_cast<const uint16_t *>(kidx_pages), block_table, n_pages, h.d_err};
+    ks.rows = tiles;
+    ks.table_ld = max_blocks;
+    const BlockKeysOut none{nullptr, 0};
+    KernelTimer timer(h, SA_KERNEL_INDEXER, st);
+    hipLaunchKernelGGL((indexer_topk_prefill_kernel<true, false>), dim3((unsigned)r.slots), dim3(kThreads), 0, st,
+                       reinterpret_cast<const uint16_t *>(q_idx), w, ks, (int64_t)0, (int64_t)0, topk, (int64_t)topk,
+                       idx, cands, r.ld, none, counter, (int32_t)r.tiles_cap);
     return hipGetLastError();
 }
 

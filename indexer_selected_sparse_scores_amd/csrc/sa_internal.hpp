@@ -137,6 +137,17 @@ hipError_t launch_prefill_topk(sa_handle_s &h, const void *q_idx, const float *w
 // bytes.  launch_varlen_rows writes each row's sequence and position to row_seq / row_pos [T] ((-1, -1)
 // and an empty selection in idx for a row of no valid sequence); it runs first.
 size_t prefill_varlen_workspace(const sa_handle_s &h, int64_t T, int32_t max_ctx);
+
+// Rows that each name their (sequence, position) -- sparse_attn_prefill_paged -- on the fused prefill row tiles:
+// the rows are sorted by (sequence, position) on the device and each sequence's run is cut into tiles of 8 rows.
+// Needs the fast decode shapes, T <= 16384 and max_ctx <= kPrefillMaxPages * 64.  Rows out of range set
+// SA_DEVERR_ROW and get empty index lists.  ws holds prefill_rows_workspace(h, T, max_ctx).
+bool prefill_rows_fused(const sa_handle_s &h, int64_t T, int32_t max_ctx);
+size_t prefill_rows_workspace(const sa_handle_s &h, int64_t T, int32_t max_ctx);
+hipError_t launch_prefill_rows(sa_handle_s &h, const void *q_idx, const float *w, const void *kidx_pages,
+                               int64_t n_pages, const int32_t *block_table, int32_t max_blocks, const int32_t *row_seq,
+                               const int32_t *row_pos, int32_t n_seqs, int64_t T, int32_t max_ctx, int32_t topk,
+                               int32_t *idx, void *ws, hipStream_t st);
 hipError_t launch_varlen_rows(sa_handle_s &h, const int32_t *cu, const int32_t *ctx_len, int32_t n_seqs, int64_t T,
                               int32_t max_ctx, int32_t topk, int32_t *idx, int32_t *row_seq, int32_t *row_pos,
                               hipStream_t st);

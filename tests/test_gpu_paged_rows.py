@@ -421,3 +421,26 @@ def test_varlen_at_128k_sampled():
     _check(d, out, lse, idx, rows, 2048, 512, "prefill_varlen 128k")
     del d, out, lse, idx
     torch.cuda.empty_cache()
+
+
+def test_row_tiles_and_per_row_path_agree_bit_for_bit():
+    """Up to 16384 rows run as fused row tiles (sorted by sequence and position on the device); one more
+    row sends the same call down the per-row path (decode indexer and top-k per row).  Both compute the
+    same scores in the same order, so on the shared rows every selection and output is bit-identical; a
+    sample is also checked against the oracle.  Rows come from 40 sequences, interleaved and shuffled."""
+    wl = inputs.WORKLOADS["decode_b64"]
+    n_seq, T = 40, 16385
+    rng = np.random.default_rng(38)
+    ctx = rng.integers(200, 3000, n_seq)
+    rs = rng.integers(0, n_seq, T)
+    rp = np.array([rng.integers(0, ctx[b]) for b in rs])
+    say(f"prefill_paged: {T - 1} rows as row tiles vs {T} rows per row, {n_seq} sequences, topk=128")
+    d = inputs.paged_rows_inputs(inputs.small(wl, topk=128), ctx, rs, rp, DEV, seed=38)
+    with sa.Handle(inputs.library_config(wl, max_topk=128)) as h:
+        out, lse, idx = _run(h, d, 128)
+        part = {k: (v[:T - 1] if isinstance(v, torch.Tensor) and v.shape[:1] == (T,) else v) for k, v in d.items()}
+        part["rp_np"] = rp[:T - 1]
+        out2, lse2, idx2 = _run(h, part, 128, max_ctx=int(rp.max()) + 1)
+    assert torch.equal(idx[:T - 1], idx2), "selections differ between the two paths"
+    assert torch.equal(out[:T - 1], out2) and torch.equal(lse[:T - 1], lse2), "outputs differ between the two paths"
+    _check(d, out, lse, idx, rng.integers(0, T, 24), 128, 512, "prefill_paged row tiles / per row")
