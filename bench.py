@@ -554,8 +554,8 @@ FLUSH_BYTES = 512 << 20  # twice the MI355X's 256 MB Infinity Cache
 
 def measure_projections(h, P, L, steps, torch):
     """The index projections at the prefill shape (not part of `value`): q_idx and w from the L
-    attention query rows (two bf16 GEMMs on hipBLASLt) and k_idx from the L latent rows (the
-    library's MFMA kernel), with synthetic N(0, 1/width) bf16 weights."""
+    attention query rows (one MFMA GEMM over [W_iq; W_w]) and k_idx from the L latent rows, with
+    synthetic N(0, 1/width) bf16 weights."""
     import indexer_selected_sparse_scores_amd as sa
     dev = "cuda"
     s = h.cfg
@@ -568,7 +568,6 @@ def measure_projections(h, P, L, steps, torch):
     q_idx = torch.empty((L, s.n_idx_heads, s.d_idx), dtype=torch.bfloat16, device=dev)
     w = torch.empty((L, s.n_idx_heads), dtype=torch.float32, device=dev)
     k_idx = torch.empty((L, s.d_idx), dtype=torch.bfloat16, device=dev)
-    ws = sa.workspace(h, sa.SA_OP_PROJECT, L)
 
     def timed(fn):
         fn()
@@ -582,7 +581,7 @@ def measure_projections(h, P, L, steps, torch):
         return e0.elapsed_time(e1) / steps
 
     log(f"[bench] index projections L={L}")
-    q_ms = timed(lambda: sa.indexer_project_q(h, P["q"], W_iq, W_w, q_idx, w, ws))
+    q_ms = timed(lambda: sa.indexer_project_q(h, P["q"], W_iq, W_w, q_idx, w))
     k_ms = timed(lambda: sa.indexer_project_k(h, P["k"], W_ik, k_idx))
     sa.sparse_attn_check(h)
     q_flop = 2.0 * L * kq * (s.n_idx_heads * s.d_idx + s.n_idx_heads)

@@ -344,12 +344,13 @@ sa_status_t sparse_attn_prefill_chunk(sa_handle_t h, const void *q, const void *
  * indexer_project_q, for each of the L query rows q[t] (H * d_qk values, [L, H, d_qk]):
  *   q_idx[t] = W_iq q[t]   W_iq [H_I * d_I, H * d_qk]  ->  q_idx [L, H_I, d_I] bf16
  *   w[t]     = W_w  q[t]   W_w  [H_I, H * d_qk]        ->  w [L, H_I] fp32
- *   Either pair (W_iq, q_idx) or (W_w, w) may be NULL to skip it.  Two plain GEMMs, run by
- *   hipBLASLt on `stream`; its handle is created on the first call of this handle (which may
- *   synchronise and may allocate device memory of hipBLASLt's own) and released by
- *   sparse_attn_destroy.  ws, ws_bytes: at least sparse_attn_workspace_size(SA_OP_PROJECT, L).
+ *   Either pair (W_iq, q_idx) or (W_w, w) may be NULL to skip it.  One kernel computes both in a
+ *   single pass over q: [W_iq; W_w] is the second operand of one tiled bf16 MFMA GEMM (fp32
+ *   accumulation), whose last column tile is W_w's.  Needs H * d_qk a multiple of 64, H_I * d_I a
+ *   multiple of 256 and H_I <= 256.  Needs no workspace: ws and ws_bytes are ignored (may be NULL / 0;
+ *   sparse_attn_workspace_size(SA_OP_PROJECT, L) is 0).
  * Errors: SA_ERR_INVALID_ARG (NULL q, L < 1, both pairs NULL, a pair half NULL, misaligned),
- * SA_ERR_UNSUPPORTED (not bf16), SA_ERR_WORKSPACE, SA_ERR_HIP (hipBLASLt failure, in last_error). */
+ * SA_ERR_UNSUPPORTED (not bf16, or another shape), SA_ERR_HIP. */
 sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const void *W_iq, const void *W_w,
                               void *q_idx, float *w, void *ws, size_t ws_bytes, void *stream);
 

@@ -42,9 +42,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    # the query projections call hipBLASLt
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp, "-L/opt/rocm/lib", "-lhipblaslt",
-           "-Wl,-rpath,/opt/rocm/lib"]
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

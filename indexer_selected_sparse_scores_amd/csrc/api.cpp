@@ -1139,11 +1139,16 @@ sa_status_t indexer_project_q(sa_handle_t h, const void *q, int64_t L, const voi
     if (h->cfg.dtype != SA_BF16) return fail(h, SA_ERR_UNSUPPORTED, "the projections take bf16 handles only");
     if (!aligned16(q) || (W_iq && (!aligned16(W_iq) || !aligned16(q_idx))) || (W_w && (!aligned16(W_w) || !aligned16(w))))
         return fail(h, SA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
-    if (!ws || ws_bytes < sa::projection_workspace())
-        return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", sa::projection_workspace(), ws_bytes);
+    const int64_t K = (int64_t)h->cfg.n_heads * h->cfg.d_qk, N1 = (int64_t)h->cfg.n_idx_heads * h->cfg.d_idx;
+    if (K % 64 != 0 || K > (1 << 24) || N1 % 256 != 0 || h->cfg.n_idx_heads > 256)
+        return fail(h, SA_ERR_UNSUPPORTED,
+                    "the query projection needs H * d_qk a multiple of 64 up to 2^24 (got %lld), H_I * d_I a "
+                    "multiple of 256 (got %lld) and H_I <= 256",
+                    (long long)K, (long long)N1);
+    (void)ws;  // no workspace is needed
+    (void)ws_bytes;
     sa_status_t s = check_device(h);
     if (s != SA_OK) return s;
-    // on failure the launcher has put hipBLASLt's reason in last_error
     return sa::launch_project_q(*h, q, L, W_iq, W_w, q_idx, w, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
 }
 

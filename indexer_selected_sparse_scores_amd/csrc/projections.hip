@@ -4,14 +4,14 @@
 // i_k = W_ik(k)).  The head weights w(t, j) of the score in section 2.2 are taken as one more
 // linear map of the query row.
 //
-//  * q side: q_idx = q W_iq^T (bf16 out) and w = q W_w^T (fp32 out) are plain GEMMs over the
-//    H * d_qk query row (9216 wide for the latent shapes): they run on hipBLASLt, bf16 inputs
-//    with fp32 accumulation.
+//  * q side: q_idx = q W_iq^T (bf16 out) and w = q W_w^T (fp32 out), one kernel and one pass over
+//    the H * d_qk query rows (9216 wide for the latent shapes): [W_iq; W_w] is the B operand of a
+//    tiled bf16 GEMM on v_mfma_f32_32x32x16_bf16 with fp32 accumulation, whose last column tile is
+//    the head weights'.
 //  * k side: k_idx = k W_ik^T over the 576-wide latent row on v_mfma_f32_32x32x16_bf16, W_ik
 //    held in LDS by persistent workgroups, each projected row written straight to where it
 //    belongs: the contiguous [L, d_I] array, or the token's slot of the paged index-key cache.
-#include <hipblaslt/hipblaslt.h>
-
+#include <string>
 #include <type_traits>
 
 #include "sa_device.hpp"
@@ -150,92 +150,264 @@ __global__ __launch_bounds__(kPThreads, 1) void project_k_kernel(
     }
 }
 
-struct BltState {
-    hipblasLtHandle_t lt = nullptr;
+// ---- query side -----------------------------------------------------------------------------
+// One workgroup of eight waves (two per SIMD, so that one wave's LDS and memory waits are covered by the
+// other's products) computes a 256 x 256 tile of [q_idx | w] = q [W_iq; W_w]^T: wave (wm, wn), wm = 0..1,
+// wn = 0..3, its 128 x 64 part as 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16.  K advances in blocks of 64
+// through two LDS buffers, each holding the block's 256 A rows and 256 B rows row-major (128 bytes a row)
+// with the eight 16-byte chunks of row r permuted to position c ^ swz(r), so the operand reads (32 rows of
+// one chunk per half-wave) hit distinct banks.  Each wave moves 64 of the rows: 8 loads of 8 whole rows (1 KB,
+// eight 128-byte lines) per block into registers and, three k-steps later, into the block's buffer, two loads
+// and two stores beside the 8 products of every k-step.  The one barrier per block comes before its last
+// k-step: it publishes the next block and frees the buffer just read.  Workgroups are ordered by XCD (id % 8):
+// each XCD takes its own M tiles, kQGroupM at a time with every N tile, so its concurrent workgroups share
+// their q and weight blocks through its L2.  The column tile past W_iq's is W_w's (n_w <= 256 rows, fp32 out).
+constexpr int kQM = 256, kQN = 256, kQK = 64;     // workgroup tile and K block
+constexpr int kQWaves = 8;
+constexpr int kQThreads = kQWaves * kWave;
+constexpr int kQPanelBytes = kQM * kQK * 2;       // one operand's rows of a K block: 32 KB
+constexpr int kQBufBytes = 2 * kQPanelBytes;      // A and B: 64 KB
+constexpr int kQLdsBytes = 2 * kQBufBytes;        // two buffers
+constexpr int kQLoads = 2 * kQM / 8 / kQWaves;     // 8-row loads per wave per K block (8)
+constexpr int kQGroupM = 4;                        // M tiles an XCD works on at once
+constexpr int kXcds = 8;
+
+struct ProjQArgs {
+    const uint16_t *q, *w_iq, *w_w;
+    uint16_t *q_idx;
+    float *w;
+    int64_t M;        // query rows
+    int K;            // row width (multiple of 64)
+    int n_iq_tiles;   // column tiles of W_iq (N1 / 256; 0 without W_iq)
+    int n_w;          // rows of W_w (0 without it)
+    int n_n;          // column tiles in all
+    int64_t n_m;      // row tiles
 };
 
-const char *blt_name(hipblasStatus_t s)
-{
-    switch (s) {
-    case HIPBLAS_STATUS_SUCCESS: return "success";
-    case HIPBLAS_STATUS_NOT_INITIALIZED: return "not initialised";
-    case HIPBLAS_STATUS_ALLOC_FAILED: return "allocation failed";
-    case HIPBLAS_STATUS_INVALID_VALUE: return "invalid value";
-    case HIPBLAS_STATUS_EXECUTION_FAILED: return "execution failed";
-    case HIPBLAS_STATUS_NOT_SUPPORTED: return "not supported";
-    default: return "error";
-    }
-}
+// chunk permutation of a row: a bijection on each 8 rows, and on the even (odd) rows of each 16, so the
+// 8 or 16 lanes an LDS cycle serves read distinct banks
+__device__ __forceinline__ int qswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// Y [L, N] = X [L, K] W [N, K]^T, row-major, bf16 inputs, fp32 accumulation, output bf16 or
-// fp32.  In hipBLASLt's column-major terms: D (N x L, ld N) = A^T B with A = W (K x N, ld K)
-// and B = X (K x L, ld K).
-sa_status_t gemm_tn(sa_handle_s &h, hipblasLtHandle_t lt, const void *X, const void *W, void *Y, int64_t L,
-                    int64_t K, int64_t N, bool out_bf16, void *ws, size_t ws_bytes, hipStream_t st)
+__global__ __launch_bounds__(kQThreads, 1) void project_q_kernel(ProjQArgs a)
 {
-    hipblasLtMatmulDesc_t desc = nullptr;
-    hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ld = nullptr;
-    hipblasLtMatmulPreference_t pref = nullptr;
-    hipblasStatus_t s = hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
-    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-    const uint64_t wsb = ws_bytes;
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta));
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb));
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, K, N, K);
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, K, L, K);
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&ld, out_bf16 ? HIP_R_16BF : HIP_R_32F, N, L, N);
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulPreferenceCreate(&pref);
-    if (s == HIPBLAS_STATUS_SUCCESS)
-        s = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb));
-    hipblasLtMatmulHeuristicResult_t res{};
-    int count = 0;
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulAlgoGetHeuristic(lt, desc, la, lb, ld, ld, pref, 1, &res, &count);
-    if (s == HIPBLAS_STATUS_SUCCESS && count < 1) s = HIPBLAS_STATUS_NOT_SUPPORTED;
-    const float alpha = 1.f, beta = 0.f;
-    if (s == HIPBLAS_STATUS_SUCCESS)
-        s = hipblasLtMatmul(lt, desc, &alpha, W, la, X, lb, &beta, Y, ld, Y, ld, &res.algo, ws, ws_bytes, st);
-    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-    if (ld) hipblasLtMatrixLayoutDestroy(ld);
-    if (lb) hipblasLtMatrixLayoutDestroy(lb);
-    if (la) hipblasLtMatrixLayoutDestroy(la);
-    if (desc) hipblasLtMatmulDescDestroy(desc);
-    if (s != HIPBLAS_STATUS_SUCCESS) {
-        h.last_error = std::string("hipBLASLt GEMM (") + std::to_string(L) + " x " + std::to_string(N) + " x " +
-                       std::to_string(K) + "): " + blt_name(s);
-        return SA_ERR_HIP;
+    extern __shared__ __attribute__((aligned(16))) unsigned char qlds[];  // two K-block buffers
+    typedef __attribute__((address_space(1))) uint32_t global_u32;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int id = blockIdx.x, xcd = id % kXcds, j = id / kXcds;
+    const int per_group = kQGroupM * a.n_n;
+    const int64_t mt = ((int64_t)(j / per_group) * kQGroupM + (j % per_group) % kQGroupM) * kXcds + xcd;
+    const int nt = (j % per_group) / kQGroupM;
+    if (mt >= a.n_m) return;
+    const bool w_tile = nt >= a.n_iq_tiles;
+    const int64_t m0 = mt * kQM;
+    const int64_t K = a.K;
+
+    // this wave's rows: waves 0..3 the A rows 64 wave + 8 jl + l / 8, waves 4..7 the B rows 64 (wave - 4) +
+    // 8 jl + l / 8 (jl = 0 .. 7); lane l takes chunk (l % 8) ^ swz(row) of its row.  Rows past M or past
+    // W_w's n_w rows are clamped: loaded but never stored.
+    const uint16_t *gp[kQLoads];
+#pragma unroll
+    for (int jl = 0; jl < kQLoads; ++jl) {
+        const int r = 64 * (wave & 3) + 8 * jl + lane / 8;
+        const int c = (lane & 7) ^ qswz(r);
+        int64_t row;
+        const uint16_t *base;
+        if (wave < 4) {
+            row = m0 + r < a.M ? m0 + r : a.M - 1;
+            base = a.q;
+        } else if (w_tile) {
+            row = r < a.n_w ? r : a.n_w - 1;
+            base = a.w_w;
+        } else {
+            row = (int64_t)nt * kQN + r;
+            base = a.w_iq;
+        }
+        gp[jl] = base + row * K + 8 * c;
     }
-    return SA_OK;
+    // staged rows: load jl of a block goes to stg[jl] and from there to LDS bytes 1024 jl + 16 l of the wave's
+    // 8 KB of the block's buffer (position l % 8 of row 8 jl + l / 8 of the wave's 64)
+    uint4 stg[kQLoads];
+    unsigned char *const dst0 = qlds + (wave < 4 ? 0 : kQPanelBytes) + 8192 * (wave & 3) + 16 * lane;
+    auto load = [&](int kb, int jl) { stg[jl] = load16(gp[jl] + (int64_t)kb * kQK); };
+    auto store = [&](int jl, int buf) {
+        *reinterpret_cast<uint4 *>(dst0 + buf * kQBufBytes + 1024 * jl) = stg[jl];
+    };
+
+    const int wm = wave >> 2, wn = wave & 3;
+    // operand reads: lane l reads row 32 i + l % 32 of its wave's rows, chunk 2 s + l / 32 of k-step s, which
+    // sits at position (2 s) ^ y with y = (l / 32) ^ swz(l % 32)
+    const int y = (lane >> 5) ^ qswz(lane & 31);
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(qlds) + 128u * (lane & 31);
+    uint32_t ra0[4], rb0[4];  // buffer-0 addresses of k-steps 0..3
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+        const uint32_t c = (uint32_t)(((2 * s2) ^ y) << 4);
+        ra0[s2] = lds0 + 16384u * wm + c;
+        rb0[s2] = lds0 + kQPanelBytes + 8192u * wn + c;
+    }
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 2; ++jn) acc[i][jn] = f32x16{};
+
+    // fragments of one k-step: A rows 32 i + l % 32 (i = 0..3), B rows 32 jn + l % 32 (jn = 0..1)
+    auto read_step = [&](int kb, int s2, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+        const uint32_t off = (uint32_t)((kb & 1) * kQBufBytes);
+        const uint32_t pa = ra0[s2] + off, pb = rb0[s2] + off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fa[i]) : "v"(pa), "i"(4096 * i) : "memory");
+#pragma unroll
+        for (int i = 0; i < 2; ++i) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(fb[i]) : "v"(pb), "i"(4096 * i) : "memory");
+    };
+    auto wait_lds = [](int n, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {  // n: 6 or 0 reads may stay in flight
+        if (n == 6)
+            asm volatile("s_waitcnt lgkmcnt(6)"
+                         : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1])
+                         :
+                         : "memory");
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1])
+                         :
+                         : "memory");
+    };
+    // the 8 products of one k-step, with the stores of staged group sg (rows jl = 2 sg, 2 sg + 1) to buffer buf
+    // after products 0 and 1 and the loads of group lg of block kb into the same registers after products 2
+    // and 3 (lg != sg)
+    auto step = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[2], int sg, int buf, int lg, int kb) {
+        __builtin_amdgcn_s_setprio(1);  // the SIMD's other wave, waiting on LDS or memory, issues second
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jn = 0; jn < 2; ++jn) {
+                const int n = 2 * i + jn;
+                acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jn], acc[i][jn], 0, 0, 0);
+                if (n < 2)
+                    store(2 * sg + n, buf);
+                else if (n < 4)
+                    load(kb, 2 * lg + n - 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    const int n_kb = a.K / kQK;
+    // The staging registers are a ring of four groups of two loads: group g of a block is loaded at k-step g
+    // and stored three k-steps later, so each k-step of block kb stores one group of block kb + 1 (k-steps
+    // 0..2: groups 1..3) or of block kb + 2 (k-step 3: group 0, into the buffer the barrier has just freed)
+    // and loads group g of block kb + 2.  At the start of iteration kb buffer kb % 2 holds block kb and buffer
+    // (kb + 1) % 2 group 0 of block kb + 1, its groups 1..3 staged.  Past the end the loads repeat the last
+    // block (stored to a free buffer, never used), so the loop has no branch.
+    auto last = [&](int kb) { return kb < n_kb ? kb : n_kb - 1; };
+#pragma unroll
+    for (int jl = 0; jl < kQLoads; ++jl) load(0, jl);
+#pragma unroll
+    for (int jl = 0; jl < kQLoads; ++jl) store(jl, 0);
+#pragma unroll
+    for (int jl = 0; jl < kQLoads; ++jl) load(last(1), jl);
+#pragma unroll
+    for (int jl = 0; jl < 2; ++jl) store(jl, 1);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    bf16x8 f0a[4], f0b[2], f1a[4], f1b[2];
+    read_step(0, 0, f0a, f0b);
+#pragma unroll 1
+    for (int kb = 0; kb < n_kb; ++kb) {
+        const int nb = (kb + 1) & 1, kl = last(kb + 2);
+        read_step(kb, 1, f1a, f1b);
+        wait_lds(6, f0a, f0b);
+        step(f0a, f0b, 1, nb, 0, kl);
+        read_step(kb, 2, f0a, f0b);
+        wait_lds(6, f1a, f1b);
+        step(f1a, f1b, 2, nb, 1, kl);
+        read_step(kb, 3, f1a, f1b);
+        wait_lds(6, f0a, f0b);
+        step(f0a, f0b, 3, nb, 2, kl);
+        // every wave's reads of block kb and stores of block kb + 1 are done: after the barrier block kb + 1 is
+        // read and buffer kb % 2 takes block kb + 2
+        wait_lds(0, f1a, f1b);
+        asm volatile("s_barrier" ::: "memory");
+        read_step(last(kb + 1), 0, f0a, f0b);
+        step(f1a, f1b, 0, kb & 1, 3, kl);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+    // register r of lane l in accumulator (i, jn): row 128 wm + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column
+    // 64 wn + 32 jn + l % 32 of the tile
+    const bool odd = lane & 1;
+    const int64_t rbase = m0 + 128 * wm + 4 * (lane / 32);
+    if (!w_tile) {
+        // bf16: neighbouring lanes swap one of two consecutive rows, so that each lane stores two adjacent
+        // columns of one row as one 4-byte store
+        const int64_t col0 = (int64_t)nt * kQN + 64 * wn + (lane % 32 & ~1);
+        const int64_t ldo = (int64_t)a.n_iq_tiles * kQN;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int64_t row = rbase + 32 * i + 8 * (r / 4) + r % 4 + (odd ? 1 : 0);
+#pragma unroll
+                for (int jn = 0; jn < 2; ++jn) {
+                    const float give = odd ? acc[i][jn][r] : acc[i][jn][r + 1];
+                    const float got = __builtin_bit_cast(
+                        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, give), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+                    const float d0 = odd ? got : acc[i][jn][r], d1 = odd ? acc[i][jn][r + 1] : got;
+                    const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)d0) |
+                                       ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)d1) << 16);
+                    if (row < a.M) *(global_u32 *)(a.q_idx + row * ldo + col0 + 32 * jn) = v;
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = rbase + 32 * i + 8 * (r / 4) + r % 4;
+#pragma unroll
+                for (int jn = 0; jn < 2; ++jn) {
+                    const int col = 64 * wn + 32 * jn + lane % 32;
+                    if (row < a.M && col < a.n_w) a.w[row * a.n_w + col] = acc[i][jn][r];
+                }
+            }
+    }
 }
 
 }  // namespace
 
-size_t projection_workspace() { return size_t(32) << 20; }
+size_t projection_workspace() { return 0; }
 
 sa_status_t launch_project_q(sa_handle_s &h, const void *q, int64_t L, const void *W_iq, const void *W_w,
                              void *q_idx, float *w, void *ws, size_t ws_bytes, hipStream_t st)
 {
-    BltState *b = static_cast<BltState *>(h.blt);
-    if (!b) {
-        b = new BltState;
-        const hipblasStatus_t s = hipblasLtCreate(&b->lt);
-        if (s != HIPBLAS_STATUS_SUCCESS) {
-            delete b;
-            h.last_error = std::string("hipblasLtCreate: ") + blt_name(s);
-            return SA_ERR_HIP;
-        }
-        h.blt = b;
-    }
+    (void)ws;
+    (void)ws_bytes;
+    // shapes checked by the caller: K a multiple of 64, N1 of 256, n_w <= 256
     const int64_t K = (int64_t)h.cfg.n_heads * h.cfg.d_qk;
-    sa_status_t s = SA_OK;
-    if (W_iq) {
-        KernelTimer timer(h, SA_KERNEL_PROJECT, st);
-        s = gemm_tn(h, b->lt, q, W_iq, q_idx, L, K, (int64_t)h.cfg.n_idx_heads * h.cfg.d_idx, true, ws, ws_bytes, st);
+    const int64_t N1 = W_iq ? (int64_t)h.cfg.n_idx_heads * h.cfg.d_idx : 0;
+    const int n_w = W_w ? h.cfg.n_idx_heads : 0;
+    ProjQArgs a{reinterpret_cast<const uint16_t *>(q), reinterpret_cast<const uint16_t *>(W_iq),
+                reinterpret_cast<const uint16_t *>(W_w), reinterpret_cast<uint16_t *>(q_idx), w, L, (int)K,
+                (int)(N1 / kQN), n_w, (int)(N1 / kQN) + (n_w > 0 ? 1 : 0), (L + kQM - 1) / kQM};
+    // workgroups: per XCD, groups of kQGroupM row tiles times every column tile
+    const int64_t groups = (a.n_m + (int64_t)kQGroupM * kXcds - 1) / ((int64_t)kQGroupM * kXcds);
+    const int64_t grid = groups * kQGroupM * a.n_n * kXcds;
+    if (grid > INT32_MAX) {
+        h.last_error = "too many query rows for one launch";
+        return SA_ERR_UNSUPPORTED;
     }
-    if (s == SA_OK && W_w) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(project_q_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kQLdsBytes);
+    if (e == hipSuccess) {
         KernelTimer timer(h, SA_KERNEL_PROJECT, st);
-        s = gemm_tn(h, b->lt, q, W_w, w, L, K, h.cfg.n_idx_heads, false, ws, ws_bytes, st);
+        hipLaunchKernelGGL(project_q_kernel, dim3((unsigned)grid), dim3(kQThreads), kQLdsBytes, st, a);
+        e = hipGetLastError();
     }
-    return s;
+    if (e != hipSuccess) {
+        h.last_error = std::string("query projection launch: ") + hipGetErrorString(e);
+        return SA_ERR_HIP;
+    }
+    return SA_OK;
 }
 
 hipError_t launch_project_k(sa_handle_s &h, const void *k, int64_t L, const void *W_ik, void *k_idx,
@@ -271,13 +443,6 @@ hipError_t launch_project_k(sa_handle_s &h, const void *k, int64_t L, const void
     }
 }
 
-void destroy_projection_state(sa_handle_s &h)
-{
-    BltState *b = static_cast<BltState *>(h.blt);
-    if (!b) return;
-    if (b->lt) hipblasLtDestroy(b->lt);
-    delete b;
-    h.blt = nullptr;
-}
+void destroy_projection_state(sa_handle_s &h) { (void)h; }
 
 }  // namespace sa

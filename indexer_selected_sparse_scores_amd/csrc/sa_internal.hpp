@@ -19,7 +19,6 @@ struct sa_handle_s {
     bool fast_indexer;      // bf16, H_I = 64, d_I = 128: MFMA indexer kernels
     bool fast_decode;       // fast_indexer with 64-token pages: the paged decode kernels
     bool fast_attn;         // bf16, H = 16, H_kv = 1, d_qk = 576, d_v = 512, v_from_k
-    void *blt = nullptr;    // hipBLASLt state of the query projections (created on first use)
     std::string last_error;
 
     // kernel timing (sparse_attn_profile)

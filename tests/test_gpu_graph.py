@@ -137,3 +137,22 @@ def test_varlen_prefill_replays_from_a_graph():
 
         _replays_match(run, [out, lse, idx])
         assert sa.sparse_attn_check(h) == 0
+
+
+def test_query_projection_replays_from_a_graph():
+    """The query projection is one kernel with no workspace and no library handle, so it captures."""
+    L, K = 777, 16 * 576
+    say(f"graph capture: indexer_project_q, L={L}")
+    g = torch.Generator(device=DEV).manual_seed(44)
+    q = torch.randn((L, K), generator=g, device=DEV).to(torch.bfloat16)
+    W_iq = (torch.randn((8192, K), generator=g, device=DEV) * K ** -0.5).to(torch.bfloat16)
+    W_w = (torch.randn((64, K), generator=g, device=DEV) * K ** -0.5).to(torch.bfloat16)
+    with sa.Handle(inputs.library_config(inputs.WORKLOADS["decode_b64"])) as h:
+        q_idx = torch.empty((L, 8192), device=DEV, dtype=torch.bfloat16)
+        w = torch.empty((L, 64), device=DEV)
+
+        def run():
+            sa.indexer_project_q(h, q, W_iq, W_w, q_idx, w)
+
+        _replays_match(run, [q_idx, w])
+        assert sa.sparse_attn_check(h) == 0

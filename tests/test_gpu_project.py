@@ -60,18 +60,42 @@ def test_project_q_ragged():
     with _handle() as h:
         q_idx = torch.empty((L, 64, 128), dtype=torch.bfloat16, device=DEV)
         w = torch.empty((L, 64), dtype=torch.float32, device=DEV)
-        ws = sa.workspace(h, sa.SA_OP_PROJECT, L)
-        sa.indexer_project_q(h, q, W_iq, W_w, q_idx, w, ws)
+        sa.indexer_project_q(h, q, W_iq, W_w, q_idx, w)
         # the two halves alone give the same results
         q_idx2 = torch.empty_like(q_idx)
         w2 = torch.empty_like(w)
-        sa.indexer_project_q(h, q, W_iq, None, q_idx2, None, ws)
-        sa.indexer_project_q(h, q, None, W_w, None, w2, ws)
+        sa.indexer_project_q(h, q, W_iq, None, q_idx2, None)
+        sa.indexer_project_q(h, q, None, W_w, None, w2)
         assert sa.sparse_attn_check(h) == 0
     x = q.reshape(L, K)
     _check_bf16(q_idx.reshape(L, -1), x, W_iq, "q_idx")
     _check_f32(w, x, W_w, "w")
     assert torch.equal(q_idx, q_idx2) and torch.equal(w, w2)
+
+
+@pytest.mark.parametrize("H,d_qk,H_I,d_I,L", [
+    (1, 64, 2, 128, 1),       # one K block, one column tile, one row
+    (8, 192, 32, 64, 257),    # a ragged row tail past one 256-row tile
+    (4, 128, 256, 32, 70),    # H_I = 256: the weight tile is full
+    (16, 576, 48, 128, 513),  # H_I * d_I = 6144: 24 column tiles, the last row tile ragged
+])
+def test_project_q_shapes(H, d_qk, H_I, d_I, L):
+    g = torch.Generator().manual_seed(26 + L)
+    K, N1 = H * d_qk, H_I * d_I
+    say(f"indexer_project_q H={H} d_qk={d_qk} H_I={H_I} d_I={d_I} L={L}")
+    q = _bf16((L, K), 1.0, g).to(DEV)
+    W_iq = _bf16((N1, K), K ** -0.5, g).to(DEV)
+    W_w = _bf16((H_I, K), K ** -0.5, g).to(DEV)
+    cfg = sa.Config(n_idx_heads=H_I, d_idx=d_I, n_heads=H, d_qk=d_qk, d_v=min(d_qk, 512))
+    with sa.Handle(cfg) as h:
+        # sentinel rows past the end: the kernel writes none of them
+        q_idx = torch.full((L + 3, N1), -9.0, dtype=torch.bfloat16, device=DEV)
+        w = torch.full((L + 3, H_I), -9.0, dtype=torch.float32, device=DEV)
+        sa.indexer_project_q(h, q, W_iq, W_w, q_idx, w)
+        assert sa.sparse_attn_check(h) == 0
+    _check_bf16(q_idx[:L], q, W_iq, "q_idx")
+    _check_f32(w[:L], q, W_w, "w")
+    assert torch.all(q_idx[L:] == -9.0) and torch.all(w[L:] == -9.0)
 
 
 def test_project_k_contiguous_ragged():
@@ -156,7 +180,7 @@ def test_project_q_128k_sampled_rows():
     with _handle() as h:
         q_idx = torch.empty((L, 8192), dtype=torch.bfloat16, device=DEV)
         w = torch.empty((L, 64), dtype=torch.float32, device=DEV)
-        sa.indexer_project_q(h, q, W_iq, W_w, q_idx, w, sa.workspace(h, sa.SA_OP_PROJECT, L))
+        sa.indexer_project_q(h, q, W_iq, W_w, q_idx, w)
         assert sa.sparse_attn_check(h) == 0
     rows = np.unique(np.concatenate([[0, 1, L - 2, L - 1], np.random.default_rng(25).integers(0, L, 12)]))
     r = torch.from_numpy(rows).to(DEV)

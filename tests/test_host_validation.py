@@ -174,12 +174,17 @@ def test_indexer_topk_checks(h):
 
 
 def test_projection_acceptance_checks(h):
-    ws = ws_size(h, sa.SA_OP_PROJECT, 100)
-    assert passed(h, "indexer_project_q", A, 100, A, A, A, A, A, ws, None)
-    assert status(h, "indexer_project_q", M, 100, A, A, A, A, A, ws, None) == sa.SA_ERR_INVALID_ARG
-    assert status(h, "indexer_project_q", A, 100, A, None, A, A, A, ws, None) == sa.SA_ERR_INVALID_ARG  # half a pair
-    assert status(h, "indexer_project_q", A, 100, None, None, None, None, A, ws, None) == sa.SA_ERR_INVALID_ARG
-    assert status(h, "indexer_project_q", A, 100, A, A, A, A, A, ws - 1, None) == sa.SA_ERR_WORKSPACE
+    assert ws_size(h, sa.SA_OP_PROJECT, 100) == 0  # the query projection needs no workspace
+    assert passed(h, "indexer_project_q", A, 100, A, A, A, A, None, 0, None)
+    assert status(h, "indexer_project_q", M, 100, A, A, A, A, None, 0, None) == sa.SA_ERR_INVALID_ARG
+    assert status(h, "indexer_project_q", A, 100, A, None, A, A, None, 0, None) == sa.SA_ERR_INVALID_ARG  # half a pair
+    assert status(h, "indexer_project_q", A, 100, None, None, None, None, None, 0, None) == sa.SA_ERR_INVALID_ARG
+    assert status(h, "indexer_project_q", A, 0, A, A, A, A, None, 0, None) == sa.SA_ERR_INVALID_ARG
+    with sa.Handle(sa.Config(d_idx=96), host_cus=256) as odd:  # H_I * d_I = 6144: a multiple of 256
+        assert passed(odd, "indexer_project_q", A, 100, A, A, A, A, None, 0, None)
+    with sa.Handle(sa.Config(n_idx_heads=3, d_idx=64), host_cus=256) as odd:  # H_I * d_I = 192
+        assert status(odd, "indexer_project_q", A, 100, A, A, A, A, None, 0, None) == sa.SA_ERR_UNSUPPORTED
+        assert "multiple of 256" in sa.sparse_attn_last_error(odd)
     assert passed(h, "indexer_project_k", A, 100, A, A, None, 0, 0, 0, None, None, 0, None)
     assert status(h, "indexer_project_k", A, 100, M, A, None, 0, 0, 0, None, None, 0, None) == sa.SA_ERR_INVALID_ARG
     assert status(h, "indexer_project_k", A, 100, A, A, A, 0, 10, 10, None, None, 0, None) == sa.SA_ERR_INVALID_ARG
