@@ -18,12 +18,13 @@
 //    that is added to the sequence's histogram in global memory, and gathers each wave's 256
 //    scores in LDS for one store at its end.  The scan over index keys is the HBM-bound part
 //    of decode (256 bytes per cached token).
-//  * decode_topk_kernel: one 1024-thread workgroup per sequence.  From the histogram, the bin
-//    b* holding the k_b-th largest score; every score in bins >= b* is appended, in token
-//    order, to a candidate list in LDS (the scores stream in coalesced rounds); the exact
-//    k_b-th key then comes from an MSD radix select and the selection is written in ascending
-//    order.  A sequence whose candidates exceed the LDS list is selected from its full score
-//    row.
+//  * decode_topk_kernel: 1024-thread workgroups, one per 32768-token chunk of a sequence.  From
+//    the histogram, the bin b* holding the k_b-th largest score; every score of the chunk in
+//    bins >= b* is appended, in token order, to a candidate list in LDS (the scores stream in
+//    coalesced rounds).  The chunks' lists meet in the sequence's list in global memory; the
+//    last chunk to finish gathers them in chunk order, takes the exact k_b-th key by an MSD
+//    radix select and writes the selection in ascending order.  A sequence whose candidates
+//    exceed the list is selected from its full score row.
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 #include "topk_device.hpp"
@@ -42,6 +43,7 @@ constexpr int kTopkWaves = 16;                      // selection workgroup: one 
 constexpr int kTopkThreads = kTopkWaves * kWave;
 constexpr int kSubRounds = 4;                       // float4 loads per thread per round
 constexpr int kRoundScores = kSubRounds * 4 * kTopkThreads;  // 16384 scores per round
+constexpr int kTopkChunk = 2 * kRoundScores;        // tokens per selection workgroup
 static_assert(kSubRounds * kTopkWaves == kWave, "one (sub-round, wave) count per lane");
 using topk::kBins;
 using topk::kBinShift;
@@ -57,10 +59,13 @@ __device__ __forceinline__ bool decode_row_ok(const int32_t *ctx_len, const int3
     return true;
 }
 
-__global__ void decode_reset_kernel(uint32_t *hist, int64_t B)
+// clears the histograms and the selection's sync words (a kernel, not a memset, so that a captured graph
+// replays it)
+__global__ void decode_reset_kernel(uint32_t *hist, uint32_t *sync, int64_t B)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < B * kBins) hist[i] = 0;
+    if (i < 2 * B) sync[i] = 0;
 }
 
 // q (as MFMA A fragments) and the head weights of the workgroup's sequence live in LDS, so a wave holds
@@ -205,16 +210,30 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
     }
 }
 
-// One workgroup per sequence: the threshold bin b* from the sequence's histogram, then every score
-// in bins >= b* appended to an LDS list in token order, then the exact selection of the m largest.
-// The scores stream in rounds of 16384 (4 coalesced float4 loads per thread, two more rounds in
-// flight while one is compacted); one barrier per round orders the candidates:
-// sub-round u of a round covers 4096 consecutive tokens in thread order, and the per-(sub-round,
-// wave) counts published in LDS give each wave its offset.  A sequence whose candidates exceed the
-// LDS list is selected from its full score row.
+// Where the chunks of one sequence meet: the sequence's candidate list ([B, kCap] keys and indices), each
+// chunk's (offset, count) in it, and per sequence the list's fill and the number of chunks done.
+struct TopkMeet {
+    uint32_t *keys;
+    int32_t *idx;
+    int32_t *info;  // [B, n_chunks, 2]
+    uint32_t *sync;  // [B, 2], zero at launch
+    int64_t n_chunks;
+};
+
+// Workgroup (c, b): tokens [32768 c, 32768 (c + 1)) of sequence b.  The threshold bin b* from the sequence's
+// histogram, then every score of the chunk in bins >= b* appended to an LDS list in token order.  The scores
+// stream in rounds of 16384 (4 coalesced float4 loads per thread, the chunk's second round in flight while
+// the first is compacted); one barrier per round orders the candidates: sub-round u of a round covers 4096
+// consecutive tokens in thread order, and the per-(sub-round, wave) counts published in LDS give each wave
+// its offset.  A sequence of one chunk selects from its LDS list at once.  Otherwise each chunk reserves a
+// stretch of the sequence's global list (atomic add on its fill) and copies its candidates there; the last
+// chunk to arrive (its arrival count is a release / acquire at device scope, which the XCDs' separate L2s
+// need) gathers the stretches in chunk order, so the list is in token order as one workgroup would have
+// built it, and selects.  A sequence whose candidates exceed kCap is selected from its full score row by
+// its first chunk alone.
 __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ ctx_len, int32_t max_ctx,
-    const int32_t *__restrict__ topk_b, int32_t max_topk, const uint32_t *__restrict__ hist_g,
+    const int32_t *__restrict__ topk_b, int32_t max_topk, const uint32_t *__restrict__ hist_g, TopkMeet meet,
     int32_t *__restrict__ idx, uint32_t *err)
 {
     __shared__ uint32_t ck[kCap];
@@ -222,39 +241,42 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
     __shared__ topk::SelectShared<kTopkWaves> sh;
     __shared__ int counts[2][kSubRounds][kTopkWaves];
     __shared__ int info[3];
+    __shared__ int meet_sh[2];
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-    const int64_t b = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int c = blockIdx.x;
     int32_t *dst = idx + b * max_topk;
     int64_t n, m;
     if (!decode_row_ok(ctx_len, topk_b, max_ctx, max_topk, b, &n, &m)) {
-        if (tid == 0) flag_error(err, SA_DEVERR_TOPK);
-        for (int i = tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
+        if (c == 0) {
+            if (tid == 0) flag_error(err, SA_DEVERR_TOPK);
+            for (int i = tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
+        }
         return;
     }
     if (m == n) {  // every visible token is selected
-        for (int i = tid; i < max_topk; i += kTopkThreads) dst[i] = i < n ? i : -1;
+        if (c == 0)
+            for (int i = tid; i < max_topk; i += kTopkThreads) dst[i] = i < n ? i : -1;
         return;
     }
-    const float *row = scores + b * ld;
-
-    // Sub-round u of the round at `base`: thread t holds tokens base + 4096 u + 4 t .. +3.  Three
-    // rounds are in flight in three register buffers (the round loop is unrolled by three, so no
-    // buffer is copied).  Every load is issued, also past the row's end (it then reads the row's
-    // first 16 bytes, never used): a fixed number of loads in flight lets each round wait for its own.
     const int32_t n32 = (int32_t)n;  // n <= max_ctx < 2^31
-    float4 v0[kSubRounds], v1[kSubRounds], v2[kSubRounds];
+    const int n_chunks = (n32 + kTopkChunk - 1) / kTopkChunk;
+    if (c >= n_chunks) return;
+    const float *row = scores + b * ld;
+    const int32_t c0 = c * kTopkChunk, c1 = c0 + kTopkChunk < n32 ? c0 + kTopkChunk : n32;
+
+    // Sub-round u of the round at `base`: thread t holds tokens base + 4096 u + 4 t .. +3.  Every load is
+    // issued, also past the chunk's end (it then reads the chunk's first 16 bytes, never used).
+    float4 v0[kSubRounds], v1[kSubRounds];
     auto load_round = [&](float4 (&v)[kSubRounds], int32_t base) {
-        int t = tid;  // recomputed per call rather than held in registers
-        asm volatile("" : "+v"(t));
 #pragma unroll
         for (int u = 0; u < kSubRounds; ++u) {
-            const int32_t p = base + u * 4 * kTopkThreads + 4 * t;
-            v[u] = *reinterpret_cast<const float4 *>(row + (p < n32 ? p : 0));
+            const int32_t p = base + u * 4 * kTopkThreads + 4 * tid;
+            v[u] = *reinterpret_cast<const float4 *>(row + (p < c1 ? p : c0));
         }
     };
-    load_round(v0, 0);  // in flight while wave 0 finds the threshold bin
-    load_round(v1, kRoundScores);
-    load_round(v2, 2 * kRoundScores);
+    load_round(v0, c0);  // in flight while wave 0 finds the threshold bin
+    load_round(v1, c0 + kRoundScores);
     if (tid < kWave) {
         int above, upto;
         const int bin = topk::threshold_bin(hist_g + b * kBins, (int)m, &above, &upto);
@@ -267,8 +289,10 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
     __syncthreads();
     const int bin = info[0], above = info[1], upto = info[2];
     if (upto > kCap) {
-        topk::select_and_emit(sh, topk::GlobalScores{row}, (int)n, bin, above, (int)m, dst);
-        for (int i = (int)m + tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
+        if (c == 0) {
+            topk::select_and_emit(sh, topk::GlobalScores{row}, (int)n, bin, above, (int)m, dst);
+            for (int i = (int)m + tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
+        }
         return;
     }
 
@@ -290,7 +314,7 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
     // append the candidates of the round at `base` (held in v)
     auto compact_round = [&](const float4 (&v)[kSubRounds], int32_t base) {
         const int par = rnd & 1;
-        const bool tail = base + kRoundScores > n32;  // uniform: only then may tokens lie past n
+        const bool tail = base + kRoundScores > c1;  // uniform: only then may tokens lie past the chunk
         uint32_t selm = 0;  // bit 4 u + i: token base + 4096 u + 4 tid + i is a candidate
 #pragma unroll
         for (int u = 0; u < kSubRounds; ++u) {
@@ -300,22 +324,21 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bool pass = (w[i] ^ X) >= Y;
-                if (tail) pass = pass && p + i < n32;
+                if (tail) pass = pass && p + i < c1;
                 selm |= (pass ? 1u : 0u) << (4 * u + i);
             }
         }
         int pre[kSubRounds];  // candidates of sub-round u in this wave's lower lanes
 #pragma unroll
         for (int u = 0; u < kSubRounds; ++u) {
-            const int c = __popc((selm >> (4 * u)) & 0xFu);
-            const int incl = topk::wave_incl_scan(c);
-            pre[u] = incl - c;
+            const int cnt = __popc((selm >> (4 * u)) & 0xFu);
+            const int incl = topk::wave_incl_scan(cnt);
+            pre[u] = incl - cnt;
             if (lane == kWave - 1) counts[par][u][wave] = incl;
         }
         __syncthreads();
         // Offsets in (sub-round, wave) order: lane l of every wave takes the count of sub-round l / 16,
-        // wave l % 16, and one scan over the wave gives all 64 offsets.  counts[par] is rewritten two
-        // rounds later, after the next round's barrier, which every reader here has passed.
+        // wave l % 16, and one scan over the wave gives all 64 offsets.
         const int cl = counts[par][lane / kTopkWaves][lane % kTopkWaves];
         const int cincl = topk::wave_incl_scan(cl);
         const int cexcl = cincl - cl;
@@ -341,18 +364,56 @@ __global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(
         total += __builtin_amdgcn_readlane(cincl, kWave - 1);
         ++rnd;
     };
-    for (int32_t base = 0; base < n32; base += 3 * kRoundScores) {
-        compact_round(v0, base);
-        load_round(v0, base + 3 * kRoundScores);
-        if (base + kRoundScores >= n32) break;
-        compact_round(v1, base + kRoundScores);
-        load_round(v1, base + 4 * kRoundScores);
-        if (base + 2 * kRoundScores >= n32) break;
-        compact_round(v2, base + 2 * kRoundScores);
-        load_round(v2, base + 5 * kRoundScores);
-    }
+    compact_round(v0, c0);
+    if (c0 + kRoundScores < c1) compact_round(v1, c0 + kRoundScores);
     __syncthreads();
-    topk::select_and_emit_inline(sh, topk::LdsCands{ck, ci}, total < kCap ? total : kCap, bin, above, (int)m, dst);
+    if (total > kCap) total = kCap;  // not reached: the chunks' candidates add up to at most upto <= kCap
+
+    if (n_chunks > 1) {
+        uint32_t *fill = meet.sync + 2 * b, *arrived = fill + 1;
+        int32_t *cinfo = meet.info + 2 * (b * meet.n_chunks);
+        uint32_t *gk = meet.keys + b * kCap;
+        int32_t *gi = meet.idx + b * kCap;
+        if (tid == 0) {
+            const int off = (int)atomicAdd(fill, (uint32_t)total);
+            cinfo[2 * c] = off;
+            cinfo[2 * c + 1] = total;
+            meet_sh[0] = off;
+        }
+        __syncthreads();
+        const int off = meet_sh[0];
+        for (int i = tid; i < total && off + i < kCap; i += kTopkThreads) {
+            gk[off + i] = ck[i];
+            gi[off + i] = ci[i];
+        }
+        // The barrier orders every wave's stores before thread 0's arrival; the arrival is a release (this
+        // workgroup's list and info, device-wide) and an acquire (every earlier chunk's), made once for the
+        // workgroup: the cache write-back and invalidation it implies are cache-wide, not per wave.
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t before =
+                __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            meet_sh[1] = before == (uint32_t)(n_chunks - 1);
+        }
+        __syncthreads();
+        if (!meet_sh[1]) return;
+        total = 0;
+        for (int cc = 0; cc < n_chunks; ++cc) {
+            const int o = cinfo[2 * cc], k = cinfo[2 * cc + 1];
+            for (int i = tid; i < k && total + i < kCap && o + i < kCap; i += kTopkThreads) {
+                ck[total + i] = gk[o + i];
+                ci[total + i] = gi[o + i];
+            }
+            total += k;
+        }
+        if (total > kCap) total = kCap;
+        if (tid == 0) {  // ready for the next call (the reset kernel clears them too)
+            *fill = 0;
+            *arrived = 0;
+        }
+        __syncthreads();
+    }
+    topk::select_and_emit_inline(sh, topk::LdsCands{ck, ci}, total, bin, above, (int)m, dst);
     for (int i = (int)m + tid; i < max_topk; i += kTopkThreads) dst[i] = -1;
 }
 
@@ -372,6 +433,11 @@ DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx)
     l.hist = take((size_t)B * kBins * sizeof(uint32_t));
     l.pmax_ld = l.ld / kPage;
     l.pmax = take((size_t)B * l.pmax_ld * sizeof(uint32_t));
+    l.n_chunks = (max_ctx + kTopkChunk - 1) / kTopkChunk;
+    l.cand_keys = take((size_t)B * kCap * sizeof(uint32_t));
+    l.cand_idx = take((size_t)B * kCap * sizeof(int32_t));
+    l.chunk_info = take((size_t)B * l.n_chunks * 2 * sizeof(int32_t));
+    l.sync = take((size_t)B * 2 * sizeof(uint32_t));
     l.total = at;
     return l;
 }
@@ -389,7 +455,7 @@ hipError_t launch_decode_indexer(sa_handle_s &h, const void *q_idx, const float 
     {
         const int64_t nz = (int64_t)B * kBins;
         hipLaunchKernelGGL(decode_reset_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist,
-                           (int64_t)B);
+                           reinterpret_cast<uint32_t *>(base + l.sync), (int64_t)B);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -424,9 +490,12 @@ hipError_t launch_decode_topk(sa_handle_s &h, const int32_t *ctx_len, const int3
     char *base = reinterpret_cast<char *>(ws);
     const float *scores = reinterpret_cast<const float *>(base + l.scores);
     const uint32_t *hist = reinterpret_cast<const uint32_t *>(base + l.hist);
+    const TopkMeet meet{reinterpret_cast<uint32_t *>(base + l.cand_keys), reinterpret_cast<int32_t *>(base + l.cand_idx),
+                        reinterpret_cast<int32_t *>(base + l.chunk_info), reinterpret_cast<uint32_t *>(base + l.sync),
+                        l.n_chunks};
     KernelTimer timer(h, SA_KERNEL_TOPK, st);
-    hipLaunchKernelGGL(decode_topk_kernel, dim3((unsigned)B), dim3(kTopkThreads), 0, st, scores, l.ld, ctx_len,
-                       max_ctx, topk_b, max_topk, hist, idx, h.d_err);
+    hipLaunchKernelGGL(decode_topk_kernel, dim3((unsigned)l.n_chunks, (unsigned)B), dim3(kTopkThreads), 0, st,
+                       scores, l.ld, ctx_len, max_ctx, topk_b, max_topk, hist, meet, idx, h.d_err);
     return hipGetLastError();
 }
 

@@ -159,7 +159,10 @@ hipError_t launch_prefill_varlen(sa_handle_s &h, const void *q_idx, const float 
 struct DecodeTopkLayout {
     int64_t ld;          // score row stride (floats)
     int64_t pmax_ld;     // page-maxima row stride (uint32 order keys, one per 64-token page)
-    size_t scores, hist, pmax, total;  // byte offsets in the workspace
+    int64_t n_chunks;    // top-k workgroups per sequence (token chunks)
+    // byte offsets in the workspace: scores, histograms, page maxima, the per-sequence candidate lists
+    // (keys, indices), each chunk's (offset, count) in them, two sync words per sequence (list fill, arrivals)
+    size_t scores, hist, pmax, cand_keys, cand_idx, chunk_info, sync, total;
 };
 DecodeTopkLayout decode_topk_layout(int64_t B, int64_t max_ctx);
 // idx [B, max_topk] gets each sequence's selection; ws holds decode_topk_layout(B, max_ctx).total
