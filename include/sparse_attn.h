@@ -251,7 +251,7 @@ sa_status_t sparse_attn_decode_blocks(sa_handle_t h, const void *q, const void *
  * threads at once) race and give undefined results; serialise them.
  * Errors: those of sparse_attn_decode; SA_ERR_UNSUPPORTED when the step needs more than the array holds
  * (sparse_attn_workspace_size(SA_OP_DECODE, B, max_ctx) > 64 MiB; B = 64 at max_ctx = 131072 with
- * max_topk = 2048 needs about 44 MB). */
+ * max_topk = 2048 needs about 48 MB). */
 sa_status_t sparse_attn_decode_noalloc(sa_handle_t h, const void *q, const void *q_idx, const float *w,
                                        const void *kv_pages, const void *v_pages, const void *kidx_pages,
                                        int64_t n_pages, const int32_t *block_table, int32_t max_blocks,
