@@ -19,11 +19,11 @@
 //  * Epilogue in registers: each lane holds 16 head rows of one key column per 32x32 tile;
 //    ReLU, the weight and the head sum run in-lane, one v_permlane32_swap finishes the head
 //    sum and leaves lane l with the score of key tile_base + l.
-//  * Streaming top-k: every score bumps a per-row 2048-bin LDS histogram of its order-
-//    preserving key's top 11 bits.  From it the wave keeps a running threshold bin: once m
-//    scores lie in bins >= b, no score in a lower bin can be selected.  Only scores in bins
-//    >= the running threshold are appended (ballot-compacted, in key order) to the row's
-//    candidate list in the workspace -- about m (1 + ln(t/m)) of the t+1 scores.
+//  * Streaming top-k: a per-row 2048-bin LDS histogram of the order-preserving keys' top 11
+//    bits gives the wave a running threshold bin: once m scores lie in bins >= b, no score in a
+//    lower bin can be selected.  Only scores in bins >= the running threshold are counted and
+//    appended (ballot-compacted, in key order) to the row's candidate list in the workspace --
+//    about m (1 + ln(t/m)) of the t+1 scores.
 //  * Query rows may be a chunk of a longer sequence (positions pos0 ..), and the keys may come from
 //    the 64-token pages of the sequence's block-table row: a key tile is then one page, whose pool
 //    page is looked up once per row tile and kept in LDS (chunked prefill against a paged cache).
@@ -301,16 +301,22 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                     prev_hi = m_hi;
                     return;
                 }
+                // Only scores in bins >= the running threshold are counted and kept: the final threshold bin
+                // is never below it (the threshold only rises, each time to a bin that at least m counted
+                // scores reach), so the counts of every bin at or above the final one stay exact.  Late in a
+                // long row most windows keep nothing and skip the LDS atomic altogether.
                 const uint32_t key = order_key(score);
-                atomicAdd(&hist[key >> kBinShift], vis ? 1u : 0u);
                 const bool keep = vis && (int)(key >> kBinShift) >= run_bin;
                 const uint64_t ballot = __ballot(keep);
-                if (keep) {
-                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
-                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
-                    my_cands[n_cand + rank] = make_uint2(key, s);
+                if (ballot) {
+                    if (keep) {
+                        atomicAdd(&hist[key >> kBinShift], 1u);
+                        const int rank = (int)__builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(ballot >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
+                        my_cands[n_cand + rank] = make_uint2(key, s);
+                    }
+                    n_cand += __popcll(ballot);
                 }
-                n_cand += __popcll(ballot);
             };
 
             // B fragment ring: slot i % kRing holds k-step i of the tile being multiplied
@@ -328,9 +334,12 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             // tile store and window finish while the other wave of its SIMD still multiplies.
 #pragma unroll 1
             for (int kt = 0; kt < n_kt; ++kt) {
+                // Tile kt + 2 is loaded and stored on every iteration, past the end as a copy of the last
+                // tile into the free buffer (never read): without a branch around them the compiler sees
+                // each load waited for at its store and puts no wait at the loop's head, where it would
+                // also wait for the previous window's candidate store to complete.
                 uint4 nxt[kTileLoads];
-                const bool more = kt + 2 < n_kt;
-                if (more) load_tile(kt + 2, nxt);
+                load_tile(kt + 2 < n_kt ? kt + 2 : n_kt - 1, nxt);
                 float part_odd = 0.f, p = 0.f;
                 const int cur = kt % kBufs, nb = (kt + 1) % kBufs;
                 const uint4 *kc = sh.keys[cur] + lane;
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 if (selects) steps(std::integral_constant<int, kSteps / 2>{}, std::integral_constant<int, kSteps>{});
                 // the next key tile goes to LDS before any candidate store is issued: its wait
                 // for the key loads must not also wait for a store
-                if (more) store_tile((kt + 2) % kBufs, nxt);
+                store_tile((kt + 2) % kBufs, nxt);
                 if (selects) {
                     // window: odd half-tile of tile kt - 1 and even half-tile of tile kt
                     finish_window(part_odd, p, (uint32_t)kt * kKT + lane);
