@@ -123,6 +123,186 @@ __device__ __forceinline__ void step_pattern()
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
 }
 
+// Selection of one row from its candidate list (nl entries of (order key, index) in index order, every
+// score in bins >= `bin` among them, upto <= kCap of those) by the whole workgroup, with the LDS of the
+// key tiles as scratch (the tiles are not in use between row tiles):
+//  * gather: the list streams in rounds of 4096 entries (entry base + 512 u + thread, u = 0..7: every
+//    load instruction reads 512 contiguous bytes), two rounds in flight; the entries in bins >= bin go
+//    to LDS in index order -- per round, the per-(u, wave) counts published in LDS give every wave its
+//    offsets with one scan over 64 lanes -- and those in bin `bin` itself count their next 11 key bits
+//    (bits 20..10) in a 2048-bin histogram;
+//  * from it one wave finds the 11-bit digit holding the (m - above)-th largest key of the bin, a
+//    second pass over the gathered keys counts the last 10 bits of those with that digit, and one wave
+//    finds the exact key tau of the m-th largest score;
+//  * ordered emit: every key > tau and the first `need` keys == tau in index order, in rounds of 4096
+//    gathered entries with the same (u, wave) offsets.
+struct RowSelScratch {
+    uint32_t hist[kBins];
+    int counts[2][8][kRows];  // per round parity: entries kept per (u, wave)
+    int eq[2][8][kRows];      // emit: keys == tau per (u, wave)
+    int digit, need;
+};
+
+typedef __attribute__((address_space(3))) RowSelScratch lds_sel_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(1))) const uint64_t glb_cu64;  // a (key, index) pair, key in the low word
+typedef __attribute__((address_space(1))) int32_t glb_i32;
+
+// Out of line, with LDS and global pointers named as such: the fused kernel's tile loop keeps its whole
+// register budget (inlined, this code made the allocator spill a pointer the loop reloads), and the
+// accesses stay LDS and global instructions.
+__device__ __noinline__ void select_row_lds(lds_sel_t *ss, lds_u32 *ck, lds_i32 *ci, glb_cu64 *list, int nl,
+                                            int bin, int above, int m, glb_i32 *dst)
+{
+    static_assert(kRows * 8 == kWave, "one lane per (u, wave) count");
+    constexpr int kU = 8;                    // entries per thread per round
+    constexpr int kRound = kU * kThreads;    // 4096
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const uint32_t lo = (uint32_t)bin << kBinShift;
+    auto lds_inc = [](lds_u32 *p) { __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
+    // offsets of (u, wave) from the counts of one round: exclusive scan in (u, wave) order
+    auto offsets = [&](const __attribute__((address_space(3))) int (*cnt)[kRows], int &excl, int &total) {
+        const int cl = cnt[lane >> 3][lane & 7];
+        const int incl = topk::wave_incl_scan(cl);
+        excl = incl - cl;
+        total = __builtin_amdgcn_readlane(incl, kWave - 1);
+    };
+
+    for (int i = tid; i < kBins; i += kThreads) ss->hist[i] = 0;
+    __syncthreads();
+    uint2 v0[kU], v1[kU];
+    auto load_round = [&](uint2 (&v)[kU], int base) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int j = base + u * kThreads + tid;
+            const uint64_t e = list[j < nl ? j : 0];
+            v[u] = make_uint2((uint32_t)e, (uint32_t)(e >> 32));
+        }
+    };
+    int out = 0, rnd = 0;
+    auto gather_round = [&](const uint2 (&v)[kU], int base) {
+        const int par = rnd & 1;
+        uint32_t selm = 0;
+        int pre[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const bool keep = base + u * kThreads + tid < nl && v[u].x >= lo;
+            if (keep && (v[u].x >> kBinShift) == (uint32_t)bin) lds_inc(&ss->hist[(v[u].x >> 10) & (kBins - 1)]);
+            const uint64_t b = __ballot(keep);
+            pre[u] = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            if (lane == 0) ss->counts[par][u][wave] = __popcll(b);
+            selm |= (keep ? 1u : 0u) << u;
+        }
+        __syncthreads();
+        int excl, total;
+        offsets(ss->counts[par], excl, total);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if ((selm >> u) & 1u) {
+                const int pos = out + __builtin_amdgcn_readlane(excl, 8 * u + wave) + pre[u];
+                if (pos < kCap) {
+                    ck[pos] = v[u].x;
+                    ci[pos] = (int32_t)v[u].y;
+                }
+            }
+        out += total;
+        ++rnd;
+    };
+    load_round(v0, 0);
+    if (nl > kRound) load_round(v1, kRound);
+#pragma unroll 1
+    for (int base = 0; base < nl; base += 2 * kRound) {
+        gather_round(v0, base);
+        if (base + 2 * kRound < nl) load_round(v0, base + 2 * kRound);
+        if (base + kRound >= nl) break;
+        gather_round(v1, base + kRound);
+        if (base + 3 * kRound < nl) load_round(v1, base + 3 * kRound);
+    }
+    const int n = out < kCap ? out : kCap;  // == upto
+
+    // bits 20..10 of the m-th key (the histogram is complete: every atomic precedes a round's barrier)
+    const int need0 = m - above;  // >= 1 keys of bin `bin` to take
+    if (tid < kWave) {
+        int ab;
+        const int d = topk::threshold_bin((const uint32_t *)ss->hist, need0, &ab, nullptr);
+        if (tid == 0) {
+            ss->digit = d;
+            ss->need = need0 - ab;
+        }
+    }
+    __syncthreads();
+    const uint32_t d1 = (uint32_t)ss->digit;
+    const int need1 = ss->need;
+    __syncthreads();  // every wave has read the digit before the histogram is cleared
+    for (int i = tid; i < kBins; i += kThreads) ss->hist[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = ((uint32_t)bin << 11) | d1;  // key >> 10 of the keys still in play
+    for (int j = tid; j < n; j += kThreads) {
+        const uint32_t key = ck[j];
+        if ((key >> 10) == prefix) lds_inc(&ss->hist[key & 1023u]);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        int ab;
+        const int d = topk::threshold_bin((const uint32_t *)ss->hist, need1, &ab, nullptr);
+        if (tid == 0) {
+            ss->digit = d;
+            ss->need = need1 - ab;
+        }
+    }
+    __syncthreads();
+    const uint32_t tau = (prefix << 10) | (uint32_t)ss->digit;  // exact key of the m-th largest score
+    const int need = ss->need;                                    // keys == tau to take, lowest indices first
+
+    // ordered emit
+    int eq_before = 0, taken = 0;
+    rnd = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += kRound) {
+        const int par = rnd & 1;
+        uint32_t gtm = 0, eqm = 0;
+        int eq_pre[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int j = base + u * kThreads + tid;
+            const bool in = j < n;
+            const uint32_t key = in ? ck[j] : 0u;
+            const bool gt = in && key > tau, eq = in && key == tau;
+            const uint64_t b = __ballot(eq);
+            eq_pre[u] = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            if (lane == 0) ss->eq[par][u][wave] = __popcll(b);
+            gtm |= (gt ? 1u : 0u) << u;
+            eqm |= (eq ? 1u : 0u) << u;
+        }
+        __syncthreads();
+        int eq_excl, eq_total;
+        offsets(ss->eq[par], eq_excl, eq_total);
+        uint32_t take = gtm;
+        int pre[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int rank = eq_before + __builtin_amdgcn_readlane(eq_excl, 8 * u + wave) + eq_pre[u];
+            if (((eqm >> u) & 1u) && rank < need) take |= 1u << u;
+            const uint64_t b = __ballot((take >> u) & 1u);
+            pre[u] = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            if (lane == 0) ss->counts[par][u][wave] = __popcll(b);
+        }
+        __syncthreads();
+        int t_excl, t_total;
+        offsets(ss->counts[par], t_excl, t_total);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if ((take >> u) & 1u) {
+                const int pos = taken + __builtin_amdgcn_readlane(t_excl, 8 * u + wave) + pre[u];
+                if (pos < m) dst[pos] = ci[base + u * kThreads + tid];
+            }
+        eq_before += eq_total;
+        taken += t_total;
+        ++rnd;
+    }
+}
+
 // Block keys instead of a selection (the first pass of the two-tier selection): for every row that has
 // more than `need` visible keys, the order key of the best visible score of each 64-key tile it sees.
 struct BlockKeysOut {
@@ -422,34 +602,9 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             const uint2 *list = cands + ((int64_t)blockIdx.x * kRows + r) * cand_ld;
             const int nl = sh.info[r][3];
             if (upto <= kCap) {
-                // gather the candidates in bins >= bin into LDS, keeping their order
-                uint32_t *ck = sh.region;
-                int32_t *ci = reinterpret_cast<int32_t *>(sh.region + kCap);
-                const uint32_t lo = (uint32_t)bin << kBinShift;
-                int out_before = 0;
-#pragma unroll 1
-                for (int base = 0; base < nl; base += kThreads * kPerThread) {
-                    const int j0 = base + tid * kPerThread;
-                    uint2 c[kPerThread];
-                    uint32_t sel = 0;
-#pragma unroll
-                    for (int i = 0; i < kPerThread; ++i) {
-                        c[i] = j0 + i < nl ? list[j0 + i] : make_uint2(0u, 0u);
-                        sel |= (j0 + i < nl && c[i].x >= lo ? 1u : 0u) << i;
-                    }
-                    int total;
-                    int pos = topk::block_scan<kRows>(__popc(sel), sh.sel.wave_sums, &total) + out_before;
-#pragma unroll
-                    for (int i = 0; i < kPerThread; ++i)
-                        if ((sel >> i) & 1u) {
-                            ck[pos] = c[i].x;
-                            ci[pos] = (int32_t)c[i].y;
-                            ++pos;
-                        }
-                    out_before += total;
-                }
-                __syncthreads();
-                topk::select_and_emit(sh.sel, topk::LdsCands{ck, ci}, upto, bin, above, mr, dst);
+                static_assert(sizeof(RowSelScratch) <= sizeof(sh.keys), "the selection scratch fits the key tiles");
+                select_row_lds((lds_sel_t *)(void *)&sh.keys[0][0], (lds_u32 *)sh.region, (lds_i32 *)(sh.region + kCap),
+                               (glb_cu64 *)(const void *)list, nl, bin, above, mr, (glb_i32 *)dst);
             } else {
                 topk::select_and_emit(sh.sel, topk::GlobalCands{list}, nl, bin, above, mr, dst);
             }
