@@ -71,17 +71,16 @@ constexpr int kLDv = 512;       // value width (leading columns of the key row)
 constexpr int kChunk = 32;      // selected rows per chunk
 constexpr int kAWaves = 4;
 constexpr int kAThreads = kAWaves * kWave;
-constexpr int kLdsRow = kLDv * 2 + 16;                  // padded LDS row of the value part (bytes)
+constexpr int kLdsRow = kLDqk * 2 + 16;                 // padded LDS row (bytes): 292 dwords, 36 mod 64 banks
 constexpr int kKSteps = kLDqk / 32;                     // 18 k-steps of the logits MFMA
 constexpr int kKHalf = kKSteps / 2;                     // each wave pair takes half of them
 constexpr int kLogitLd = kChunk + 4;                    // padded per-head row of logits (floats)
-constexpr int kVPieces = kLDv / 8;                      // 16-byte pieces of the value part (64)
 constexpr int kColsPerWave = kLDv / kAWaves;            // 128 value columns per wave
 constexpr int kNTiles = kColsPerWave / 16;              // 8 MFMA column tiles per wave
 constexpr int kHeadsPerWave = kLH / kAWaves;            // softmax heads owned by a wave (4)
 
 struct AttnShared {
-    unsigned char vrows[kChunk * kLdsRow];  // value part of the current chunk's rows
+    unsigned char rows[kChunk * kLdsRow];   // the current chunk's selected rows (all 576 columns)
     float logits[2][kLH * kLogitLd];        // partial logits of the two K-halves, [head][slot]
     uint4 p_hi[kLH][4];                     // P as the A operand of P.V: [head][lane group]
     uint4 p_lo[kLH][4];                     //   (8 bf16 each), hi part and bf16 residual
@@ -144,11 +143,12 @@ __device__ __forceinline__ float row16_sum(float x)
 
 // One 4-wave workgroup = one query row (all 16 heads) and a range of its selected rows, in
 // chunks of 32 rows; three workgroups share a compute unit, so one's barriers and memory
-// waits overlap the others' work.  Per chunk:
+// waits overlap the others' work.  The selected rows are gathered whole (eight lanes per row,
+// 128-byte lines), one chunk in flight in registers while the previous one sits in LDS: a
+// gather of whole lines moves more bytes per second through the fabric than one in which each
+// lane fetches only the pieces its own MFMAs use.  Per chunk:
 //  * logits: wave w takes rows 16 (w % 2) .. +15 over half w / 2 of the 576-wide contraction
-//    (v_mfma_f32_16x16x32_bf16, q fragments in registers).  Each thread gathers exactly the
-//    nine 16-byte pieces of K its own MFMAs consume (16-byte loads, one chunk ahead), so the
-//    logits come straight from registers; only the value part of the rows goes through LDS.
+//    (v_mfma_f32_16x16x32_bf16, q fragments in registers, K fragments from LDS).
 //  * online softmax: wave w owns heads 4w .. 4w+3 (running max / sum, exp2 with log2(e)
 //    folded into the scale) and publishes P as bf16 hi + residual (~16 mantissa bits).
 //  * P.V: every wave accumulates 128 of the 512 value columns, with V fragments from
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     const int n_chunks = (int)((j_end - j_begin + kChunk - 1) / kChunk);
 
     const int nt_qk = wave & 1, kh = wave >> 1;
-    const int my_row = 16 * nt_qk + hh;  // the chunk row whose K pieces this lane gathers
+    const int my_row = 16 * nt_qk + hh;  // the chunk row whose logits this lane's MFMA B fragments cover
     bf16x8 qa[kKHalf];
     const uint16_t *qr = q + (r * kLH + hh) * kLDqk;
 #pragma unroll
@@ -192,32 +192,31 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
     }
     __syncthreads();
 
-    // piece i of this thread: 16 bytes at dims 32 (9 kh + i) + 8 grp of row my_row; an unused
-    // slot reads the first row of the source and is zeroed (no branch around the loads)
+    // Gather: eight lanes per selected row, wave w taking rows 8 w .. 8 w + 7 of a chunk; lane l copies
+    // the 16-byte pieces l % 8 + 8 i (i = 0..8) of row 8 w + l / 8, so each load instruction reads whole
+    // 128-byte lines of 8 rows.  An unused slot reads the first row of the source and is zeroed (no
+    // branch around the loads).
+    const int g_row = 8 * wave + lane / 8, g_col = lane % 8;
     uint4 g[kKHalf];
     auto gather = [&](int buf) {
-        const int64_t off = sh.row_off[buf][my_row];
-        const uint16_t *src = kv_base + (off >= 0 ? off : 0) + 32 * kKHalf * kh + 8 * grp;
+        const int64_t off = sh.row_off[buf][g_row];
+        const uint16_t *src = kv_base + (off >= 0 ? off : 0) + 8 * g_col;
 #pragma unroll
-        for (int i = 0; i < kKHalf; ++i) g[i] = load16(src + 32 * i);
+        for (int i = 0; i < kKHalf; ++i) g[i] = load16(src + 64 * i);
         if (off < 0) {
 #pragma unroll
             for (int i = 0; i < kKHalf; ++i) g[i] = make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    // the value part (pieces 0..63 of a row) goes to LDS for P.V
     auto stash = [&]() {
 #pragma unroll
-        for (int i = 0; i < kKHalf; ++i) {
-            const int piece = 4 * (kKHalf * kh + i) + grp;
-            if (piece < kVPieces)
-                *reinterpret_cast<uint4 *>(sh.vrows + my_row * kLdsRow + piece * 16) = g[i];
-        }
+        for (int i = 0; i < kKHalf; ++i)
+            *reinterpret_cast<uint4 *>(sh.rows + g_row * kLdsRow + 16 * (g_col + 8 * i)) = g[i];
     };
     gather(0);
     stash();
-#pragma unroll
-    for (int i = 0; i < kKHalf; ++i) asm volatile("" : : "v"(g[i].x));  // complete before the loop
+    gather(1);
+    __syncthreads();
 
     const float neg_inf = -__builtin_inff();
     // softmax state of head 4 wave + lane / 16 (log2 domain), owned by this wave
@@ -229,9 +228,8 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
 
 #pragma unroll 1
     for (int c = 0; c < n_chunks; ++c) {
-        // vrows = values of chunk c, kf = K pieces of chunk c, row_off[c & 1] = chunk c,
+        // rows = chunk c, g = chunk c + 1 in flight, row_off[c & 1] = chunk c,
         // row_off[(c + 1) & 1] = chunk c + 1
-        const bool more = c + 1 < n_chunks;
         // Slot pend_j (chunk c + 2): its index arrived during the previous chunk; its page
         // lookup and the index of chunk c + 3 are issued before this chunk's gather loads, so
         // the memory counter reaches them first, and they are consumed after the compute.
@@ -255,17 +253,20 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
         pend_s = -1;
         if (tid < kChunk && pend_j < j_end) pend_s = idx_row[pend_j];
 
-        // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh; g holds
-        // this chunk's K pieces until the MFMAs have taken them, then the next chunk's gather
+        // partial logits of rows 16 nt_qk + (0..15), heads 0..15, k-steps of half kh; lane (hh, grp)
+        // reads its B fragments (row my_row, dims 32 (9 kh + i) + 8 grp .. +7) from the chunk in LDS
         {
+            const unsigned char *kb = sh.rows + my_row * kLdsRow + 2 * (32 * kKHalf * kh + 8 * grp);
+            uint4 kf[kKHalf];
+#pragma unroll
+            for (int i = 0; i < kKHalf; ++i) kf[i] = *reinterpret_cast<const uint4 *>(kb + 64 * i);
             f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = {0.f, 0.f, 0.f, 0.f};  // two chains
 #pragma unroll
             for (int i = 0; i < kKHalf; i += 2) {
-                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], as_bf16x8(g[i]), sa0, 0, 0, 0);
+                sa0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], as_bf16x8(kf[i]), sa0, 0, 0, 0);
                 if (i + 1 < kKHalf)
-                    sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i + 1], as_bf16x8(g[i + 1]), sa1, 0, 0, 0);
+                    sa1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i + 1], as_bf16x8(kf[i + 1]), sa1, 0, 0, 0);
             }
-            if (more) gather((c + 1) & 1);
             const f32x4 sacc = sa0 + sa1;
             // output (head 4 grp + i, row my_row)
             const bool valid = sh.row_off[c & 1][my_row] >= 0;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
         {
             const bf16x8 pa_hi = as_bf16x8(sh.p_hi[hh][grp]);
             const bf16x8 pa_lo = as_bf16x8(sh.p_lo[hh][grp]);
-            const unsigned char *vb0 = sh.vrows + (8 * grp + 2 * (hh / 4)) * kLdsRow +
+            const unsigned char *vb0 = sh.rows + (8 * grp + 2 * (hh / 4)) * kLdsRow +
                                        2 * (kColsPerWave * wave + 4 * (hh % 4));
 #pragma unroll
             for (int nt = 0; nt < kNTiles; ++nt) {
@@ -347,14 +348,12 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
             }
         }
         if (tid < kChunk) sh.row_off[c & 1][tid] = off_next;
-        __syncthreads();  // every wave is done with vrows, logits and P; row_off is published
-        // unconditional (after the last chunk it stores values nothing reads), and every piece is
-        // consumed here, so that the gathered pieces are complete at the top of the loop on every
-        // path: the logits MFMAs then wait for nothing, not even for the index and page loads
-        // issued before them
+        __syncthreads();  // every wave is done with rows, logits and P; row_off is published
+        // chunk c + 1 into LDS and chunk c + 2 in flight, both unconditional: past the last chunk
+        // they store values nothing reads and load the source's first row (offsets -1)
         stash();
-#pragma unroll
-        for (int i = 0; i < kKHalf; ++i) asm volatile("" : : "v"(g[i].x));
+        gather(c & 1);
+        __syncthreads();
     }
 
     if (hh == 0) sh.inv_l[sm_head] = l_run > 0.f ? 1.f / l_run : 0.f;
