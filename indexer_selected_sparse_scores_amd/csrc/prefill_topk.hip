@@ -414,12 +414,16 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                     const int32_t pg = __builtin_amdgcn_readfirstlane(sh.pages[kt]);
                     shift = ((int64_t)(pg >= 0 ? pg : 0) - kt) * kKT;
                 }
+                // uniform tile base and 32-bit lane offsets (keys past t_last read key t_last), so the
+                // addressing stays in scalar registers but for one min and one shift-add per load
+                const int64_t k0 = (int64_t)kt * kKT;
+                const unsigned char *tbase = reinterpret_cast<const unsigned char *>(k_idx + (k0 + shift) * kD);
+                const int lim = (int)(t_last - k0 < kKT ? t_last - k0 : kKT);
 #pragma unroll
                 for (int u = 0; u < kTileLoads; ++u) {
                     const int c = tid + u * kThreads;
-                    int64_t s = (int64_t)kt * kKT + chunk_key(c);
-                    if (s > t_last) s = t_last;
-                    v[u] = load16(k_idx + (s + shift) * kD + 8 * chunk_col(c));
+                    const int key = chunk_key(c) < lim ? chunk_key(c) : lim;
+                    v[u] = load16(tbase + (uint32_t)(key * (kD * 2) + 16 * chunk_col(c)));
                 }
             };
             auto store_tile = [&](int buf, const uint4 (&v)[kTileLoads]) {
@@ -440,6 +444,11 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             }
             uint32_t *hist = sh.region + wave * kBins;
             int run_bin = 0;  // running threshold bin: scores in lower bins are dropped
+            // the score at the lower edge of run_bin (NaN for bin 0: every score is kept), so that the
+            // window's test is one float compare, !(score < run_thr) <=> order_key(score) >> kBinShift >=
+            // run_bin for every non-NaN score; a NaN score is kept whatever the bin (harmless: only bins at or
+            // above the final threshold, never below run_bin, are read again)
+            float run_thr = __builtin_nanf("");
 
             // Software pipeline over half-tiles of 32 keys: while the MFMAs of half-tile h run,
             // the VALU applies ReLU, the weights and the in-lane head sum to the accumulators of
@@ -485,11 +494,11 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 // is never below it (the threshold only rises, each time to a bin that at least m counted
                 // scores reach), so the counts of every bin at or above the final one stay exact.  Late in a
                 // long row most windows keep nothing and skip the LDS atomic altogether.
-                const uint32_t key = order_key(score);
-                const bool keep = vis && (int)(key >> kBinShift) >= run_bin;
-                const uint64_t ballot = __ballot(keep);
+                const bool keep = vis && !(score < run_thr);
+                const uint64_t ballot = __builtin_amdgcn_ballot_w64(keep);
                 if (ballot) {
                     if (keep) {
+                        const uint32_t key = order_key(score);
                         atomicAdd(&hist[key >> kBinShift], 1u);
                         const int rank = (int)__builtin_amdgcn_mbcnt_hi(
                             (uint32_t)(ballot >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
@@ -548,9 +557,19 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                         step_pattern();
                     }
                 };
-                if (selects) steps(std::integral_constant<int, 0>{}, std::integral_constant<int, kSteps / 2>{});
+                // The half-tiles' MFMA streams issue at raised priority: the SIMD's other wave, in its tile
+                // store, window finish or selection, then issues second and the matrix pipe stays fed.
+                if (selects) {
+                    __builtin_amdgcn_s_setprio(1);
+                    steps(std::integral_constant<int, 0>{}, std::integral_constant<int, kSteps / 2>{});
+                    __builtin_amdgcn_s_setprio(0);
+                }
                 __syncthreads();  // every wave, selecting or not, passes it once per tile
-                if (selects) steps(std::integral_constant<int, kSteps / 2>{}, std::integral_constant<int, kSteps>{});
+                if (selects) {
+                    __builtin_amdgcn_s_setprio(1);
+                    steps(std::integral_constant<int, kSteps / 2>{}, std::integral_constant<int, kSteps>{});
+                    __builtin_amdgcn_s_setprio(0);
+                }
                 // the next key tile goes to LDS before any candidate store is issued: its wait
                 // for the key loads must not also wait for a store
                 store_tile((kt + 2) % kBufs, nxt);
@@ -559,7 +578,11 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                     finish_window(part_odd, p, (uint32_t)kt * kKT + lane);
                     if (!kBlockKeys && (kt % kRefresh) == kRefresh - 1 && (int64_t)kt * kKT >= m) {
                         const int b = topk::threshold_bin(hist, m, nullptr, nullptr);
-                        if (b > run_bin) run_bin = b;
+                        if (b > run_bin) {
+                            run_bin = b;
+                            const uint32_t k_lo = (uint32_t)b << kBinShift;  // the bin's smallest key
+                            run_thr = __uint_as_float((k_lo & 0x80000000u) ? (k_lo & 0x7FFFFFFFu) : ~k_lo);
+                        }
                     }
                 }
             }
