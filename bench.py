@@ -44,8 +44,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--prefill-len", type=int, default=131072)
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--decode-ctx", type=int, default=131072)
