@@ -52,7 +52,7 @@ constexpr int kRing = 4;            // B fragments in flight per wave
 constexpr int kBufs = 3;            // LDS key tiles
 constexpr int kTileLoads = kKT * 16 / 512;  // 16-byte chunks each thread moves per tile
 constexpr int kChunks = kD * 2 / 16;  // 16-byte chunks per key row (16)
-constexpr int kRefresh = 16;        // key tiles between running-threshold refreshes
+constexpr int kRefresh = 32;        // key tiles between running-threshold refreshes
 static_assert(kSteps % kRing == 0, "ring slots repeat every tile");
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt not waited on
 using topk::kBins;
