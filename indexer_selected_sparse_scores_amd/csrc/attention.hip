@@ -350,9 +350,12 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
         if (tid < kChunk) sh.row_off[c & 1][tid] = off_next;
         __syncthreads();  // every wave is done with rows, logits and P; row_off is published
         // chunk c + 1 into LDS and chunk c + 2 in flight, both unconditional: past the last chunk
-        // they store values nothing reads and load the source's first row (offsets -1)
+        // they store values nothing reads and load the source's first row (offsets -1).  Issued at raised
+        // wave priority, so that the loads leave ahead of the other workgroups' softmax and MFMA work.
+        __builtin_amdgcn_s_setprio(1);
         stash();
         gather(c & 1);
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     }
 
