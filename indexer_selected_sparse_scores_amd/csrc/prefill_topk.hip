@@ -521,8 +521,9 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
             // kt - 1 (so the buffer of tile kt + 2 is free) and stored tile kt + 1 (which the ring
             // starts reading at k-step 12).  A wave that finishes its half-tiles early does its
             // tile store and window finish while the other wave of its SIMD still multiplies.
-#pragma unroll 1
-            for (int kt = 0; kt < n_kt; ++kt) {
+            // The loop runs three tiles per iteration, one per key buffer, so that every LDS address in it is
+            // a register plus an immediate offset.
+            auto tile = [&](int kt, auto cur_c) {
                 // Tile kt + 2 is loaded and stored on every iteration, past the end as a copy of the last
                 // tile into the free buffer (never read): without a branch around them the compiler sees
                 // each load waited for at its store and puts no wait at the loop's head, where it would
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 uint4 nxt[kTileLoads];
                 load_tile(kt + 2 < n_kt ? kt + 2 : n_kt - 1, nxt);
                 float part_odd = 0.f, p = 0.f;
-                const int cur = kt % kBufs, nb = (kt + 1) % kBufs;
+                constexpr int cur = decltype(cur_c)::value, nb = (cur + 1) % kBufs;
                 const uint4 *kc = sh.keys[cur] + lane;
                 const uint4 *kn = sh.keys[nb] + lane;
                 // k-steps [i0, i1) of this tile
@@ -572,7 +573,10 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                 }
                 // the next key tile goes to LDS before any candidate store is issued: its wait
                 // for the key loads must not also wait for a store
-                store_tile((kt + 2) % kBufs, nxt);
+                // kept after the second half's MFMAs: scheduled among them, the store would wait there for
+                // the tile's loads
+                __builtin_amdgcn_sched_barrier(0);
+                store_tile((cur + 2) % kBufs, nxt);
                 if (selects) {
                     // window: odd half-tile of tile kt - 1 and even half-tile of tile kt
                     finish_window(part_odd, p, (uint32_t)kt * kKT + lane);
@@ -585,7 +589,16 @@ __global__ __launch_bounds__(kThreads, 1) void indexer_topk_prefill_kernel(
                         }
                     }
                 }
+            };
+            int kt3 = 0;
+#pragma unroll 1
+            for (; kt3 + kBufs <= n_kt; kt3 += kBufs) {
+                tile(kt3, std::integral_constant<int, 0>{});
+                tile(kt3 + 1, std::integral_constant<int, 1>{});
+                tile(kt3 + 2, std::integral_constant<int, 2>{});
             }
+            if (kt3 < n_kt) tile(kt3, std::integral_constant<int, 0>{});
+            if (kt3 + 1 < n_kt) tile(kt3 + 1, std::integral_constant<int, 1>{});
             if (selects) {  // the odd half of the last tile
                 float p = 0.f;
 #pragma unroll
