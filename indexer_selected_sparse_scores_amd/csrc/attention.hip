@@ -9,10 +9,9 @@
 //
 // attn_latent_mfma_kernel serves the latent layout in prefill (bf16, 16 heads sharing one
 // 576-wide row per token whose first 512 columns are the value).  A 4-wave workgroup walks
-// the selected rows of one query in chunks of 32; each thread gathers with 16-byte loads the
-// pieces of K that its own logits MFMAs consume (the next chunk's pieces in flight while the
-// current one is computed), so every 1152-byte row is read once for all 16 heads and only
-// its value part passes through LDS.  Logits and P.V run on v_mfma_f32_16x16x32_bf16 with
+// the selected rows of one query in chunks of 32, gathered whole with 16-byte loads (eight
+// lanes per row) into LDS, the next chunk in flight while the current one is computed, so
+// every 1152-byte row is read once for all 16 heads.  Logits and P.V run on v_mfma_f32_16x16x32_bf16 with
 // an online softmax (running max / sum per head, exp2 with the log2(e) factor folded into
 // the scale).  P enters the MFMA as a bf16 hi part plus a bf16 residual, so the weights keep
 // ~16 mantissa bits.
@@ -336,7 +335,7 @@ __global__ __launch_bounds__(kAThreads, 3) void attn_latent_mfma_kernel(
             }
         }
         // row_off[c & 1] was last read by this chunk's logits (before the barriers above); it
-        // now takes chunk c + 2, which the next iteration's gather reads after the barrier below.
+        // now takes chunk c + 2, which the gather after the barrier below reads.
         // The page lookup is consumed here on every path, so no wait for it is left pending
         // into the next chunk (where `page` is reset).
         asm volatile("" : : "v"(page));
