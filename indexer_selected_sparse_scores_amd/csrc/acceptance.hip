@@ -13,9 +13,10 @@
 //    over the workgroup; pass 2 streams them again, in reverse order so that the part read last
 //    is still in the caches, and sums min(p, q).  HBM-bound: 8 bytes per vocabulary entry.
 //  * bin_stats_kernel: one workgroup per bin.  The count and the (double) sum of the bin's values
-//    from one scan of the tokens, then the two order statistics around the percentile, each found
-//    exactly by an MSD radix select over the values' order keys (four 8-bit passes, each one scan
-//    of the tokens with a 256-bin LDS histogram), and the linear interpolation between them.
+//    from one scan of the tokens, which also stages their order keys in LDS (up to 8192), then the two
+//    order statistics around the percentile, each found exactly by an MSD radix select over the order
+//    keys (four 8-bit passes with a 256-bin LDS histogram, over the staged keys, or over the tokens
+//    again for a larger bin), and the linear interpolation between them.
 #include <math.h>
 
 #include "sa_device.hpp"
@@ -192,6 +193,58 @@ __device__ float rank_value(const float *__restrict__ alpha, const int32_t *__re
     return key_value(prefix);
 }
 
+// The same from the bin's n <= kBinCap order keys staged in LDS: four 8-bit MSD passes over LDS, each digit found
+// by one wave's prefix scan of the 256-bin histogram.
+constexpr int kBinCap = 8192;
+__device__ float rank_value_lds(const uint32_t *keys, int n, int64_t r, uint32_t *hist, uint32_t *sh_digit,
+                                int64_t *sh_rank)
+{
+    const int tid = threadIdx.x, lane = lane_id();
+    uint32_t prefix = 0, mask = 0;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kBinThreads) {
+            const uint32_t k = keys[i];
+            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l holds digits 4 l .. 4 l + 3; the lane whose counts span rank r names the digit
+            uint32_t c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = hist[4 * lane + j];
+            const uint32_t own = c[0] + c[1] + c[2] + c[3];
+            uint32_t incl = own;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t v = __shfl_up(incl, off);
+                if (lane >= off) incl += v;
+            }
+            int64_t below = (int64_t)(incl - own);
+            if (below <= r && r < (int64_t)incl) {
+                int j = 0;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    if (j == q && below + c[q] <= r) {
+                        below += c[q];
+                        j = q + 1;
+                    }
+                }
+                *sh_digit = (uint32_t)(4 * lane + j);
+                *sh_rank = r - below;
+            }
+        }
+        __syncthreads();
+        prefix |= *sh_digit << shift;
+        mask |= 255u << shift;
+        r = *sh_rank;
+        __syncthreads();
+    }
+    return key_value(prefix);
+}
+
 __global__ __launch_bounds__(kBinThreads) void bin_stats_kernel(const float *__restrict__ alpha,
                                                                 const int32_t *__restrict__ pos, int64_t T,
                                                                 int32_t bin_size, double percentile,
@@ -203,15 +256,22 @@ __global__ __launch_bounds__(kBinThreads) void bin_stats_kernel(const float *__r
     __shared__ int64_t sh_rank;
     __shared__ double sh_sum[kBinThreads / kWave];
     __shared__ int64_t sh_cnt[kBinThreads / kWave];
+    __shared__ uint32_t keys[kBinCap];  // the bin's order keys, in no particular order (up to kBinCap)
+    __shared__ uint32_t sh_staged;
     const int64_t bin = blockIdx.x;
     const int tid = threadIdx.x;
+    if (tid == 0) sh_staged = 0;
+    __syncthreads();
 
     double sum = 0.0;
     int64_t n = 0;
     for (int64_t t = tid; t < T; t += kBinThreads) {
         if (bin_of(pos[t], bin_size) != bin) continue;
-        sum += (double)alpha[t];
+        const float a = alpha[t];
+        sum += (double)a;
         ++n;
+        const uint32_t slot = atomicAdd(&sh_staged, 1u);
+        if (slot < (uint32_t)kBinCap) keys[slot] = order_key(a);
     }
     for (int off = kWave / 2; off > 0; off >>= 1) {
         sum += __shfl_xor(sum, off);
@@ -239,8 +299,14 @@ __global__ __launch_bounds__(kBinThreads) void bin_stats_kernel(const float *__r
     const double h = (double)(n - 1) * percentile / 100.0;
     const int64_t lo = (int64_t)floor(h);
     const int64_t hi = lo + 1 < n ? lo + 1 : n - 1;
-    const float x_lo = rank_value(alpha, pos, T, bin_size, bin, lo, hist, &sh_digit, &sh_rank);
-    const float x_hi = hi == lo ? x_lo : rank_value(alpha, pos, T, bin_size, bin, hi, hist, &sh_digit, &sh_rank);
+    float x_lo, x_hi;
+    if (n <= kBinCap) {  // all of the bin's values are in LDS
+        x_lo = rank_value_lds(keys, (int)n, lo, hist, &sh_digit, &sh_rank);
+        x_hi = hi == lo ? x_lo : rank_value_lds(keys, (int)n, hi, hist, &sh_digit, &sh_rank);
+    } else {
+        x_lo = rank_value(alpha, pos, T, bin_size, bin, lo, hist, &sh_digit, &sh_rank);
+        x_hi = hi == lo ? x_lo : rank_value(alpha, pos, T, bin_size, bin, hi, hist, &sh_digit, &sh_rank);
+    }
     if (tid == 0) {
         count[bin] = (int32_t)n;
         mean[bin] = (float)(sum / (double)n);

@@ -86,11 +86,13 @@ def test_alpha_special_rows():
     assert abs(a[3] - 1.0) <= 1e-5
 
 
-def test_bin_stats_on_given_values():
+@pytest.mark.parametrize("bin_size,n_bins", [(2048, 21), (65536, 2)])
+def test_bin_stats_on_given_values(bin_size, n_bins):
     """On the same fp32 values both sides take the same order statistics: the GPU's statistics are
     the oracle's rounded to fp32 (the mean within its float32 rounding).  Includes empty bins, a
-    single-value bin, ties, negative positions and positions past the last bin."""
-    say("acceptance_bin_stats on given values")
+    single-value bin, ties, negative positions and positions past the last bin; with 65536-position
+    bins the first bin holds ~37000 values, more than the kernel stages on chip (its other path)."""
+    say(f"acceptance_bin_stats on given values, bin_size={bin_size}")
     rng = np.random.default_rng(63)
     T = 40000
     alpha = (1 - rng.beta(0.3, 3, size=T)).astype(np.float32)
@@ -99,17 +101,16 @@ def test_bin_stats_on_given_values():
     pos[(pos >= 4 * 2048) & (pos < 5 * 2048)] = 3 * 2048        # bin 4 empty
     pos[(pos >= 7 * 2048) & (pos < 8 * 2048)] = -5               # bin 7 empty, those tokens ignored
     pos[10] = 7 * 2048 + 3                                        # bin 7: one value
-    pos[11] = 25 * 2048                                           # beyond the bins
-    n_bins = 21
+    pos[11] = 25 * 2048                                           # beyond the bins (of 2048)
     with _handle() as h:
         for pc in (5.0, 0.0, 50.0, 100.0, 37.5):
             count = torch.empty(n_bins, dtype=torch.int32, device=DEV)
             mean = torch.empty(n_bins, dtype=torch.float32, device=DEV)
             pct = torch.empty(n_bins, dtype=torch.float32, device=DEV)
-            sa.acceptance_bin_stats(h, torch.from_numpy(alpha).to(DEV), torch.from_numpy(pos).to(DEV), 2048, n_bins,
-                                    pc, count, mean, pct)
+            sa.acceptance_bin_stats(h, torch.from_numpy(alpha).to(DEV), torch.from_numpy(pos).to(DEV), bin_size,
+                                    n_bins, pc, count, mean, pct)
             assert sa.sparse_attn_check(h) == 0
-            rc, rm, rp = oracle.bin_percentiles(alpha, pos, 2048, n_bins, pc)
+            rc, rm, rp = oracle.bin_percentiles(alpha, pos, bin_size, n_bins, pc)
             np.testing.assert_array_equal(to_np(count), rc)
             gm, gp = to_np(mean), to_np(pct)
             for j in range(n_bins):
