@@ -857,32 +857,43 @@ def measure_acceptance(cfg, args, torch, T=4096, V=151936):
     pct = torch.empty(n_bins, dtype=torch.float32, device=dev)
     log(f"[bench] acceptance rate T={T} V={V}")
     with sa.Handle(cfg) as h:
+        ws = sa.workspace(h, sa.SA_OP_ACCEPT, T, V)  # the single-read path
+
         def run():
-            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha)
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha, ws=ws)
             sa.acceptance_bin_stats(h, alpha, d["pos"], 2048, n_bins, 5.0, count, mean, pct)
 
         run()
         torch.cuda.synchronize()
         sa.sparse_attn_check(h)
         reps = max(1, args.steps)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
         for _ in range(reps):
-            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha)
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha, ws=ws)
         ev[1].record()
         for _ in range(reps):
             sa.acceptance_bin_stats(h, alpha, d["pos"], 2048, n_bins, 5.0, count, mean, pct)
         ev[2].record()
+        alpha2 = torch.empty_like(alpha)
+        for _ in range(reps):
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha2)  # two passes over the logits
+        ev[3].record()
         torch.cuda.synchronize()
         sa.sparse_attn_check(h)
         a_ms = ev[0].elapsed_time(ev[1]) / reps
         b_ms = ev[1].elapsed_time(ev[2]) / reps
+        two_ms = ev[2].elapsed_time(ev[3]) / reps
+        two_diff = float((alpha - alpha2).abs().max())
     nbytes = 2 * T * V * 4
     gbs = nbytes / (a_ms * 1e-3) / 1e9
     res = {"workload": f"{T} tokens x {V} vocabulary, fp32 logits, 5-percentile per 2048 positions",
            "alpha_ms": round(a_ms, 4), "bin_stats_ms": round(b_ms, 4),
            "tokens_per_s": round(T / ((a_ms + b_ms) * 1e-3), 1),
-           "roofline": {"kernel": "acceptance_rate_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+           "two_pass": {"alpha_ms": round(two_ms, 4), "max_abs_diff": two_diff,
+                        "note": "the same call without a workspace: each logit read twice"},
+           "roofline": {"kernel": "acceptance_once_kernel (with its fill and sum launches)", "bound": "hbm",
+                        "achieved": round(gbs, 1),
                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "algorithmic_per_launch": f"{nbytes} B = {T} tokens x 2 rows x {V} x 4 B (each logit "
                                                   f"read once)"},

@@ -64,6 +64,7 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype_t;
 #define SA_DEVERR_CTX_LEN       4u  /* ctx_len[b] outside [1, max_ctx]                   */
 #define SA_DEVERR_TOPK          8u  /* topk[b] outside [1, max_topk]                     */
 #define SA_DEVERR_ROW          16u  /* row_seq[t] / row_pos[t] out of range (row skipped) */
+#define SA_DEVERR_SYNC         32u  /* acceptance_rate: a token's workgroups never met (alpha invalid) */
 
 typedef struct {
     int32_t n_idx_heads;   /* H_I: index heads (e.g. 64)                                  */
@@ -93,6 +94,7 @@ typedef struct {
 #define SA_OP_PREFILL_PAGED  7  /* sparse_attn_prefill_paged: n = T query rows, max_ctx   */
 #define SA_OP_PREFILL_CHUNK  8  /* sparse_attn_prefill_chunk: n = C rows, max_ctx = pos0 + C */
 #define SA_OP_PREFILL_VARLEN 9  /* sparse_attn_prefill_varlen: n = T rows, max_ctx           */
+#define SA_OP_ACCEPT        10  /* acceptance_rate: n = T tokens, max_ctx = V (0: two-pass only) */
 
 /* Create a handle for one configuration.  Validates the config, allocates the 4-byte
  * device error word on the current device (the only device allocation the library makes)
@@ -380,10 +382,18 @@ sa_status_t indexer_project_k(sa_handle_t h, const void *k, int64_t L, const voi
  * logit rows t of logits_p and logits_q over the vocabulary.
  *   logits_p, logits_q [T, ld] fp32 (row t: entries 0 .. V-1); each row needs a finite entry
  *   alpha [T] fp32 out, in [0, 1]
- * Streams both rows twice (max and sum of exp, then the sum of minima); fp32 arithmetic.
- * Needs no workspace.  Errors: SA_ERR_INVALID_ARG (NULL pointer, T < 1, V < 1, ld < V). */
+ *   ws, ws_bytes: NULL / 0, or at least sparse_attn_workspace_size(SA_OP_ACCEPT, T, V) bytes
+ * With a workspace (and V % 4 == 0, ld % 4 == 0, 16-byte aligned rows, V <= 450560 on 256 CUs) each
+ * logit is read once: a token's rows are split over a group of co-resident workgroups that hold
+ * them in registers and exchange their normalisers through the workspace; the launch takes every
+ * CU until it ends, and a group whose members cannot all be scheduled together gives up after a
+ * bounded wait with SA_DEVERR_SYNC.  Otherwise (no workspace, or a size of 0) both rows are
+ * streamed twice (max and sum of exp, then the sum of minima).  fp32 arithmetic either way; the
+ * result is deterministic for a given path.  Calls sharing one workspace must not overlap.
+ * Errors: SA_ERR_INVALID_ARG (NULL pointer, T < 1, V < 1, ld < V), SA_ERR_WORKSPACE (ws given
+ * but smaller than the size above). */
 sa_status_t acceptance_rate(sa_handle_t h, const float *logits_p, const float *logits_q, int64_t T, int64_t V,
-                            int64_t ld, float *alpha, void *stream);
+                            int64_t ld, float *alpha, void *ws, size_t ws_bytes, void *stream);
 
 /* The lower-tail statistic of the acceptance rate per bin of positions -- the same page and
  * section (the 5-percentile of the per-token values in bins of 2K positions).  Token t falls in

@@ -28,8 +28,9 @@ LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_DEVICE_CHECK = range(6)
 SA_F32, SA_BF16 = 0, 1
 SA_OP_PREFILL, SA_OP_DECODE, SA_OP_TOPK, SA_OP_PROJECT, SA_OP_PREFILL_BLOCKS, SA_OP_DECODE_BLOCKS = 1, 2, 3, 4, 5, 6
-SA_OP_PREFILL_PAGED, SA_OP_PREFILL_CHUNK, SA_OP_PREFILL_VARLEN = 7, 8, 9
+SA_OP_PREFILL_PAGED, SA_OP_PREFILL_CHUNK, SA_OP_PREFILL_VARLEN, SA_OP_ACCEPT = 7, 8, 9, 10
 SA_DEVERR_INDEX_RANGE, SA_DEVERR_BLOCK_TABLE, SA_DEVERR_CTX_LEN, SA_DEVERR_TOPK, SA_DEVERR_ROW = 1, 2, 4, 8, 16
+SA_DEVERR_SYNC = 32
 
 # Every symbol include/sparse_attn.h declares.
 EXPORTED = ("sparse_attn_create", "sparse_attn_create_host", "sparse_attn_destroy", "sparse_attn_last_error",
@@ -113,7 +114,7 @@ def load_library() -> ctypes.CDLL:
         "sparse_attn_prefill_varlen": ([P, P, P, P, P, P, P, i64, P, i32, i32, P, P, i64, i32, i32, P, P, P, P, sz,
                                         P], st),
         "indexer_project_q": ([P, P, i64, P, P, P, P, P, sz, P], st),
-        "acceptance_rate": ([P, P, P, i64, i64, i64, P, P], st),
+        "acceptance_rate": ([P, P, P, i64, i64, i64, P, P, sz, P], st),
         "acceptance_bin_stats": ([P, P, P, i64, i32, i32, ctypes.c_float, P, P, P, P], st),
         "indexer_project_k": ([P, P, i64, P, P, P, i32, i32, i64, P, P, i64, P], st),
         "sparse_attn_peak_mfma": ([P, P, i32, P, P, P], st),
@@ -356,14 +357,16 @@ def indexer_project_k(h: Handle, k, W_ik, k_idx, block_table=None, n_pages: int 
                                                    int(pos0), _stream(stream)))
 
 
-def acceptance_rate(h: Handle, logits_p, logits_q, alpha, V: int | None = None, stream=None) -> None:
-    """alpha[t] = sum_x min(softmax(logits_p[t])(x), softmax(logits_q[t])(x)) over the first V entries."""
+def acceptance_rate(h: Handle, logits_p, logits_q, alpha, V: int | None = None, ws=None, stream=None) -> None:
+    """alpha[t] = sum_x min(softmax(logits_p[t])(x), softmax(logits_q[t])(x)) over the first V entries.
+    ws: a workspace(h, SA_OP_ACCEPT, T, V) tensor for the path that reads each logit once, or None."""
     T, ld = logits_p.shape
     V = ld if V is None else V
     if logits_q.shape != logits_p.shape:
         raise ValueError("logits_p and logits_q must have the same shape")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(h.ptr, load_library().acceptance_rate(h.ptr, _ptr(logits_p), _ptr(logits_q), T, int(V), ld, _ptr(alpha),
-                                                 _stream(stream)))
+                                                 _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def acceptance_bin_stats(h: Handle, alpha, pos, bin_size: int, n_bins: int, percentile: float, count, mean, pct,

@@ -7,11 +7,13 @@
 // next-token distributions p, q (softmax of the logit rows), and summarised per bin of 2K
 // positions by a low percentile (the 5th) of the per-token values.
 //
-//  * acceptance_rate_kernel: 1024-thread workgroups, two per CU, each taking tokens in turn (more loads
-//    in flight per workgroup than one small workgroup per token: 12 % faster).  Pass 1 streams both logit rows
-//    once (16-byte loads) keeping an online (max, sum of exp) per thread for each row, reduced
-//    over the workgroup; pass 2 streams them again, in reverse order so that the part read last
-//    is still in the caches, and sums min(p, q).  HBM-bound: 8 bytes per vocabulary entry.
+//  * acceptance_once_kernel (with a workspace): each logit read once.  A token's rows are split over a
+//    group of co-resident workgroups that hold their chunks in registers and exchange the chunks'
+//    normalisers through device memory; see the section below.  HBM-bound: 8 bytes per vocabulary entry.
+//  * acceptance_rate_kernel (without one): 1024-thread workgroups, two per CU, each taking tokens in turn.
+//    Pass 1 streams both logit rows (16-byte loads) keeping an online (max, sum of exp) per thread for
+//    each row, reduced over the workgroup; pass 2 streams them again, in reverse order so that the part
+//    read last is still in the caches, and sums min(p, q): 16 bytes per vocabulary entry.
 //  * bin_stats_kernel: one workgroup per bin.  The count and the (double) sum of the bin's values
 //    from one scan of the tokens, which also stages their order keys in LDS (up to 8192), then the two
 //    order statistics around the percentile, each found exactly by an MSD radix select over the order
@@ -144,6 +146,255 @@ __global__ __launch_bounds__(kAccThreads) void acceptance_rate_kernel(const floa
         acc = block_sum(acc, shr);
         if (tid == 0) alpha[t] = acc;
     }
+}
+
+// ---- each logit read once -------------------------------------------------------------------
+// A token's two rows are cut into G consecutive chunks, one per workgroup of a group; the group's G
+// workgroups (one per CU, all resident together) take the same tokens in turn.  A workgroup holds its
+// chunk of both rows in registers: waves 1..11 (the data waves) hold kA1Per float4 of each row per lane,
+// wave 0 exchanges normalisers with the group.  Per token a data wave reduces its lanes to (max, sum of
+// exp) per row, keeping exp2(x - lane max) of every entry in place; wave 0 merges the data waves' states
+// and publishes the chunk's as one 64-bit word per row (the max's bits low, the sum's high), written and
+// polled with relaxed device-scope atomics -- a word is its own flag (an unpublished word has an all-ones
+// max, a NaN no reduction produces), so no fence orders it against other data; it waits for the group's
+// 2 G words and merges them in chunk order, so every member gets the same normalisers bit for bit.  A
+// data wave then sums its entries' min(p, q) (one multiply each: exp2(x - M) = exp2(x - m) exp2(m - M))
+// and stores one partial per (token, chunk, wave), which acceptance_sum_kernel adds in that order.
+// Wave 0 and the data waves meet only through LDS counters, so the device-wide exchange of token t's
+// normalisers proceeds while the data waves load token t + 2 and reduce token t + 1 (three register
+// buffers).  Every wait is bounded: each polling lane has kAccSpin device polls for the whole launch
+// (about 0.1 s; once spent, a word still unpublished counts as an empty chunk and SA_DEVERR_SYNC is
+// flagged -- only if some member could not be scheduled), and each LDS wait kLdsSpin polls.
+constexpr int kA1Threads = 768;
+constexpr int kA1Waves = kA1Threads / kWave;
+constexpr int kA1DataWaves = kA1Waves - 1;
+constexpr int kA1Data = kA1Threads - kWave;              // data lanes: waves 1 .. 11
+constexpr int kA1Per = 5;                                 // float4 of each row per data lane and token
+constexpr int64_t kA1Chunk = (int64_t)kA1Data * kA1Per;  // float4 of each row per workgroup (3520)
+constexpr int kA1MaxGroup = kWave / 2;                    // 2 G words polled by one wave's lanes
+constexpr int kA1Slots = 4;                               // normaliser slots (tokens) in LDS
+constexpr uint64_t kAccEmpty = ~0ull;
+constexpr int kAccSpin = 1 << 16;
+constexpr int kLdsSpin = 1 << 24;
+
+__device__ __forceinline__ float max4(float4 v) { return fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)); }
+
+__global__ void acceptance_fill_kernel(uint64_t *__restrict__ states, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        states[i] = kAccEmpty;
+}
+
+template <int N>
+using Rows = float4[N];
+
+// an LDS counter read that the compiler neither caches nor reorders
+__device__ __forceinline__ int lds_get(const int *c) { return __hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP); }
+
+__global__ __launch_bounds__(kA1Threads, 1) void acceptance_once_kernel(
+    const float4 *__restrict__ lp, const float4 *__restrict__ lq, int64_t V4, int64_t ld4, int64_t T, int G,
+    int64_t C4, int n_groups, uint64_t *__restrict__ states, float *__restrict__ part, uint32_t *err)
+{
+    __shared__ float sh_st[2][kA1Waves][4];     // per token parity and data wave: (mp, sp, mq, sq)
+    __shared__ float sh_tot[kA1Slots][4];       // per token slot: normalisers (MP, SP, MQ, SQ)
+    __shared__ uint64_t sh_words[2 * kA1MaxGroup];
+    __shared__ int sh_reduced[2];                // data-wave reductions done, per token parity (sh_st slot)
+    __shared__ int sh_ready;                     // tokens whose normalisers are in sh_tot
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    const int gi = blockIdx.x / G, g = blockIdx.x % G;
+    if (gi >= n_groups) return;
+    const int64_t c0 = (int64_t)g * C4, c1 = c0 + C4 < V4 ? c0 + C4 : V4;  // this chunk: float4 c0 .. c1 - 1
+    const float lowest = -3.402823466e38f;
+    auto tok = [&](int64_t r) { return gi + r * n_groups; };  // the group's r-th token
+    if (tok(0) >= T) return;
+    if (tid == 0) {
+        sh_reduced[0] = 0;
+        sh_reduced[1] = 0;
+        sh_ready = 0;
+    }
+    __syncthreads();  // the only barrier: the counters are set
+
+    if (wave == 0) {
+        int polls = kAccSpin;  // this lane's device polls left
+        int spins = kLdsSpin;  // LDS polls left
+        for (int64_t r = 0; tok(r) < T; ++r) {
+            const int64_t t = tok(r);
+            // every data wave has reduced token r: the count of its parity slot reaches 11 (r / 2 + 1) (a wave
+            // reduces token r + 2 only after token r's normalisers are ready, so the count never runs ahead)
+            while (lds_get(&sh_reduced[r & 1]) < kA1DataWaves * (int)(r / 2 + 1) && spins > 0) {
+                --spins;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            uint64_t *const words = states + 2 * (t * G);
+            if (lane == 0) {  // the chunk's states, merged over the data waves and published
+                const float(*st)[4] = sh_st[r & 1];
+                float mp = st[1][0], sp = st[1][1], mq = st[1][2], sq = st[1][3];
+                for (int w = 2; w < kA1Waves; ++w) {
+                    merge_state(mp, sp, st[w][0], st[w][1]);
+                    merge_state(mq, sq, st[w][2], st[w][3]);
+                }
+                const uint64_t wp = ((uint64_t)__float_as_uint(sp) << 32) | __float_as_uint(mp);
+                const uint64_t wq = ((uint64_t)__float_as_uint(sq) << 32) | __float_as_uint(mq);
+                __hip_atomic_store(words + 2 * g, wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(words + 2 * g + 1, wq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (lane < 2 * G) {  // lane 2 h + q waits for chunk h's state of row q
+                uint64_t v = __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                while (v == kAccEmpty && polls > 0) {
+                    --polls;
+                    __builtin_amdgcn_s_sleep(1);
+                    v = __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (v == kAccEmpty) {
+                    flag_error(err, SA_DEVERR_SYNC);
+                    v = (uint64_t)__float_as_uint(lowest);  // (lowest, 0): the chunk counts as empty
+                }
+                sh_words[lane] = v;
+            }
+            if (lane == 0) {  // merged in chunk order
+                float MP = lowest, SP = 0.f, MQ = lowest, SQ = 0.f;
+                for (int h = 0; h < G; ++h) {
+                    const uint64_t wp = sh_words[2 * h], wq = sh_words[2 * h + 1];
+                    merge_state(MP, SP, __uint_as_float((uint32_t)wp), __uint_as_float((uint32_t)(wp >> 32)));
+                    merge_state(MQ, SQ, __uint_as_float((uint32_t)wq), __uint_as_float((uint32_t)(wq >> 32)));
+                }
+                float *tot = sh_tot[r % kA1Slots];
+                tot[0] = MP;
+                tot[1] = SP;
+                tot[2] = MQ;
+                tot[3] = SQ;
+                __hip_atomic_store(&sh_ready, (int)(r + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+        if (spins == 0) flag_error(err, SA_DEVERR_SYNC);
+        return;
+    }
+
+    // ---- data waves ----
+    const int dl = tid - kWave;
+    bool valid[kA1Per];
+    uint32_t off[kA1Per];  // lane offsets of the chunk's float4 (lanes past it read its last one, unused)
+#pragma unroll
+    for (int j = 0; j < kA1Per; ++j) {
+        const int64_t i = c0 + dl + (int64_t)kA1Data * j;
+        valid[j] = i < c1;
+        off[j] = (uint32_t)(16 * (i < c1 ? i : c1 - 1));
+    }
+    // token t's chunk into (a, b) from uniform row bases (a token past the end reads the last one, unused)
+    auto load = [&](int64_t t, Rows<kA1Per> &a, Rows<kA1Per> &b) {
+        const int64_t tc = t < T ? t : T - 1;
+        const unsigned char *rp = reinterpret_cast<const unsigned char *>(lp + tc * ld4);
+        const unsigned char *rq = reinterpret_cast<const unsigned char *>(lq + tc * ld4);
+#pragma unroll
+        for (int j = 0; j < kA1Per; ++j) {
+            uint32_t o = off[j];
+            asm volatile("" : "+v"(o));  // kept 32-bit: a uniform base and a lane offset per load
+            a[j] = *reinterpret_cast<const float4 *>(rp + o);
+            b[j] = *reinterpret_cast<const float4 *>(rq + o);
+        }
+    };
+    // token r's chunk: this wave's (max, sum of exp2) per row into sh_st[r & 1]; the buffer keeps
+    // exp2(x - m) of every entry (x = logit * log2 e, m = the lane's maximum, returned in m[0], m[1])
+    auto reduce = [&](int64_t r, Rows<kA1Per> &a, Rows<kA1Per> &b, float (&m)[2]) {
+        float mp = lowest, mq = lowest;
+#pragma unroll
+        for (int j = 0; j < kA1Per; ++j)
+            if (valid[j]) {
+                mp = fmaxf(mp, max4(a[j]) * kLog2e);
+                mq = fmaxf(mq, max4(b[j]) * kLog2e);
+            }
+        float sp = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < kA1Per; ++j) {
+            float4 &x = a[j], &y = b[j];
+            x.x = exp2_fast(x.x * kLog2e - mp);
+            x.y = exp2_fast(x.y * kLog2e - mp);
+            x.z = exp2_fast(x.z * kLog2e - mp);
+            x.w = exp2_fast(x.w * kLog2e - mp);
+            y.x = exp2_fast(y.x * kLog2e - mq);
+            y.y = exp2_fast(y.y * kLog2e - mq);
+            y.z = exp2_fast(y.z * kLog2e - mq);
+            y.w = exp2_fast(y.w * kLog2e - mq);
+            if (valid[j]) {
+                sp += (x.x + x.y) + (x.z + x.w);
+                sq += (y.x + y.y) + (y.z + y.w);
+            }
+        }
+        m[0] = mp;
+        m[1] = mq;
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+            merge_state(mp, sp, __shfl_xor(mp, o), __shfl_xor(sp, o));
+            merge_state(mq, sq, __shfl_xor(mq, o), __shfl_xor(sq, o));
+        }
+        if (lane == 0) {
+            float *st = sh_st[r & 1][wave];
+            st[0] = mp;
+            st[1] = sp;
+            st[2] = mq;
+            st[3] = sq;
+            __hip_atomic_fetch_add(&sh_reduced[r & 1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    };
+    int spins = kLdsSpin;
+    // token r's minima once its normalisers are ready; one partial per (token, chunk, data wave)
+    auto sum = [&](int64_t r, const Rows<kA1Per> &a, const Rows<kA1Per> &b, const float (&m)[2]) {
+        while (lds_get(&sh_ready) <= (int)r && spins > 0) {
+            --spins;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const float *tot = sh_tot[r % kA1Slots];
+        const float fp = exp2_fast(m[0] - tot[0]) / tot[1], fq = exp2_fast(m[1] - tot[2]) / tot[3];
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kA1Per; ++j)
+            if (valid[j]) {
+                acc += fminf(a[j].x * fp, b[j].x * fq);
+                acc += fminf(a[j].y * fp, b[j].y * fq);
+                acc += fminf(a[j].z * fp, b[j].z * fq);
+                acc += fminf(a[j].w * fp, b[j].w * fq);
+            }
+        for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if (lane == 0) part[(tok(r) * G + g) * kA1DataWaves + (wave - 1)] = acc;
+    };
+    // step r: token r + 2's loads out, token r + 1 reduced, token r summed.  A token is reduced two
+    // steps before its slot of sh_tot is written again (kA1Slots > 2), and sh_st[r & 1] is rewritten
+    // for token r + 2 only after token r's normalisers are ready, i.e. after wave 0 has read it.
+    Rows<kA1Per> a0, b0, a1, b1, a2, b2;
+    float m0[2], m1[2], m2[2];
+    load(tok(0), a0, b0);
+    load(tok(1), a1, b1);
+    reduce(0, a0, b0, m0);
+    for (int64_t r = 0;; r += 3) {
+        load(tok(r + 2), a2, b2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tok(r + 1) < T) reduce(r + 1, a1, b1, m1);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(r, a0, b0, m0);
+        if (tok(r + 1) >= T) break;
+        load(tok(r + 3), a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tok(r + 2) < T) reduce(r + 2, a2, b2, m2);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(r + 1, a1, b1, m1);
+        if (tok(r + 2) >= T) break;
+        load(tok(r + 4), a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tok(r + 3) < T) reduce(r + 3, a0, b0, m0);
+        __builtin_amdgcn_sched_barrier(0);
+        sum(r + 2, a2, b2, m2);
+        if (tok(r + 3) >= T) break;
+    }
+    if (spins == 0) flag_error(err, SA_DEVERR_SYNC);
+}
+
+// alpha[t] = the sum of token t's partials (G chunks x kA1DataWaves waves), in that order.
+__global__ void acceptance_sum_kernel(const float *__restrict__ part, int n, int64_t T, float *__restrict__ alpha)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    float acc = 0.f;
+    for (int h = 0; h < n; ++h) acc += part[t * n + h];
+    alpha[t] = acc;
 }
 
 // The inverse of order_key.
@@ -316,11 +567,49 @@ __global__ __launch_bounds__(kBinThreads) void bin_stats_kernel(const float *__r
 
 }  // namespace
 
+int acceptance_group(const sa_handle_s &h, int64_t V)
+{
+    if (V % 4 != 0) return 0;
+    const int64_t G = (V / 4 + kA1Chunk - 1) / kA1Chunk;
+    return G <= kA1MaxGroup && G <= h.n_cu ? (int)G : 0;
+}
+
+size_t acceptance_workspace(const sa_handle_s &h, int64_t T, int64_t V)
+{
+    const int G = acceptance_group(h, V);
+    if (G == 0) return 0;
+    // 2 G state words, then G x (data waves) partial sums, per token
+    return (size_t)T * G * (2 * sizeof(uint64_t)) + (size_t)T * G * kA1DataWaves * sizeof(float);
+}
+
 hipError_t launch_acceptance_rate(sa_handle_s &h, const float *lp, const float *lq, int64_t T, int64_t V, int64_t ld,
-                                  float *alpha, hipStream_t st)
+                                  float *alpha, void *ws, hipStream_t st)
 {
     const bool vec = V % 4 == 0 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(lp) & 15u) == 0 &&
                      (reinterpret_cast<uintptr_t>(lq) & 15u) == 0;
+    const int G = vec && ws ? acceptance_group(h, V) : 0;
+    if (G > 0) {
+        uint64_t *states = static_cast<uint64_t *>(ws);
+        float *part = reinterpret_cast<float *>(states + (size_t)T * G * 2);
+        const int n_groups = h.n_cu / G;
+        const int64_t V4 = V / 4, C4 = (V4 + G - 1) / G;
+        {
+            KernelTimer timer(h, SA_KERNEL_ACCEPT, st);
+            const int64_t n = T * G * 2;
+            const int64_t blocks = (n + 255) / 256 < 4 * (int64_t)h.n_cu ? (n + 255) / 256 : 4 * (int64_t)h.n_cu;
+            hipLaunchKernelGGL(acceptance_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, states, n);
+        }
+        {
+            KernelTimer timer(h, SA_KERNEL_ACCEPT, st);
+            hipLaunchKernelGGL(acceptance_once_kernel, dim3((unsigned)(n_groups * G)), dim3(kA1Threads), 0, st,
+                               reinterpret_cast<const float4 *>(lp), reinterpret_cast<const float4 *>(lq), V4, ld / 4,
+                               T, G, C4, n_groups, states, part, h.d_err);
+        }
+        KernelTimer timer(h, SA_KERNEL_ACCEPT, st);
+        hipLaunchKernelGGL(acceptance_sum_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, part,
+                           G * kA1DataWaves, T, alpha);
+        return hipGetLastError();
+    }
     KernelTimer timer(h, SA_KERNEL_ACCEPT, st);
     const int64_t grid = T < 2 * (int64_t)h.n_cu ? T : 2 * (int64_t)h.n_cu;  // two workgroups per CU
     if (vec)

@@ -532,6 +532,10 @@ sa_status_t sparse_attn_workspace_size(sa_handle_t h, int op, int64_t n, int64_t
     case SA_OP_PROJECT:
         *bytes = sa::projection_workspace();
         return SA_OK;
+    case SA_OP_ACCEPT:
+        if (max_ctx < 1) return fail(h, SA_ERR_INVALID_ARG, "V must be >= 1");
+        *bytes = sa::acceptance_workspace(*h, n, max_ctx);
+        return SA_OK;
     default:
         return fail(h, SA_ERR_INVALID_ARG, "unknown op %d", op);
     }
@@ -1093,7 +1097,7 @@ sa_status_t sparse_attn_prefill_chunk(sa_handle_t h, const void *q, const void *
 }
 
 sa_status_t acceptance_rate(sa_handle_t h, const float *logits_p, const float *logits_q, int64_t T, int64_t V,
-                            int64_t ld, float *alpha, void *stream)
+                            int64_t ld, float *alpha, void *ws, size_t ws_bytes, void *stream)
 {
     if (!h) return fail(nullptr, SA_ERR_INVALID_ARG, "handle is NULL");
     h->last_error.clear();
@@ -1101,9 +1105,15 @@ sa_status_t acceptance_rate(sa_handle_t h, const float *logits_p, const float *l
     if (T < 1 || T > INT32_MAX) return fail(h, SA_ERR_INVALID_ARG, "T must be in [1, 2^31)");
     if (V < 1 || ld < V) return fail(h, SA_ERR_INVALID_ARG, "need 1 <= V <= ld (V %lld, ld %lld)", (long long)V,
                                      (long long)ld);
+    if (ws) {
+        const size_t need = sa::acceptance_workspace(*h, T, V);
+        if (ws_bytes < need)
+            return fail(h, SA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+        if (need == 0) ws = nullptr;
+    }
     sa_status_t s = check_device(h);
     if (s != SA_OK) return s;
-    return hip_status(h, sa::launch_acceptance_rate(*h, logits_p, logits_q, T, V, ld, alpha,
+    return hip_status(h, sa::launch_acceptance_rate(*h, logits_p, logits_q, T, V, ld, alpha, ws,
                                                     reinterpret_cast<hipStream_t>(stream)),
                       "acceptance-rate launch");
 }

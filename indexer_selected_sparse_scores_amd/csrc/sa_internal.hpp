@@ -202,8 +202,12 @@ hipError_t launch_paged_rows(sa_handle_s &h, const int32_t *row_seq, const int32
                              int32_t *budget, hipStream_t st);
 
 // ---- acceptance rate between two next-token distributions ---------------------------------
+// The single-read path's workgroups per token (0: V does not suit it) and its workspace (0 likewise).
+int acceptance_group(const sa_handle_s &h, int64_t V);
+size_t acceptance_workspace(const sa_handle_s &h, int64_t T, int64_t V);
+// ws: acceptance_workspace(h, T, V) bytes for the single-read path, or nullptr for the two-pass kernel.
 hipError_t launch_acceptance_rate(sa_handle_s &h, const float *lp, const float *lq, int64_t T, int64_t V, int64_t ld,
-                                  float *alpha, hipStream_t st);
+                                  float *alpha, void *ws, hipStream_t st);
 hipError_t launch_bin_stats(sa_handle_s &h, const float *alpha, const int32_t *pos, int64_t T, int32_t bin_size,
                             int32_t n_bins, float percentile, int32_t *count, float *mean, float *pct, hipStream_t st);
 

@@ -3,10 +3,12 @@
 Page: "Sparrow: Sparse Rollout for Stable and Efficient Long-context RL of Large Language Models",
 section 3.1 (alpha = sum_x min(p(x), q(x)) per token; its 5-percentile per bin of 2K positions).
 
-Tolerance for alpha: 1e-4 absolute.  The kernel sums in fp32: each thread adds about V/256 terms in
-sequence (594 at V = 151936) before a tree reduction, so each of the two normalisers and the sum of
-minima carries a relative error below 594 * 2^-24 = 3.5e-5, and exp2 with the log2(e) scaling adds
-a few 1e-7; alpha <= 1, so the total stays below 1e-4.  The percentile of a bin is 1-Lipschitz in
+Tolerance for alpha: 1e-4 absolute.  Both kernels sum in fp32: a thread adds at most about V/1024 terms
+in sequence (149 at V = 151936; the single-read path 20 per lane) before tree and chunk reductions, so
+each of the two normalisers and the sum of minima carries a relative error well below 1e-5, and exp2
+with the log2(e) scaling adds a few 1e-7; alpha <= 1, so the total stays below 1e-4.  Every case runs
+both paths: the two-pass kernel (no workspace) and the single-read one (a workspace; used where V % 4 == 0
+and a token's rows fit 32 chunks of 3520 float4).  The percentile of a bin is 1-Lipschitz in
 the largest change of any value, so it inherits the same bound; on given fp32 values it must equal
 the oracle's up to the final rounding to fp32 (1 ulp)."""
 from __future__ import annotations
@@ -43,30 +45,50 @@ def _handle():
     return sa.Handle(sa.Config())
 
 
-def _alpha(h, lp, lq, V=None):
-    alpha = torch.empty(lp.shape[0], dtype=torch.float32, device=DEV)
-    sa.acceptance_rate(h, lp, lq, alpha, V=V)
+def _alpha(h, lp, lq, V=None, once=False):
+    T = lp.shape[0]
+    alpha = torch.empty(T, dtype=torch.float32, device=DEV)
+    ws = sa.workspace(h, sa.SA_OP_ACCEPT, T, lp.shape[1] if V is None else V) if once else None
+    sa.acceptance_rate(h, lp, lq, alpha, V=V, ws=ws)
     assert sa.sparse_attn_check(h) == 0
     return to_np(alpha)
 
 
-@pytest.mark.parametrize("T,V,pad", [(64, 151936, 0), (7, 1001, 3), (5, 4, 0), (3, 1, 0)])
-def test_alpha_matches_oracle(T, V, pad):
-    say(f"acceptance_rate T={T} V={V} row padding={pad}")
+# (64, 151936): 11 chunks a token, 2 or 3 tokens per group of workgroups; (9, 151936, 8): padded rows, most
+# groups idle; (33, 40004, 4): 3 chunks, the last one shorter; (5, 4): one chunk of one float4; V % 4 != 0
+# and V past 32 chunks take the two-pass kernel on both paths
+@pytest.mark.parametrize("once", [False, True])
+@pytest.mark.parametrize("T,V,pad", [(64, 151936, 0), (9, 151936, 8), (33, 40004, 4), (7, 1001, 3), (5, 4, 0),
+                                     (3, 1, 0), (2, 4 * 3520 * 33, 0)])
+def test_alpha_matches_oracle(T, V, pad, once):
+    say(f"acceptance_rate T={T} V={V} row padding={pad} single-read={once}")
     d = inputs.acceptance_inputs(T, V + pad, DEV, seed=61)
     with _handle() as h:
-        a = _alpha(h, d["logits_p"], d["logits_q"], V=V)
+        a = _alpha(h, d["logits_p"], d["logits_q"], V=V, once=once)
     ref = oracle.acceptance_rate(to_np(d["logits_p"])[:, :V], to_np(d["logits_q"])[:, :V])
     err = np.abs(a - ref).max()
     say(f"  max|d alpha|={err:.2e}, alpha range [{ref.min():.4f}, {ref.max():.4f}]")
     assert err <= ALPHA_ABS
 
 
-def test_alpha_special_rows():
+def test_alpha_single_read_repeats_bit_for_bit():
+    """The single-read path merges the chunks' normalisers and partial sums in chunk order: the same
+    inputs give the same bits on every call, whichever workgroups publish first."""
+    T, V = 96, 151936
+    say(f"acceptance_rate single-read determinism T={T} V={V}")
+    d = inputs.acceptance_inputs(T, V, DEV, seed=65)
+    with _handle() as h:
+        runs = [_alpha(h, d["logits_p"], d["logits_q"], once=True) for _ in range(3)]
+    assert all(np.array_equal(runs[0], r) for r in runs[1:])
+
+
+@pytest.mark.parametrize("V", [4096, 40000])
+@pytest.mark.parametrize("once", [False, True])
+def test_alpha_special_rows(V, once):
     """Identical rows give 1, disjoint one-hot rows give 0, masked (-inf) entries count as zero
-    probability, and a constant added to a row changes nothing."""
-    say("acceptance_rate special rows")
-    V = 4096
+    probability (at V = 40000 a whole chunk of row 2 is masked), and a constant added to a row changes
+    nothing."""
+    say(f"acceptance_rate special rows V={V} single-read={once}")
     r = torch.Generator(device=DEV).manual_seed(62)
     base = torch.randn((4, V), generator=r, device=DEV) * 3
     lp = base.clone()
@@ -75,10 +97,10 @@ def test_alpha_special_rows():
     lp[1, 7] = 0.0
     lq[1].fill_(-1e4)
     lq[1, 4000] = 0.0
-    lp[2, :2048] = -float("inf")
+    lp[2, :V // 2] = -float("inf")
     lq[3] = lp[3] + 11.25
     with _handle() as h:
-        a = _alpha(h, lp, lq)
+        a = _alpha(h, lp, lq, once=once)
     ref = oracle.acceptance_rate(to_np(lp), to_np(lq))
     assert abs(a[0] - 1.0) <= 1e-5
     assert a[1] <= 1e-6
@@ -123,15 +145,15 @@ def test_bin_stats_on_given_values(bin_size, n_bins):
 
 
 def test_pipeline_at_bench_size():
-    """The measurement as the benchmark runs it: 4096 tokens over a 151936-entry vocabulary, the
-    5-percentile per bin of 2048 positions; alpha checked on sampled tokens, the statistics of the
+    """The measurement as the benchmark runs it: 4096 tokens over a 151936-entry vocabulary on the
+    single-read path, the 5-percentile per bin of 2048 positions; alpha checked on sampled tokens, the statistics of the
     GPU's alphas against the oracle's statistics of its own alphas."""
     T, V = 4096, 151936
     say(f"acceptance pipeline T={T} V={V}")
     d = inputs.acceptance_inputs(T, V, DEV)
     with _handle() as h:
         alpha = torch.empty(T, dtype=torch.float32, device=DEV)
-        sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha)
+        sa.acceptance_rate(h, d["logits_p"], d["logits_q"], alpha, ws=sa.workspace(h, sa.SA_OP_ACCEPT, T, V))
         count = torch.empty(2, dtype=torch.int32, device=DEV)
         mean = torch.empty(2, dtype=torch.float32, device=DEV)
         pct = torch.empty(2, dtype=torch.float32, device=DEV)

@@ -188,8 +188,19 @@ def test_projection_acceptance_checks(h):
     assert passed(h, "indexer_project_k", A, 100, A, A, None, 0, 0, 0, None, None, 0, None)
     assert status(h, "indexer_project_k", A, 100, M, A, None, 0, 0, 0, None, None, 0, None) == sa.SA_ERR_INVALID_ARG
     assert status(h, "indexer_project_k", A, 100, A, A, A, 0, 10, 10, None, None, 0, None) == sa.SA_ERR_INVALID_ARG
-    assert passed(h, "acceptance_rate", A, A, 100, 1000, 1000, A, None)
-    assert status(h, "acceptance_rate", A, A, 100, 1000, 999, A, None) == sa.SA_ERR_INVALID_ARG
+    assert passed(h, "acceptance_rate", A, A, 100, 1000, 1000, A, None, 0, None)
+    assert status(h, "acceptance_rate", A, A, 100, 1000, 999, A, None, 0, None) == sa.SA_ERR_INVALID_ARG
+    # the single-read path: per token and chunk of 3520 float4 per row, 2 state words and 11 partials
+    need = ws_size(h, sa.SA_OP_ACCEPT, 100, 151936)
+    assert need == 100 * 11 * (16 + 11 * 4)
+    assert passed(h, "acceptance_rate", A, A, 100, 151936, 151936, A, A, need, None)
+    assert status(h, "acceptance_rate", A, A, 100, 151936, 151936, A, A, need - 1, None) == sa.SA_ERR_WORKSPACE
+    assert ws_size(h, sa.SA_OP_ACCEPT, 100, 1001) == 0          # V % 4 != 0: two passes only
+    assert ws_size(h, sa.SA_OP_ACCEPT, 100, 4 * 3520 * 33) == 0  # more than 32 workgroups per token
+    assert ws_size(h, sa.SA_OP_ACCEPT, 1, 4) == 1 * 1 * (16 + 11 * 4)
+    assert passed(h, "acceptance_rate", A, A, 100, 1001, 1001, A, A, 1, None)  # a workspace it does not need
+    with sa.Handle(sa.Config(), host_cus=4) as few:              # 11 workgroups per token on 4 CUs
+        assert ws_size(few, sa.SA_OP_ACCEPT, 100, 151936) == 0
     assert passed(h, "acceptance_bin_stats", A, A, 100, 2048, 1, ctypes.c_float(5.0), A, A, A, None)
     assert status(h, "acceptance_bin_stats", A, A, 100, 2048, 1, ctypes.c_float(100.5), A, A, A, None) \
         == sa.SA_ERR_INVALID_ARG
