@@ -387,14 +387,17 @@ __global__ __launch_bounds__(kA1Threads, 1) void acceptance_once_kernel(
     if (spins == 0) flag_error(err, SA_DEVERR_SYNC);
 }
 
-// alpha[t] = the sum of token t's partials (G chunks x kA1DataWaves waves), in that order.
+// alpha[t] = the sum of token t's n partials (G chunks x kA1DataWaves waves), one wave per token: lane l adds
+// partials l, l + 64, ... in order, then a fixed butterfly over the lanes, so the result is the same on every call.
 __global__ void acceptance_sum_kernel(const float *__restrict__ part, int n, int64_t T, float *__restrict__ alpha)
 {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const int lane = lane_id();
     if (t >= T) return;
     float acc = 0.f;
-    for (int h = 0; h < n; ++h) acc += part[t * n + h];
-    alpha[t] = acc;
+    for (int h = lane; h < n; h += kWave) acc += part[t * n + h];
+    for (int o = kWave / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) alpha[t] = acc;
 }
 
 // The inverse of order_key.
@@ -606,7 +609,7 @@ hipError_t launch_acceptance_rate(sa_handle_s &h, const float *lp, const float *
                                T, G, C4, n_groups, states, part, h.d_err);
         }
         KernelTimer timer(h, SA_KERNEL_ACCEPT, st);
-        hipLaunchKernelGGL(acceptance_sum_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, part,
+        hipLaunchKernelGGL(acceptance_sum_kernel, dim3((unsigned)((T + 3) / 4)), dim3(4 * kWave), 0, st, part,
                            G * kA1DataWaves, T, alpha);
         return hipGetLastError();
     }
