@@ -156,3 +156,27 @@ def test_query_projection_replays_from_a_graph():
 
         _replays_match(run, [q_idx, w])
         assert sa.sparse_attn_check(h) == 0
+
+
+def test_acceptance_rate_replays_from_a_graph():
+    """The single-read acceptance rate refills its exchange words with a kernel before every run, so a
+    captured call (with the per-bin statistics) replays to the eager result; the two-pass call as well."""
+    T, V = 300, 151936
+    say(f"graph capture: acceptance_rate T={T} V={V}, both paths, and acceptance_bin_stats")
+    d = inputs.acceptance_inputs(T, V, DEV, seed=66)
+    with sa.Handle(sa.Config()) as h:
+        ws = sa.workspace(h, sa.SA_OP_ACCEPT, T, V)
+        a1 = torch.empty(T, dtype=torch.float32, device=DEV)
+        a2 = torch.empty(T, dtype=torch.float32, device=DEV)
+        count = torch.empty(1, dtype=torch.int32, device=DEV)
+        mean = torch.empty(1, dtype=torch.float32, device=DEV)
+        pct = torch.empty(1, dtype=torch.float32, device=DEV)
+
+        def run():  # on the current stream: the capture stream while capturing
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], a1, ws=ws)
+            sa.acceptance_rate(h, d["logits_p"], d["logits_q"], a2)
+            sa.acceptance_bin_stats(h, a1, d["pos"], 2048, 1, 5.0, count, mean, pct)
+
+        _replays_match(run, [a1, a2, count, mean, pct])
+        assert sa.sparse_attn_check(h) == 0
+        assert (a1 - a2).abs().max().item() <= 1e-4
