@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kAccThreads) void acceptance_rate_kernel(const floa
 // normalisers proceeds while the data waves load token t + 2 and reduce token t + 1 (three register
 // buffers).  Every wait is bounded: each polling lane has kAccSpin device polls for the whole launch
 // (about 0.1 s; once spent, a word still unpublished counts as an empty chunk and SA_DEVERR_SYNC is
-// flagged -- only if some member could not be scheduled), and each LDS wait kLdsSpin polls.
+// flagged -- only if some member could not be scheduled), and each wave kLdsSpin LDS polls for the launch.
 constexpr int kA1Threads = 768;
 constexpr int kA1Waves = kA1Threads / kWave;
 constexpr int kA1DataWaves = kA1Waves - 1;
