@@ -55,10 +55,10 @@ def _alpha(h, lp, lq, V=None, once=False):
 
 
 # (64, 151936): 11 chunks a token, 2 or 3 tokens per group of workgroups; (9, 151936, 8): padded rows, most
-# groups idle; (33, 40004, 4): 3 chunks, the last one shorter; (5, 4): one chunk of one float4; V % 4 != 0
+# groups idle; (1, 151936): one token, one group; (33, 40004, 4): 3 chunks, the last one shorter; (5, 4): one chunk of one float4; V % 4 != 0
 # and V past 32 chunks take the two-pass kernel on both paths
 @pytest.mark.parametrize("once", [False, True])
-@pytest.mark.parametrize("T,V,pad", [(64, 151936, 0), (9, 151936, 8), (33, 40004, 4), (7, 1001, 3), (5, 4, 0),
+@pytest.mark.parametrize("T,V,pad", [(64, 151936, 0), (9, 151936, 8), (1, 151936, 0), (33, 40004, 4), (7, 1001, 3), (5, 4, 0),
                                      (3, 1, 0), (2, 4 * 3520 * 33, 0)])
 def test_alpha_matches_oracle(T, V, pad, once):
     say(f"acceptance_rate T={T} V={V} row padding={pad} single-read={once}")
