@@ -92,7 +92,11 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_decode_kernel(
         if (tid == 0 && blockIdx.x == 0) flag_error(err, SA_DEVERR_CTX_LEN);
         return;
     }
-    const int64_t key0 = (int64_t)blockIdx.x * kKeysPerBlock;
+    // the row's key block, rotated by the row index: workgroups reach the XCDs round-robin by linear id, so
+    // with gridDim.x a multiple of 8 block x of every row would land on XCD x % 8 and the partial last blocks
+    // of ragged rows would pile onto the low XCDs; rotated, each row's blocks start on a different XCD
+    const int64_t xb = ((int64_t)blockIdx.x + b) % gridDim.x;
+    const int64_t key0 = xb * kKeysPerBlock;
     if (key0 >= n) return;
 
     // this wave's pages: logical pages lp0 .. lp0 + 3 of the row's sequence
