@@ -428,8 +428,11 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_decode_lds_kernel(
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int hh = lane % 16, grp = lane / 16;
-    const int64_t r = blockIdx.x;
+    // row rotated by the range: workgroups reach the XCDs round-robin by linear id, so with a row count that
+    // is a multiple of 8 every range of row r would run on XCD r % 8, and rows' unequal budgets would load the
+    // XCDs unequally; rotated, the ranges of a row spread over the XCDs
     const int split = (int)blockIdx.y;
+    const int64_t r = ((int64_t)blockIdx.x + split) % gridDim.x;
     uint32_t *err0 = (tid == 0 && split == 0) ? err : nullptr;
     const int64_t visible = visible_len(vis, r, err0);
     const int64_t kr = budget(sel, r, err0);
